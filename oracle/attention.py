@@ -1,0 +1,144 @@
+"""Plain fp64 reference of exact scaled dot-product attention (CPU, numpy).
+
+TEST INFRASTRUCTURE ONLY: the product path never imports this module.
+
+What is computed, and where the pages define it:
+
+* Forward.  "Flash Attention" skill guide, Workflow 1, step 2 ("Before
+  (standard attention)"): the weights are the row softmax of
+  ``q @ k^T / sqrt(d_k)`` and the output is those weights times ``v``.  The
+  same guide's step 3 and step 4 snippets divide by 8.0 for head dim 64, and
+  Workflow 2 step 2 passes ``softmax_scale=None`` for the automatic
+  ``1/sqrt(d)``.  The scale is therefore an explicit argument here.
+* Causal masking.  The ``causal=True`` / ``is_causal=True`` calls in the same
+  guide (quick start, Workflow 2) and in the glossary article's SDPA pattern
+  B.  Reading taken (pages silent on Nq != Nk): top-left alignment, query i
+  sees keys j <= i, as PyTorch's ``is_causal``.
+* Exactness.  The glossary article ("FlashAttention とは", and misconception 1)
+  states the tiled method returns the same result as standard attention up
+  to rounding; so this oracle is the definition itself, with the N x N score
+  and probability matrices materialised, never the tiled algorithm.
+* Log-sum-exp.  The pages give recomputation in the backward (skill guide
+  quick start; the refbase Q&A entry on tiling and recomputation) but no
+  formula.  Reading: ``lse_i = log sum_j exp(s_ij)`` with ``s = scale*q.k``,
+  natural log, the quantity that lets P be recomputed as ``exp(s - lse)``.
+* Backward.  The pages only say that training (forward + backward) is
+  supported (glossary comparison table; misconception 2; FA2 FAQ Q2).  The
+  gradients here are the textbook chain rule through softmax:
+  ``dV = P^T dO``, ``dP = dO V^T``,
+  ``dS = P * (dP - rowsum(P * dP))``, ``dQ = scale * dS K``,
+  ``dK = scale * dS^T Q``.  Deliberately the ``rowsum(P*dP)`` form, not the
+  ``rowsum(dO*O)`` identity a fast kernel uses, so parity tests that identity.
+
+Layout of every array: ``[batch, heads, seq, dim]`` (``[B, H, N, d]``), float64.
+"""
+import numpy as np
+
+__all__ = [
+    "attention_fwd64",
+    "attention_rows_fwd64",
+    "attention_bwd64",
+]
+
+
+def _as64(x):
+    a = np.asarray(x, dtype=np.float64)
+    if a.ndim != 4:
+        raise ValueError("expected a [B, H, N, d] array, got shape %r" % (a.shape,))
+    return a
+
+
+def _scores(q2, k2, scale, causal, rows):
+    """s_ij = scale * q_i . k_j for the query rows ``rows`` (global indices);
+    masked entries (key j after query i) are -inf."""
+    s = scale * (q2 @ k2.T)
+    if causal:
+        keys = np.arange(k2.shape[0])
+        s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+    return s
+
+
+def _softmax_rows(s):
+    """Row softmax written out: p = exp(s - m) / sum exp(s - m) with
+    m = row max (subtracting m changes nothing mathematically).  Also returns
+    lse = m + log(sum exp(s - m)) = log sum exp(s)."""
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = np.sum(e, axis=1, keepdims=True)
+    p = e / z
+    lse = (m + np.log(z))[:, 0]
+    return p, lse
+
+
+def attention_fwd64(q, k, v, scale, causal):
+    """O = softmax(scale * Q K^T [causal mask]) V and its log-sum-exp.
+
+    q: [B, H, Nq, d]; k, v: [B, H, Nk, d] (any float dtype, widened to fp64).
+    Returns (o [B, H, Nq, d], lse [B, H, Nq]) in float64.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, Nq, d = q.shape
+    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != d:
+        raise ValueError("shape mismatch q%r k%r v%r" % (q.shape, k.shape, v.shape))
+    scale = float(scale)
+    o = np.empty((B, H, Nq, d), dtype=np.float64)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(H):
+            s = _scores(q[b, h], k[b, h], scale, causal, rows)
+            p, lse[b, h] = _softmax_rows(s)
+            o[b, h] = p @ v[b, h]
+    return o, lse
+
+
+def attention_rows_fwd64(q, k, v, scale, causal, rows):
+    """The forward restricted to selected query rows (each against all keys).
+
+    rows: int array [B, H, R] of query indices.  Returns
+    (o [B, H, R, d], lse [B, H, R]).  Row i of the result is exactly row
+    rows[b,h,i] of ``attention_fwd64`` (softmax rows are independent).
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    rows = np.asarray(rows, dtype=np.int64)
+    B, H, Nq, d = q.shape
+    if rows.ndim != 3 or rows.shape[:2] != (B, H):
+        raise ValueError("rows must be [B, H, R]")
+    R = rows.shape[2]
+    o = np.empty((B, H, R, d), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            r = rows[b, h]
+            s = _scores(q[b, h][r], k[b, h], float(scale), causal, r)
+            p, lse[b, h] = _softmax_rows(s)
+            o[b, h] = p @ v[b, h]
+    return o, lse
+
+
+def attention_bwd64(q, k, v, do, scale, causal):
+    """Gradients of L = sum(O * dO) with respect to Q, K and V.
+
+    Recomputes P from Q and K (its own P: nothing produced by a fast kernel
+    is used), then applies the chain rule listed in the module docstring.
+    Returns (dq, dk, dv) with the shapes of q, k, v, in float64.
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    B, H, Nq, d = q.shape
+    if do.shape != q.shape:
+        raise ValueError("dO must have the shape of Q")
+    scale = float(scale)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(H):
+            qq, kk, vv, g = q[b, h], k[b, h], v[b, h], do[b, h]
+            p, _ = _softmax_rows(_scores(qq, kk, scale, causal, rows))
+            dv[b, h] = p.T @ g
+            dp = g @ vv.T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[b, h] = scale * (ds @ kk)
+            dk[b, h] = scale * (ds.T @ qq)
+    return dq, dk, dv
