@@ -1,0 +1,267 @@
+"""Exact attention on MI355X: Python binding of libfa.so.
+
+Thin ctypes marshalling over the C ABI in ``include/fa.h``.  The functions
+named like the C entry points (``fa_fwd``, ``fa_fwd_strided``, ``fa_bwd``,
+``fa_bwd_strided``, ``fa_bwd_workspace_bytes``, ``fa_status_string``,
+``fa_last_error_message``) take torch tensors, read their sizes and strides,
+and call the library on the tensors' device and current stream.  Every step
+of the computation runs in the library's HIP kernels; there is no other
+implementation here, and nothing falls back: if libfa.so is missing or the
+device is not gfx950, calls raise.
+
+``attention_fwd`` / ``attention_bwd`` are conveniences that allocate the
+outputs (and the backward workspace) with torch, then call the entry points.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_DEVICE", "FA_ERR_LAUNCH",
+    "FA_FP16", "FA_BF16", "FaError", "lib_path", "load_library",
+    "fa_fwd", "fa_fwd_strided", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages", "fa_bwd_workspace_bytes",
+    "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
+    "fa_status_string", "fa_last_error_message", "fa_abi_version",
+    "attention_fwd", "attention_bwd", "EXPORTED_SYMBOLS",
+]
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_DEVICE, FA_ERR_LAUNCH = 0, 1, 2, 3, 4
+FA_FP16, FA_BF16 = 0, 1
+FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
+
+EXPORTED_SYMBOLS = (
+    "fa_fwd", "fa_fwd_strided", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
+    "fa_status_string", "fa_last_error_message", "fa_abi_version",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_I64x3 = ctypes.c_int64 * 3
+
+
+class FaError(RuntimeError):
+    """A nonzero status from libfa.so."""
+
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__("%s: %s" % (fa_status_string(status), detail))
+
+
+def lib_path():
+    return os.path.join(_HERE, "libfa.so")
+
+
+def load_library():
+    """Load libfa.so (built in-tree by ``python -m exact_io_aware_02_amd.build``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError("libfa.so is not built (%s); run: python -m exact_io_aware_02_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+    lib.fa_fwd.restype = _i
+    lib.fa_fwd_strided.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
+                                   _I64x3, _I64x3, _I64x3, _I64x3, _vp]
+    lib.fa_fwd_strided.restype = _i
+    lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+    lib.fa_bwd_workspace_bytes.restype = _sz
+    lib.fa_bwd.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp, _sz, _vp]
+    lib.fa_bwd.restype = _i
+    lib.fa_bwd_strided.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i] + [_I64x3] * 8 + [_vp, _sz, _vp]
+    lib.fa_bwd_strided.restype = _i
+    lib.fa_bwd_stages.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i] + [_I64x3] * 8 + [_vp, _sz, _i, _vp]
+    lib.fa_bwd_stages.restype = _i
+    lib.fa_status_string.argtypes = [_i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error_message.argtypes = []
+    lib.fa_last_error_message.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = _i
+    _LIB = lib
+    return lib
+
+
+def fa_status_string(status):
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_last_error_message():
+    return load_library().fa_last_error_message().decode()
+
+
+def fa_abi_version():
+    return load_library().fa_abi_version()
+
+
+def _check(status):
+    if status != FA_OK:
+        raise FaError(status, fa_last_error_message())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float16:
+        return FA_FP16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise FaError(FA_ERR_UNSUPPORTED, "dtype %s unsupported (float16 or bfloat16; fp32 is not supported)" % t.dtype)
+
+
+def _on_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise FaError(FA_ERR_INVALID_ARG, "tensors must live on a HIP device (got %s)" % t.device)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+_AXES = {"bhsd": (0, 1, 2, 3), "bshd": (0, 2, 1, 3)}
+
+
+def _axes(layout):
+    try:
+        return _AXES[layout]
+    except KeyError:
+        raise ValueError("layout must be 'bhsd' or 'bshd'") from None
+
+
+def _dims(t, layout):
+    """(B, H, N, d) of a 4-D tensor in the given layout."""
+    if t.dim() != 4:
+        raise ValueError("expected a 4-D tensor, got shape %r" % (tuple(t.shape),))
+    ab, ah, as_, ad = _axes(layout)
+    return t.shape[ab], t.shape[ah], t.shape[as_], t.shape[ad]
+
+
+def _strides(t, layout):
+    ab, ah, as_, ad = _axes(layout)
+    if t.shape[ad] > 1 and t.stride(ad) != 1:
+        raise FaError(FA_ERR_INVALID_ARG, "the d dimension must be contiguous")
+    return _I64x3(t.stride(ab), t.stride(ah), t.stride(as_))
+
+
+def _default_scale(d, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fa_fwd(q, k, v, o, lse, scale, causal, stream=None):
+    """C ``fa_fwd`` on contiguous BHSD tensors: q/o [B,H,Nq,d], k/v [B,H,Nk,d],
+    lse fp32 [B,H,Nq].  Enqueues on ``stream`` (default: current stream)."""
+    dt = _dtype_code(q)
+    _on_device(q, k, v, o, lse)
+    B, H, Nq, d = _dims(q, "bhsd")
+    Nk = k.shape[2]
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                                     float(scale), int(bool(causal)), dt, _stream(q, stream)))
+
+
+def fa_fwd_strided(q, k, v, o, lse, scale, causal, layout="bshd", stream=None):
+    """C ``fa_fwd_strided``: the tensors' own strides, read in ``layout``."""
+    dt = _dtype_code(q)
+    _on_device(q, k, v, o, lse)
+    B, H, Nq, d = _dims(q, layout)
+    Nk = _dims(k, layout)[2]
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_fwd_strided(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+            dt, _strides(q, layout), _strides(k, layout), _strides(v, layout), _strides(o, layout),
+            _stream(q, stream)))
+
+
+def fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype):
+    return int(load_library().fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype))
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, stream=None):
+    """C ``fa_bwd`` on contiguous BHSD tensors; ``workspace`` is a device
+    tensor of at least ``fa_bwd_workspace_bytes`` bytes."""
+    dt = _dtype_code(q)
+    _on_device(q, k, v, o, lse, do, dq, dk, dv, workspace)
+    B, H, Nq, d = _dims(q, "bhsd")
+    Nk = k.shape[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, H, Nq, Nk, d, float(scale), int(bool(causal)), dt, _ptr(workspace), nbytes,
+            _stream(q, stream)))
+
+
+def fa_bwd_strided(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, layout="bshd", stream=None):
+    """C ``fa_bwd_strided``: every d-major tensor's own strides, read in ``layout``."""
+    dt = _dtype_code(q)
+    _on_device(q, k, v, o, lse, do, dq, dk, dv, workspace)
+    B, H, Nq, d = _dims(q, layout)
+    Nk = _dims(k, layout)[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    st = [_strides(t, layout) for t in (q, k, v, o, do, dq, dk, dv)]
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_bwd_strided(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, H, Nq, Nk, d, float(scale), int(bool(causal)), dt, *st, _ptr(workspace), nbytes,
+            _stream(q, stream)))
+
+
+def fa_bwd_stages(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, stages, layout="bhsd", stream=None):
+    """C ``fa_bwd_stages``: run the selected backward stages (OR of FA_BWD_*)."""
+    dt = _dtype_code(q)
+    _on_device(q, k, v, o, lse, do, dq, dk, dv, workspace)
+    B, H, Nq, d = _dims(q, layout)
+    Nk = _dims(k, layout)[2]
+    nbytes = workspace.numel() * workspace.element_size()
+    st = [_strides(t, layout) for t in (q, k, v, o, do, dq, dk, dv)]
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_bwd_stages(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, H, Nq, Nk, d, float(scale), int(bool(causal)), dt, *st, _ptr(workspace), nbytes, int(stages),
+            _stream(q, stream)))
+
+
+def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None):
+    """O = softmax(scale Q K^T) V (top-left causal mask if ``causal``).
+
+    Allocates o (like q) and lse (fp32 [B,H,Nq]); returns (o, lse).  ``scale``
+    defaults to 1/sqrt(d).
+    """
+    _dtype_code(q)
+    _on_device(q, k, v)
+    B, H, Nq, d = _dims(q, layout)
+    s = _default_scale(d, scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if layout == "bhsd" and q.is_contiguous() and k.is_contiguous() and v.is_contiguous():
+        fa_fwd(q, k, v, o, lse, s, causal, stream)
+    else:
+        fa_fwd_strided(q, k, v, o, lse, s, causal, layout, stream)
+    return o, lse
+
+
+def attention_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bhsd", stream=None):
+    """Gradients (dq, dk, dv) of sum(O * dO), recomputing P from ``lse``."""
+    _on_device(q, k, v, o, lse, do)
+    B, H, Nq, d = _dims(q, layout)
+    Nk = _dims(k, layout)[2]
+    s = _default_scale(d, scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, _dtype_code(q))
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    contiguous = all(t.is_contiguous() for t in (q, k, v, o, do))
+    if layout == "bhsd" and contiguous:
+        fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, stream)
+    else:
+        fa_bwd_strided(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, layout, stream)
+    return dq, dk, dv

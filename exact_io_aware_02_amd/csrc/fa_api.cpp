@@ -1,0 +1,291 @@
+// C ABI of libfa.so: argument validation, device check and dispatch.
+// Every check runs before the first HIP call, so an invalid call enqueues
+// nothing and touches no device.  Declarations and the contract are in
+// include/fa.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950, 2 = other architecture.
+std::atomic<int> g_arch_state[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(FA_ERR_DEVICE, "no HIP device available (%s)", hipGetErrorString(e));
+  }
+  if (dev >= kMaxDevices) return fail(FA_ERR_DEVICE, "device ordinal %d out of range", dev);
+  int st = g_arch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(FA_ERR_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    }
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_release);
+    if (st == 2) return fail(FA_ERR_UNSUPPORTED, "device %d is %s; these kernels are built for gfx950", dev, prop.gcnArchName);
+  }
+  if (st == 2) return fail(FA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest element offset touched within one (b, h) slice, and the whole-tensor
+// extent, for overflow checks and aliasing.
+struct Extent {
+  int64_t lo_bytes, hi_bytes;  // [lo, hi) byte range relative to the base pointer
+};
+
+int check_tensor(const char* name, const void* ptr, const int64_t st[3], int B, int H, int N, int d, Extent* ext) {
+  ext->lo_bytes = 0;
+  ext->hi_bytes = 0;
+  if (N == 0) return FA_OK;  // empty tensor: never dereferenced
+  if (!ptr) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(FA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0) return fail(FA_ERR_INVALID_ARG, "%s stride[%d] = %lld is negative", name, i, (long long)st[i]);
+    if (st[i] % 8 != 0)
+      return fail(FA_ERR_INVALID_ARG, "%s stride[%d] = %lld is not a multiple of 8 elements", name, i, (long long)st[i]);
+  }
+  if (N > 1 && st[2] < d) return fail(FA_ERR_INVALID_ARG, "%s seq stride %lld < d = %d (rows overlap)", name, (long long)st[2], d);
+  // within one (b, h) slice the kernels use 32-bit-safe offsets
+  const int64_t slice_max = (int64_t)(N - 1) * st[2] + d;
+  if (slice_max > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "%s: per-head extent exceeds 2^31 elements", name);
+  const int64_t last = (int64_t)(B - 1) * st[0] + (int64_t)(H - 1) * st[1] + (int64_t)(N - 1) * st[2] + d;
+  if (last > (INT64_MAX / 4)) return fail(FA_ERR_INVALID_ARG, "%s: extent overflows", name);
+  ext->lo_bytes = 0;
+  ext->hi_bytes = last * 2;
+  return FA_OK;
+}
+
+bool overlaps(const void* a, const Extent& ea, const void* b, const Extent& eb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  const uintptr_t a1 = a0 + (uintptr_t)ea.hi_bytes, b1 = b0 + (uintptr_t)eb.hi_bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+int check_common(int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative size (B=%d H=%d Nq=%d Nk=%d)", B, H, Nq, Nk);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", d);
+  if (dtype != FA_FP16 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "dtype %d unsupported (FA_FP16=0 or FA_BF16=1; fp32 is not supported)", dtype);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale is not finite");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (Nq > 0 && B > 0 && H > 0 && Nk < 1) return fail(FA_ERR_INVALID_ARG, "Nk must be >= 1 when there are queries");
+  if ((int64_t)B * H > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "B*H overflows");
+  return FA_OK;
+}
+
+float softmax_c(float scale) {
+  // |scale| * log2(e); a tiny floor keeps c > 0 so masked (-inf) scores stay
+  // -inf after scaling.  For |scale| below it the weights are uniform to
+  // well under fp32 rounding either way.
+  float c = std::fabs(scale) * 1.4426950408889634f;
+  return c < 1e-30f ? 1e-30f : c;
+}
+
+void contiguous_strides(int H, int N, int d, int64_t st[3]) {
+  st[2] = d;
+  st[1] = (int64_t)N * d;
+  st[0] = (int64_t)H * N * d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return 1; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_DEVICE: return "FA_ERR_DEVICE";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH";
+    default: return "FA_UNKNOWN_STATUS";
+  }
+}
+
+const char* fa_last_error_message(void) { return g_msg; }
+
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, int dtype, const int64_t q_strides[3],
+                   const int64_t k_strides[3], const int64_t v_strides[3], const int64_t o_strides[3],
+                   void* stream) {
+  g_msg[0] = '\0';
+  int st = check_common(B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st) return st;
+  if (!q_strides || !k_strides || !v_strides || !o_strides) return fail(FA_ERR_INVALID_ARG, "a strides array is NULL");
+  if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+  Extent eq, ek, ev, eo;
+  if ((st = check_tensor("q", q, q_strides, B, H, Nq, d, &eq))) return st;
+  if ((st = check_tensor("k", k, k_strides, B, H, Nk, d, &ek))) return st;
+  if ((st = check_tensor("v", v, v_strides, B, H, Nk, d, &ev))) return st;
+  if ((st = check_tensor("o", o, o_strides, B, H, Nq, d, &eo))) return st;
+  if (!lse) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  Extent el{0, (int64_t)B * H * Nq * 4};
+  if (overlaps(o, eo, q, eq) || overlaps(o, eo, k, ek) || overlaps(o, eo, v, ev))
+    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+  if (overlaps(lse, el, q, eq) || overlaps(lse, el, k, ek) || overlaps(lse, el, v, ev) || overlaps(lse, el, o, eo))
+    return fail(FA_ERR_INVALID_ARG, "lse overlaps another tensor");
+  if ((st = check_device())) return st;
+
+  fa::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.sq = {q_strides[0], q_strides[1], q_strides[2]};
+  p.sk = {k_strides[0], k_strides[1], k_strides[2]};
+  p.sv = {v_strides[0], v_strides[1], v_strides[2]};
+  p.so = {o_strides[0], o_strides[1], o_strides[2]};
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.c = softmax_c(scale);
+  p.qflip = std::signbit(scale) ? 0x80008000u : 0u;
+  hipError_t e = fa::launch_fwd(p, d, dtype, causal != 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "forward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
+           float scale, int causal, int dtype, void* stream) {
+  int64_t sq[3], sk[3];
+  contiguous_strides(H, Nq, d, sq);
+  contiguous_strides(H, Nk, d, sk);
+  return fa_fwd_strided(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, sq, sk, sk, sq, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || (d != 64 && d != 128) || (dtype != FA_FP16 && dtype != FA_BF16)) return 0;
+  const size_t n = (size_t)B * (size_t)H * (size_t)Nq * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                  int dtype, const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+                  const int64_t o_strides[3], const int64_t do_strides[3], const int64_t dq_strides[3],
+                  const int64_t dk_strides[3], const int64_t dv_strides[3], void* workspace,
+                  size_t workspace_bytes, int stages, void* stream) {
+  g_msg[0] = '\0';
+  int st = check_common(B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st) return st;
+  if (stages <= 0 || (stages & ~FA_BWD_ALL)) return fail(FA_ERR_INVALID_ARG, "stages = %d is not a nonzero OR of FA_BWD_*", stages);
+  if (!q_strides || !k_strides || !v_strides || !o_strides || !do_strides || !dq_strides || !dk_strides || !dv_strides)
+    return fail(FA_ERR_INVALID_ARG, "a strides array is NULL");
+  if (B == 0 || H == 0) return FA_OK;
+  if (Nq == 0 && Nk == 0) return FA_OK;  // with Nq = 0 and Nk > 0, dK = dV = 0 are written
+  Extent eq, ek, ev, eo, edo, edq, edk, edv;
+  if ((st = check_tensor("q", q, q_strides, B, H, Nq, d, &eq))) return st;
+  if ((st = check_tensor("k", k, k_strides, B, H, Nk, d, &ek))) return st;
+  if ((st = check_tensor("v", v, v_strides, B, H, Nk, d, &ev))) return st;
+  if ((st = check_tensor("o", o, o_strides, B, H, Nq, d, &eo))) return st;
+  if ((st = check_tensor("dout", dout, do_strides, B, H, Nq, d, &edo))) return st;
+  if ((st = check_tensor("dq", dq, dq_strides, B, H, Nq, d, &edq))) return st;
+  if ((st = check_tensor("dk", dk, dk_strides, B, H, Nk, d, &edk))) return st;
+  if ((st = check_tensor("dv", dv, dv_strides, B, H, Nk, d, &edv))) return st;
+  if (Nq > 0 && !lse) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  const size_t need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype);
+  if (need > 0 && !workspace) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(FA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARG, "workspace_bytes = %zu < required %zu", workspace_bytes, need);
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const Extent eins[6] = {eq, ek, ev, eo, edo, Extent{0, (int64_t)B * H * Nq * 4}};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const Extent eouts[4] = {edq, edk, edv, Extent{0, (int64_t)need}};
+  const char* onames[4] = {"dq", "dk", "dv", "workspace"};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], eouts[i], ins[j], eins[j])) return fail(FA_ERR_INVALID_ARG, "%s overlaps an input", onames[i]);
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], eouts[i], outs[j], eouts[j]))
+        return fail(FA_ERR_INVALID_ARG, "%s overlaps %s", onames[i], onames[j]);
+  }
+  if ((st = check_device())) return st;
+
+  fa::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.lse = lse;
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.dsum = static_cast<float*>(workspace);
+  p.sq = {q_strides[0], q_strides[1], q_strides[2]};
+  p.sk = {k_strides[0], k_strides[1], k_strides[2]};
+  p.sv = {v_strides[0], v_strides[1], v_strides[2]};
+  p.so = {o_strides[0], o_strides[1], o_strides[2]};
+  p.sdo = {do_strides[0], do_strides[1], do_strides[2]};
+  p.sdq = {dq_strides[0], dq_strides[1], dq_strides[2]};
+  p.sdk = {dk_strides[0], dk_strides[1], dk_strides[2]};
+  p.sdv = {dv_strides[0], dv_strides[1], dv_strides[2]};
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_bwd(p, d, dtype, causal != 0, stages, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "backward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   int dtype, const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+                   const int64_t o_strides[3], const int64_t do_strides[3], const int64_t dq_strides[3],
+                   const int64_t dk_strides[3], const int64_t dv_strides[3], void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return fa_bwd_stages(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype, q_strides, k_strides,
+                       v_strides, o_strides, do_strides, dq_strides, dk_strides, dv_strides, workspace,
+                       workspace_bytes, FA_BWD_ALL, stream);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t sq[3], sk[3];
+  contiguous_strides(H, Nq, d, sq);
+  contiguous_strides(H, Nk, d, sk);
+  return fa_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype, sq, sk, sk, sq, sq,
+                        sq, sk, sk, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

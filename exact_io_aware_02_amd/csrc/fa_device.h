@@ -1,0 +1,128 @@
+// Device helpers shared by the gfx950 attention kernels: operand types, the
+// 32x32x16 MFMA wrappers, fp32 -> fp16/bf16 packing, the LDS tile swizzle
+// and the transposing LDS read.
+//
+// Register layouts of v_mfma_f32_32x32x16_{f16,bf16} (one wave, lane i):
+//   A (32 x 16, M x K): lane i holds A[i % 32][8*(i/32) + 0..7]
+//   B (16 x 32, K x N): lane i holds B[8*(i/32) + 0..7][i % 32]
+//   C (32 x 32)       : lane i, register r holds C[row(i, r)][i % 32] with
+//                       row(i, r) = 8*(r/4) + 4*(i/32) + r%4
+// Only the pairing of A's and B's k-slots matters for a contraction, so a
+// kernel may feed any consistent permutation of the k index to both.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<DT_F16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<DT_BF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// Two fp32 values rounded to nearest-even into one dword (lo in bits 0..15).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <>
+__device__ __forceinline__ uint32_t pack2<DT_F16>(float lo, float hi) {
+  f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<DT_BF16>(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Row of the 32x32 accumulator held by lane-half `half` in register r.
+__device__ __forceinline__ int acc_row(int half, int r) { return ((r >> 2) << 3) + (half << 2) + (r & 3); }
+
+// LDS tiles are [rows][D] 16-bit elements, rows of D/8 16-byte chunks; chunk
+// c of row r lives at physical chunk c ^ swz(r).  The XOR keeps every 8-byte
+// group contiguous and makes both read patterns the kernels use free of bank
+// conflicts: 16 consecutive rows at one chunk (128-bit operand reads) and
+// 4 consecutive rows x 4 consecutive chunks (transposing 64-bit reads).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+}
+// Element offset of (row r, column col) in a swizzled [rows][D] tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  return r * D + ((((col >> 3) ^ swz<D>(r)) << 3) | (col & 7));
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane l receives element
+// j (j = 0..3) from the 8-byte word addressed by lane 4*j + (l%16)/4 of the
+// group, at 16-bit offset l%4.  With lane p of a group pointing at
+// (row0 + p/4, col0 + 4*(p%4)), lane l gets rows row0..row0+3 of column
+// col0 + l%16: a 4-key x 16-column transpose.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_ptr) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds_ptr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// A-operand of an MFMA whose k index runs over tile rows (keys or queries)
+// and whose m index runs over the d columns: lane i gets column
+// 32*db + i%32 and rows {kb + 4*(i/32) + 0..3, kb + 8 + 4*(i/32) + 0..3},
+// matching the k order of a 32x32 accumulator's registers 8*kk..8*kk+7
+// (see acc_row).  `kb` is the first of the 16 rows.
+template <int D>
+__device__ __forceinline__ u32x4 load_transposed_a(const uint16_t* tile, int lane, int kb, int db) {
+  const int g = lane >> 4, p = lane & 15;
+  const int row0 = kb + 4 * (g >> 1) + (p >> 2);
+  const int col = db * 32 + 16 * (g & 1) + 4 * (p & 3);
+  u32x2 lo = lds_read_tr16(tile + tile_off<D>(row0, col));
+  u32x2 hi = lds_read_tr16(tile + tile_off<D>(row0 + 8, col));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// A- or B-operand whose k index runs over the d columns: 8 consecutive
+// columns 16*ks + 8*(lane/32) .. +7 of tile row `r`.
+template <int D>
+__device__ __forceinline__ u32x4 load_rowmajor_op(const uint16_t* tile, int r, int ks, int half) {
+  const int c = 2 * ks + half;
+  return *(const u32x4*)(tile + r * D + ((c ^ swz<D>(r)) << 3));
+}
+
+// Pack registers 8*kk .. 8*kk+7 of an fp32 accumulator into an MFMA operand.
+template <int DT>
+__device__ __forceinline__ u32x4 pack_acc8(const f32x16& s, int kk) {
+  const int o = 8 * kk;
+  return u32x4{pack2<DT>(s[o + 0], s[o + 1]), pack2<DT>(s[o + 2], s[o + 3]), pack2<DT>(s[o + 4], s[o + 5]),
+               pack2<DT>(s[o + 6], s[o + 7])};
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+}  // namespace fa

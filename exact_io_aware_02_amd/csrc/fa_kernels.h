@@ -1,0 +1,48 @@
+// Kernel parameter blocks and host-side launchers (internal to libfa.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Element strides {batch, head, seq}; the d dimension is contiguous.
+struct Strides {
+  int64_t b, h, s;
+};
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  Strides sq, sk, sv, so;
+  int B, H, Nq, Nk;
+  float c;         // |scale| * log2(e), clamped away from 0
+  uint32_t qflip;  // 0x80008000 when scale < 0 (Q is negated on load), else 0
+};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dsum;  // workspace: D_i = dO_i . O_i, fp32 [B][H][Nq]
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
+  int B, H, Nq, Nk;
+  float scale;  // the softmax scale as given
+  float c;      // scale * log2(e) (signed)
+};
+
+// Return hipSuccess or the launch error.  d in {64,128}, dtype 0 = fp16,
+// 1 = bf16; the caller has validated every argument.
+hipError_t launch_fwd(const FwdParams& p, int d, int dtype, bool causal, hipStream_t stream);
+// stages: OR of 1 (D = rowsum(dO*O)), 2 (dK, dV), 4 (dQ), run in that order.
+hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool causal, int stages, hipStream_t stream);
+
+}  // namespace fa

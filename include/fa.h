@@ -1,0 +1,151 @@
+/*
+ * fa.h - exact scaled dot-product attention on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (per batch b and head h):
+ *
+ *     S   = scale * Q K^T                      (Nq x Nk, never stored)
+ *     P   = softmax_rows(S)                    (causal: entries j > i are -inf)
+ *     O   = P V                                (Nq x d)
+ *     LSE = log sum_j exp(S_ij)                (natural log, per query row)
+ *
+ * This is the "standard attention" the "Flash Attention" skill guide replaces
+ * in Workflow 1, step 2 (softmax of q k^T / sqrt(d_k), times v), computed the
+ * way the glossary article's "FlashAttention の仕組み" section and its four-step
+ * figure describe: Q/K/V split into blocks that live in on-chip memory, an
+ * online softmax whose running maximum and normaliser are updated as each
+ * key block arrives, and one merged write of the result, so the Nq x Nk score
+ * matrix is never written to HBM.  The backward recomputes P from the saved
+ * LSE instead of storing it (skill guide quick start: tiling and
+ * recomputation; refbase entry, "Capability").
+ *
+ * Causal masking is top-left aligned: query i attends to keys j <= i (the
+ * reading of the pages' causal=True / is_causal=True that matches PyTorch
+ * when Nq != Nk).  A causal row therefore always sees key 0.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or retains them, and never synchronises.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously on it; a kernel fault shows at the
+ *    caller's next synchronisation, as usual in HIP.
+ *  - Element type of Q, K, V, O, dO, dQ, dK, dV is `dtype` (FA_FP16 or
+ *    FA_BF16; fp32 is not supported, as the skill guide's "精度が落ちる"
+ *    issue and the glossary article's FP32 anti-pattern state).  LSE and the
+ *    backward workspace are fp32.
+ *  - Head dimension d must be 64 or 128.
+ *  - Default layout ("BHSD", the SDPA layout of the skill guide's quick
+ *    start): Q/O are [B][H][Nq][d], K/V are [B][H][Nk][d], contiguous.
+ *    The *_strided variants take, per tensor, three element strides
+ *    {batch, head, seq}; the d dimension must be contiguous (stride 1).
+ *    This covers the flash_attn layout [B][N][H][d] ("BSHD", skill guide
+ *    Workflow 2 step 2) with strides {N*H*d, d, H*d}.
+ *  - LSE is always a contiguous fp32 array [B][H][Nq].
+ *  - `scale` is any finite float (1/sqrt(d) is the pages' default).
+ *  - B, H or Nq equal to 0: nothing to do, FA_OK.  Nk must be >= 1 when
+ *    Nq >= 1 (a softmax over no keys is undefined).
+ *  - Each base pointer must be 16-byte aligned and each stride a multiple of
+ *    8 elements; element offsets within one (b, h) slice must fit in 31
+ *    bits.  O must not alias Q, K or V; dQ/dK/dV must not alias any input.
+ *  - Return value: FA_OK (0) or an fa_status code.  Arguments are checked
+ *    before any HIP call; on error nothing is enqueued.  A thread-local
+ *    human-readable detail is available from fa_last_error_message().
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, bad size/stride/alignment, aliasing, small workspace */
+  FA_ERR_UNSUPPORTED = 2, /* d not in {64,128}, dtype not fp16/bf16, device is not gfx950 */
+  FA_ERR_DEVICE = 3,      /* no HIP device, or a device query failed */
+  FA_ERR_LAUNCH = 4       /* the kernel launch itself reported an error */
+} fa_status;
+
+typedef enum { FA_FP16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Forward, BHSD contiguous.
+ *   q   [B][H][Nq][d]   in
+ *   k,v [B][H][Nk][d]   in
+ *   o   [B][H][Nq][d]   out, O = softmax(scale Q K^T) V in dtype (RNE)
+ *   lse [B][H][Nq] fp32 out, natural-log sum of exp(scale q.k) per row
+ *   causal: 0 or 1. */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+           void* stream);
+
+/* Forward with explicit element strides {batch, head, seq} for q, k, v, o.
+ * Same kernels as fa_fwd. */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                   const int64_t q_strides[3], const int64_t k_strides[3],
+                   const int64_t v_strides[3], const int64_t o_strides[3],
+                   void* stream);
+
+/* Bytes of device workspace fa_bwd needs for these sizes (0 if the sizes are
+ * invalid).  Holds D_i = sum_d dO_i O_i (fp32 [B][H][Nq]). */
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
+
+/* Backward of L = sum(O * dO): gradients of Q, K, V, BHSD contiguous.
+ *   q,k,v,o,lse  the forward's inputs and outputs (lse exactly as fa_fwd wrote it)
+ *   dout [B][H][Nq][d]  upstream gradient dO
+ *   dq [B][H][Nq][d], dk/dv [B][H][Nk][d]  out, in dtype
+ *   workspace: caller-owned device memory of at least
+ *   fa_bwd_workspace_bytes(...) bytes, 256-byte aligned; contents on entry
+ *   are ignored and on return unspecified.  P is recomputed as
+ *   exp(scale q.k - lse); dS = P * (dP - D) with dP = dO V^T. */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward with explicit {batch, head, seq} element strides for every
+ * d-major tensor (q, k, v, o, dout, dq, dk, dv).  lse and workspace as in
+ * fa_bwd. */
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                   const int64_t q_strides[3], const int64_t k_strides[3],
+                   const int64_t v_strides[3], const int64_t o_strides[3],
+                   const int64_t do_strides[3], const int64_t dq_strides[3],
+                   const int64_t dk_strides[3], const int64_t dv_strides[3],
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stages of the backward, for callers that schedule them themselves.
+ * fa_bwd_strided runs FA_BWD_ALL.  FA_BWD_PREP writes D_i = dO_i . O_i into
+ * the workspace; FA_BWD_DKDV (dK, dV) and FA_BWD_DQ (dQ) read it and are
+ * independent of each other, so after PREP has completed they may run on
+ * two streams at once.  Stages in one call run in the order PREP, DKDV, DQ
+ * on `stream`.  Same arguments and checks as fa_bwd_strided; `stages` is a
+ * nonzero OR of the flags below. */
+enum { FA_BWD_PREP = 1, FA_BWD_DKDV = 2, FA_BWD_DQ = 4, FA_BWD_ALL = 7 };
+int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv,
+                  int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                  const int64_t q_strides[3], const int64_t k_strides[3],
+                  const int64_t v_strides[3], const int64_t o_strides[3],
+                  const int64_t do_strides[3], const int64_t dq_strides[3],
+                  const int64_t dk_strides[3], const int64_t dv_strides[3],
+                  void* workspace, size_t workspace_bytes, int stages, void* stream);
+
+/* Static name of a status code ("FA_OK", ...); "FA_UNKNOWN_STATUS" otherwise. */
+const char* fa_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* fa_last_error_message(void);
+
+/* Library ABI version, currently 1. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,184 @@
+"""C-ABI boundary checks that need no GPU.
+
+libfa.so must load, export every function include/fa.h declares, and reject
+invalid arguments with the documented status codes before it makes any HIP
+call.  Pointers passed here are fake (never dereferenced): every case fails
+validation first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_02_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()), reason="libfa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert set(declared_functions()) == set(fa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_exported_dynamic_symbols_are_c_names():
+    """The symbols are unmangled C names in the dynamic symbol table."""
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.lib_path()], capture_output=True, text=True).stdout
+    names = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in names, name
+
+
+def test_status_strings_and_version():
+    assert fa.fa_abi_version() == 1
+    assert fa.fa_status_string(0) == "FA_OK"
+    assert fa.fa_status_string(1) == "FA_ERR_INVALID_ARG"
+    assert fa.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
+    assert fa.fa_status_string(3) == "FA_ERR_DEVICE"
+    assert fa.fa_status_string(4) == "FA_ERR_LAUNCH"
+    assert fa.fa_status_string(99) == "FA_UNKNOWN_STATUS"
+
+
+def test_workspace_bytes():
+    n = fa.fa_bwd_workspace_bytes(2, 8, 2048, 2048, 64, 0)
+    assert n >= 2 * 8 * 2048 * 4 and n % 256 == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 1, 96, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 1, 64, 7) == 0
+    assert fa.fa_bwd_workspace_bytes(-1, 1, 1, 1, 64, 0) == 0
+
+
+# --- forward validation -------------------------------------------------------
+
+P = lambda a: ctypes.c_void_p(a)  # noqa: E731
+A = 1 << 20  # fake, 16-byte aligned "device" addresses, far apart
+
+
+def fwd(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.125, causal=0, dtype=0):
+    lib = fa.load_library()
+    return lib.fa_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, Nq, Nk, d, scale, causal, dtype, None)
+
+
+def fwd_strided(strides, **kw):
+    lib = fa.load_library()
+    I3 = ctypes.c_int64 * 3
+    s = [I3(*x) for x in strides]
+    a = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.125, causal=0, dtype=0)
+    a.update(kw)
+    return lib.fa_fwd_strided(P(a["q"]), P(a["k"]), P(a["v"]), P(a["o"]), P(a["lse"]), a["B"], a["H"], a["Nq"],
+                              a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], *s, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(v=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(q=A + 2), fa.FA_ERR_INVALID_ARG),          # misaligned
+    (dict(lse=5 * A + 2), fa.FA_ERR_INVALID_ARG),    # misaligned lse
+    (dict(B=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),             # softmax over no keys
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),          # fp32 / unknown
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(o=A), fa.FA_ERR_INVALID_ARG),              # o aliases q
+    (dict(o=A + 1024), fa.FA_ERR_INVALID_ARG),       # o overlaps q
+    (dict(lse=4 * A + 64), fa.FA_ERR_INVALID_ARG),   # lse overlaps o
+])
+def test_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+    assert fa.fa_last_error_message() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Nq=0), dict(Nq=0, Nk=0)])
+def test_fwd_empty_is_ok_without_touching_pointers(kw):
+    assert fwd(q=0, k=0, v=0, o=0, lse=0, **kw) == fa.FA_OK
+
+
+def test_fwd_strided_rejects_bad_strides():
+    good = [(16 * 64, 16 * 64, 64)] * 4
+    bad_mult = [(16 * 64, 16 * 64, 68)] + good[1:]
+    assert fwd_strided(bad_mult) == fa.FA_ERR_INVALID_ARG
+    neg = [(16 * 64, 16 * 64, -64)] + good[1:]
+    assert fwd_strided(neg) == fa.FA_ERR_INVALID_ARG
+    overlap_rows = [(16 * 64, 16 * 64, 32)] + good[1:]
+    assert fwd_strided(overlap_rows) == fa.FA_ERR_INVALID_ARG
+    huge = [(0, 0, 1 << 28)] + good[1:]
+    assert fwd_strided(huge) == fa.FA_ERR_INVALID_ARG  # per-head extent > 2^31 elements
+
+
+# --- backward validation ------------------------------------------------------
+
+def bwd(ws=10 * A, ws_bytes=1 << 16, dq=7 * A, dk=8 * A, dv=9 * A, d=64, Nq=16, Nk=16, dtype=0):
+    lib = fa.load_library()
+    return lib.fa_bwd(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), P(6 * A), P(dq), P(dk), P(dv),
+                      1, 1, Nq, Nk, d, 0.125, 1, dtype, P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=4), fa.FA_ERR_INVALID_ARG),        # too small
+    (dict(ws=10 * A + 16), fa.FA_ERR_INVALID_ARG),    # workspace not 256-aligned
+    (dict(dq=A), fa.FA_ERR_INVALID_ARG),              # dq aliases q
+    (dict(dk=7 * A), fa.FA_ERR_INVALID_ARG),          # dk aliases dq
+    (dict(ws=9 * A), fa.FA_ERR_INVALID_ARG),          # workspace aliases dv
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+])
+def test_bwd_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_stages_rejects_bad_mask():
+    lib = fa.load_library()
+    I3 = ctypes.c_int64 * 3
+    st = [I3(16 * 64, 16 * 64, 64)] * 8
+    for stages in (0, 8, -1, 16):
+        r = lib.fa_bwd_stages(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), P(6 * A), P(7 * A), P(8 * A), P(9 * A),
+                              1, 1, 16, 16, 64, 0.125, 1, 0, *st, P(10 * A), 1 << 16, stages, None)
+        assert r == fa.FA_ERR_INVALID_ARG, stages
+
+
+def test_python_binding_rejects_fp32():
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(fa.FaError) as e:
+        fa.attention_fwd(q, q, q)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+
+
+def _gpu_visible():
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful where no HIP device exists")
+def test_valid_call_without_device_reports_device_error():
+    """Arguments are valid, so the call reaches the device check, which fails
+    here; nothing is launched."""
+    assert fwd() == fa.FA_ERR_DEVICE
