@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (3 times), so a counter "
+                         "profile of this command can calibrate FETCH_SIZE/WRITE_SIZE against known bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -142,6 +145,15 @@ def main():
     def step():
         fa.fa_fwd(q, k, v, o, lse, s, causal, stream)
         fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, stream)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

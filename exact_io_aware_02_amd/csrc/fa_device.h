@@ -123,6 +123,10 @@ __device__ __forceinline__ u32x4 pack_acc8(const f32x16& s, int kk) {
                pack2<DT>(s[o + 6], s[o + 7])};
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// Combine lane i with lane i^32.  (v_permlane32_swap would avoid the LDS
+// round trip of ds_bpermute, but this compiler maps the builtin's second
+// result onto the first one's register, so it cannot be used for this.)
+__device__ __forceinline__ float max_pair32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float sum_pair32(float x) { return x + __shfl_xor(x, 32); }
 
 }  // namespace fa

@@ -55,7 +55,9 @@ struct FwdTile {
   static constexpr int NQB = D == 64 ? 2 : 1;
   static constexpr int QW = 32 * NQB;       // queries per wave
   static constexpr int BM = kWaves * QW;    // queries per workgroup
-  static constexpr int WAVES_PER_SIMD = D == 64 ? 2 : 3;
+  static constexpr int WAVES_PER_SIMD = 2;
+  static constexpr bool UNROLL_RING = false;  // true: constant slot addresses (but spills at d=128)
+  static constexpr int QK_LOOKAHEAD = 4;     // K operand reads issued ahead of their MFMAs
 };
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
@@ -116,11 +118,10 @@ __device__ __forceinline__ float dot2_sum<DT_BF16>(uint32_t packed, float acc) {
 }
 
 // S^T (32 keys x 64 queries) of one tile: A = K rows from LDS, B = Q^T.
-// The issue order is pinned (two operand reads ahead, then two MFMAs per
-// read) so at most three K operands are live: the scheduler would otherwise
-// hoist all of them and overflow the 256-register budget of two waves per
-// SIMD, where the other wave already covers the LDS latency.
-template <int D, int DT, int kNQB>
+// The issue order is pinned (LA operand reads ahead, then the MFMAs of one
+// k-step per read) so at most LA + 1 K operands are live: the scheduler
+// would otherwise hoist all of them.
+template <int D, int DT, int kNQB, int LA = FwdTile<D>::QK_LOOKAHEAD>
 __device__ __forceinline__ void qk(f32x16 (&s)[kNQB], const uint16_t* Kt, const u32x4 (&qf)[kNQB][D / 16], int col,
                                    int half) {
   constexpr int KS = D / 16;
@@ -132,13 +133,13 @@ __device__ __forceinline__ void qk(f32x16 (&s)[kNQB], const uint16_t* Kt, const 
 #pragma unroll
     for (int nb = 0; nb < kNQB; ++nb) s[nb] = mfma32<DT>(a, qf[nb][ks], s[nb]);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read x2
+  __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS read x LA
 #pragma unroll
-  for (int i = 0; i < KS - 2; ++i) {
+  for (int i = 0; i < KS - LA; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, kNQB, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2 * kNQB, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, LA * kNQB, 0);
 }
 
 template <int kNQB>
@@ -193,7 +194,7 @@ __device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __rest
     float mx = s[nb][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_pair32(mx);
     mxc[nb] = mx * c;
     raise |= mxc[nb] > st.m[nb] + kRescaleSlack;
   }
@@ -224,8 +225,8 @@ __device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __rest
         const float p1 = exp2_fast(__builtin_fmaf(s[nb][r + 1], c, mneg));
         w[e] = pack2<DT>(p0, p1);
         if constexpr (DT == DT_BF16) {  // bf16 rounding (2^-9) is too coarse for the normaliser
-          ls0 += p0;
-          ls1 += p1;
+          ls0 = (r == 0) ? p0 : ls0 + p0;
+          ls1 = (r == 0) ? p1 : ls1 + p1;
         }
       }
       if constexpr (DT == DT_F16) {  // fp16-rounded P is accurate enough: sum pairs in one op
@@ -339,21 +340,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   wait_loads();
   lds_barrier();
 
-  int buf = 0;
-  for (int j = 0; j < n_kt; ++j) {
-    // prefetch tile j+2 into the slot tile j-1 used (free since the last barrier)
-    int nbuf = buf + 2;
-    nbuf = nbuf >= NBUF ? nbuf - NBUF : nbuf;
-    fwd_iter<D, DT, CAUSAL>(j, n_kt, Ks[buf], Vs[buf], Ks[nbuf], Vs[nbuf], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st,
-                            p.Nk, qw0, c, lane, wave);
-    buf = buf + 1 >= NBUF ? 0 : buf + 1;
+  static_assert(NBUF == 3, "the loops below assume a 3-slot ring");
+  if constexpr (FwdTile<D>::UNROLL_RING) {
+    // unrolled by the ring depth: every slot address is a compile-time
+    // constant, folded into the LDS instructions' offsets
+    for (int j = 0; j < n_kt; j += 3) {
+      fwd_iter<D, DT, CAUSAL>(j, n_kt, Ks[0], Vs[0], Ks[2], Vs[2], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk,
+                              qw0, c, lane, wave);
+      if (j + 1 >= n_kt) break;
+      fwd_iter<D, DT, CAUSAL>(j + 1, n_kt, Ks[1], Vs[1], Ks[0], Vs[0], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st,
+                              p.Nk, qw0, c, lane, wave);
+      if (j + 2 >= n_kt) break;
+      fwd_iter<D, DT, CAUSAL>(j + 2, n_kt, Ks[2], Vs[2], Ks[1], Vs[1], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st,
+                              p.Nk, qw0, c, lane, wave);
+    }
+  } else {
+    int buf = 0;
+    for (int j = 0; j < n_kt; ++j) {
+      // prefetch tile j+2 into the slot tile j-1 used (free since the last barrier)
+      int nbuf = buf + 2;
+      nbuf = nbuf >= NBUF ? nbuf - NBUF : nbuf;
+      fwd_iter<D, DT, CAUSAL>(j, n_kt, Ks[buf], Vs[buf], Ks[nbuf], Vs[nbuf], krs, vrs, krow, vrow, ktb, vtb, qf, acc,
+                              st, p.Nk, qw0, c, lane, wave);
+      buf = buf + 1 >= NBUF ? 0 : buf + 1;
+    }
   }
 
   // ---- epilogue: O = O^T / l, LSE
   uint16_t* op = p.o + b * p.so.b + h * p.so.h;
 #pragma unroll
   for (int nb = 0; nb < kNQB; ++nb) {
-    const float lt = st.l[nb] + xor32(st.l[nb]);
+    const float lt = sum_pair32(st.l[nb]);
     const int qi = qw0 + 32 * nb + col;
     if (qi < p.Nq) {
       const float inv = 1.0f / lt;
