@@ -189,8 +189,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || (d != 64 && d != 128) || (dtype != FA_FP16 && dtype != FA_BF16)) return 0;
-  const size_t n = (size_t)B * (size_t)H * (size_t)Nq * sizeof(float);
-  return (n + 255) & ~(size_t)255;
+  return fa::bwd_workspace_bytes(B, H, Nq);
 }
 
 int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -248,6 +247,7 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
   p.dsum = static_cast<float*>(workspace);
+  p.lse2 = fa::bwd_lse2_region(workspace, B, H, Nq);
   p.sq = {q_strides[0], q_strides[1], q_strides[2]};
   p.sk = {k_strides[0], k_strides[1], k_strides[2]};
   p.sv = {v_strides[0], v_strides[1], v_strides[2]};

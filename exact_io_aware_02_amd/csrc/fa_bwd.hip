@@ -9,17 +9,21 @@
 //   dK = scale dS^T Q  dQ = scale dS K
 //
 // Three kernels, deterministic (no atomics):
-//   dsum_kernel  D_i = dO_i . O_i                       (HBM bound, tiny)
-//   dkdv_kernel  one workgroup per 128 keys; loops over 64-query tiles;
-//                K and V stay in registers, Q / dO / lse / D tiles stream
-//                through LDS double buffered.  S = Q K^T and dP = dO V^T
-//                come out with a key per lane, which is exactly the B
-//                operand layout for dV^T += dO^T P and dK^T += Q^T dS; the
-//                transposed A operands (dO^T, Q^T) are read from the
-//                untransposed LDS tiles with ds_read_b64_tr_b16.
-//   dq_kernel    one workgroup per 128 queries; loops over 64-key tiles
-//                like the forward; S^T and dP^T have a query per lane;
-//                dQ^T += K^T dS^T with K^T read transposed from LDS.
+//   prep_kernel  D_i = dO_i . O_i and lse_i * log2(e) per query row, into
+//                the workspace (HBM bound, tiny).
+//   dkdv_kernel  a workgroup owns 128 keys (32 per wave) with K and V held
+//                in registers; 32-query tiles of Q, dO and the two row
+//                statistics stream HBM -> LDS through a 3-slot ring.
+//                S = Q K^T and dP = dO V^T come out with a key per lane,
+//                which is the B-operand layout of dV^T += dO^T P and
+//                dK^T += Q^T dS; the transposed A operands (dO^T, Q^T) are
+//                read from the same untransposed LDS tiles with
+//                ds_read_b64_tr_b16.
+//   dq_kernel    a workgroup owns 128 queries (32 per wave) with Q and dO
+//                in registers; 32-key tiles of K and V stream through a
+//                3-slot ring like the forward.  S^T and dP^T have a query
+//                per lane (its lse and D are lane-local); dQ^T += K^T dS^T
+//                reads K^T transposed from the K tile.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -29,6 +33,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kT = 32;        // rows per streamed tile (queries in dkdv, keys in dq)
+constexpr int kNBuf = 3;      // ring slots: tile t+2 loads while tile t is computed
+constexpr int kStatPad = 64;  // per-(b,h) stride of the workspace statistics, rounded up to this
 
 template <int DT>
 __device__ __forceinline__ float lo_f32(uint32_t w);
@@ -51,9 +58,11 @@ __device__ __forceinline__ float hi_f32<DT_BF16>(uint32_t w) {
   return __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
-// ------------------------------------------------------------ D = rowsum(dO * O)
+__host__ __device__ __forceinline__ int stat_stride(int Nq) { return (Nq + kStatPad - 1) / kStatPad * kStatPad; }
+
+// ------------------------------------------------------------ D and lse*log2(e)
 template <int D, int DT>
-__global__ __launch_bounds__(kThreads) void dsum_kernel(BwdParams p, int blocks_per_bh) {
+__global__ __launch_bounds__(kThreads) void prep_kernel(BwdParams p, int blocks_per_bh) {
   constexpr int CH = D / 8;
   constexpr int RPB = kThreads / CH;
   const int bh = blockIdx.x / blocks_per_bh;
@@ -70,11 +79,17 @@ __global__ __launch_bounds__(kThreads) void dsum_kernel(BwdParams p, int blocks_
   }
 #pragma unroll
   for (int off = CH / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (ch == 0 && row < p.Nq) p.dsum[(int64_t)bh * p.Nq + row] = acc;
+  // rows in [Nq, stat_stride) get zeros: the kernels then treat them as
+  // queries with zero Q/dO rows, which contribute nothing
+  if (ch == 0 && row < stat_stride(p.Nq)) {
+    const int64_t o = (int64_t)bh * stat_stride(p.Nq) + row;
+    p.dsum[o] = acc;
+    p.lse2[o] = row < p.Nq ? p.lse[(int64_t)bh * p.Nq + row] * kLog2e : 0.f;
+  }
 }
 
-// Write a [d x 32] fp32 accumulator block column (one row of the output per
-// lane) as 4-element groups: out row `row`, columns 32*db + acc_row(half, r).
+// Write a [d x 32] fp32 accumulator block column (one output row per lane)
+// as 4-element groups: columns 32*db + acc_row(half, r) of row `rowp`.
 template <int DT, int DB>
 __device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16 (&acc)[DB], float mul, int half) {
 #pragma unroll
@@ -89,26 +104,46 @@ __device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16 (&acc)[D
     }
 }
 
+// 32x32 accumulator = rows of a row-major LDS tile (32 rows) times B held in
+// registers, contracting over d.
+template <int D, int DT>
+__device__ __forceinline__ f32x16 rows_times_regs(const uint16_t* tile, const u32x4 (&bf)[D / 16], int col, int half) {
+  f32x16 s = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) s = mfma32<DT>(load_rowmajor_op<D>(tile, col, ks, half), bf[ks], s);
+  return s;
+}
+
+// acc[db] += tile^T (d x 32 tile rows, read transposed) x B (32 tile rows x
+// 32, packed from a 32x32 accumulator in its register k order).
+template <int D, int DT>
+__device__ __forceinline__ void tile_t_times(f32x16 (&acc)[D / 32], const uint16_t* tile, const u32x4 (&bp)[2],
+                                             int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      acc[db] = mfma32<DT>(load_transposed_a<D>(tile, lane, kk * 16, db), bp[kk], acc[db]);
+}
+
 // ------------------------------------------------------------ dK, dV
 template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdParams p) {
-  constexpr int KW = 32;                // keys per wave
-  constexpr int BNK = kWaves * KW;      // keys per workgroup
-  constexpr int BMQ = 64;               // queries per streamed tile
-  constexpr int QB = BMQ / 32;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(BwdParams p) {
+  constexpr int KW = 32;            // keys per wave
+  constexpr int BNK = kWaves * KW;  // keys per workgroup
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int CH = D / 8;
-  constexpr int RPP = kThreads / CH;
-  constexpr int PASSES = BMQ / RPP;
+  using TC = TileCopyT<D, kT, kWaves>;
+  constexpr int NLOADS = 2 * TC::NI + 2;  // per wave per tile: Q, dO, 8 lse2 and 8 D values
 
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BMQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[2][BMQ * D];  // dO tile
-  __shared__ __attribute__((aligned(16))) float Ls[2][BMQ];         // lse * log2(e), +inf past Nq
-  __shared__ __attribute__((aligned(16))) float Dsm[2][BMQ];        // D_i
+  __shared__ __attribute__((aligned(1024))) uint16_t Qs[kNBuf][kT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Os[kNBuf][kT * D];  // dO
+  __shared__ __attribute__((aligned(16))) float Ls[kNBuf][kT];           // lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float Dsm[kNBuf][kT];          // D
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
+  const int lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = p.B * p.H;
   const int t = blockIdx.x;
   const int kt = t / BH;  // ascending key tiles: the causal-heaviest first
@@ -120,11 +155,27 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdParams p) {
 
   const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h;
   const uint16_t* dop = p.dout + b * p.sdo.b + h * p.sdo.h;
-  const float* lsep = p.lse + (int64_t)bh * p.Nq;
-  const float* dsp = p.dsum + (int64_t)bh * p.Nq;
+  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(qp, p.Nq, p.sq.s, D);
+  const __amdgpu_buffer_rsrc_t ors = head_rsrc(dop, p.Nq, p.sdo.s, D);
+  const int sst = stat_stride(p.Nq);
+  const __amdgpu_buffer_rsrc_t lrs = f32_rsrc(p.lse2 + (int64_t)bh * sst, sst);
+  const __amdgpu_buffer_rsrc_t drs = f32_rsrc(p.dsum + (int64_t)bh * sst, sst);
+  const uint32_t qrow = (uint32_t)(p.sq.s * 2), orow = (uint32_t)(p.sdo.s * 2);
 
-  // K and V of this wave's keys as B operands (K^T, V^T): lane holds
-  // row `key`, columns 16*ks + 8*half .. +7.
+  const int qt0 = CAUSAL ? (k0 / kT) : 0;
+  const int n_qt = (p.Nq + kT - 1) / kT;
+
+  auto issue = [&](int it, int slot) {
+    TC::issue(qrs, qrow, (uint32_t)it * kT * qrow, Qs[slot], lane, wave);
+    TC::issue(ors, orow, (uint32_t)it * kT * orow, Os[slot], lane, wave);
+    vec_to_lds<8>(lrs, (uint32_t)(it * kT + 8 * wave) * 4, Ls[slot] + 8 * wave, lane);
+    vec_to_lds<8>(drs, (uint32_t)(it * kT + 8 * wave) * 4, Dsm[slot] + 8 * wave, lane);
+  };
+  if (qt0 < n_qt) issue(qt0, 0);
+  if (qt0 + 1 < n_qt) issue(qt0 + 1, 1);
+
+  // K^T and V^T of this wave's keys as B operands: lane holds row `key`,
+  // columns 16*ks + 8*half .. +7 (zeros past Nk).
   u32x4 kf[KS], vf[KS];
   {
     const uint16_t* kp = p.k + b * p.sk.b + h * p.sk.h;
@@ -140,46 +191,6 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdParams p) {
       vf[ks] = y;
     }
   }
-
-  const int qt0 = CAUSAL ? (k0 / BMQ) : 0;
-  const int n_qt = (p.Nq + BMQ - 1) / BMQ;
-
-  u32x4 qreg[PASSES], oreg[PASSES];
-  float lreg = 0.f, dreg = 0.f;
-  const int lrow = tid / CH, lch = tid % CH;
-  auto load_tile = [&](int it) {
-    const int i0 = it * BMQ;
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int q = i0 + lrow + i * RPP;
-      u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
-      if (q < p.Nq) {
-        x = *(const u32x4*)(qp + q * p.sq.s + lch * 8);
-        y = *(const u32x4*)(dop + q * p.sdo.s + lch * 8);
-      }
-      qreg[i] = x;
-      oreg[i] = y;
-    }
-    if (tid < BMQ) {
-      const int q = i0 + tid;
-      lreg = q < p.Nq ? lsep[q] * kLog2e : __builtin_inff();
-      dreg = q < p.Nq ? dsp[q] : 0.f;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int r = lrow + i * RPP;
-      const int off = r * D + ((lch ^ swz<D>(r)) << 3);
-      *(u32x4*)(&Qs[buf][off]) = qreg[i];
-      *(u32x4*)(&Os[buf][off]) = oreg[i];
-    }
-    if (tid < BMQ) {
-      Ls[buf][tid] = lreg;
-      Dsm[buf][tid] = dreg;
-    }
-  };
-
   f32x16 adk[DB], adv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -188,75 +199,55 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdParams p) {
   }
   const float c = p.c;
 
-  if (qt0 < n_qt) {
-    load_tile(qt0);
-    store_tile(0);
-  }
-  __syncthreads();
+  wait_loads();
+  lds_barrier();
 
+  int slot = 0;
   for (int it = qt0; it < n_qt; ++it) {
-    const int buf = (it - qt0) & 1;
-    const int i0 = it * BMQ;
-    if (it + 1 < n_qt) load_tile(it + 1);
+    const int i0 = it * kT;
+    int nslot = slot + 2;
+    nslot = nslot >= kNBuf ? nslot - kNBuf : nslot;
+    if (it + 2 < n_qt) issue(it + 2, nslot);
 
-    const bool active = kw0 < p.Nk && !(CAUSAL && i0 + BMQ - 1 < kw0);
+    // Queries past Nq read as zero rows with zero statistics, so they add
+    // nothing to dK or dV; keys past Nk are never written.
+    const bool active = kw0 < p.Nk && !(CAUSAL && i0 + kT - 1 < kw0);
     if (active) {
-      const uint16_t* Qt = Qs[buf];
-      const uint16_t* Ot = Os[buf];
-      f32x16 s[QB], dp[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const u32x4 aq = load_rowmajor_op<D>(Qt, qb * 32 + col, ks, half);
-          const u32x4 ao = load_rowmajor_op<D>(Ot, qb * 32 + col, ks, half);
-          s[qb] = mfma32<DT>(aq, kf[ks], s[qb]);
-          dp[qb] = mfma32<DT>(ao, vf[ks], dp[qb]);
-        }
-      // P and dS; rows are queries i0 + 32*qb + acc_row(half, r).
+      const uint16_t* Qt = Qs[slot];
+      const uint16_t* Ot = Os[slot];
+      // S = Q K^T and dP = dO V^T: rows are queries i0 + acc_row(half, r); column = this lane's key
+      f32x16 s = rows_times_regs<D, DT>(Qt, kf, col, half);
+      f32x16 dp = rows_times_regs<D, DT>(Ot, vf, col, half);
       const bool need_mask = CAUSAL && (i0 < kw0 + KW - 1);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int rq = 8 * g4 + 4 * half;
+        const float4 lv = *(const float4*)(&Ls[slot][rq]);
+        const float4 dv = *(const float4*)(&Dsm[slot][rq]);
+        const float lz[4] = {lv.x, lv.y, lv.z, lv.w};
+        const float dz[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int rq = qb * 32 + 8 * g4 + 4 * half;
-          const float4 lv = *(const float4*)(&Ls[buf][rq]);
-          const float4 dv = *(const float4*)(&Dsm[buf][rq]);
-          const float lz[4] = {lv.x, lv.y, lv.z, lv.w};
-          const float dz[4] = {dv.x, dv.y, dv.z, dv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            float pv = exp2_fast(__builtin_fmaf(s[qb][r], c, -lz[e]));
-            if (need_mask && key > i0 + rq + e) pv = 0.f;
-            s[qb][r] = pv;
-            dp[qb][r] = pv * (dp[qb][r] - dz[e]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float pv = exp2_fast(__builtin_fmaf(s[r], c, -lz[e]));
+          if (need_mask && key > i0 + rq + e) pv = 0.f;
+          s[r] = pv;
+          dp[r] = pv * (dp[r] - dz[e]);
         }
-      // dV^T += dO^T P ; dK^T += Q^T dS   (k runs over this tile's queries)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const u32x4 bp = pack_acc8<DT>(s[qb], kk);
-          const u32x4 bd = pack_acc8<DT>(dp[qb], kk);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const u32x4 ao = load_transposed_a<D>(Ot, lane, qb * 32 + kk * 16, db);
-            adv[db] = mfma32<DT>(ao, bp, adv[db]);
-            const u32x4 aq = load_transposed_a<D>(Qt, lane, qb * 32 + kk * 16, db);
-            adk[db] = mfma32<DT>(aq, bd, adk[db]);
-          }
-        }
+      }
+      const u32x4 bp[2] = {pack_acc8<DT>(s, 0), pack_acc8<DT>(s, 1)};
+      const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
+      tile_t_times<D, DT>(adv, Ot, bp, lane);  // dV^T += dO^T P
+      tile_t_times<D, DT>(adk, Qt, bd, lane);  // dK^T += Q^T dS
     }
 
-    if (it + 1 < n_qt) store_tile(buf ^ 1);
-    __syncthreads();
+    if (it + 2 < n_qt) {
+      wait_vmcnt<NLOADS>();
+    } else {
+      wait_loads();
+    }
+    lds_barrier();
+    slot = slot + 1 >= kNBuf ? 0 : slot + 1;
   }
 
   if (key < p.Nk) {
@@ -267,22 +258,19 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdParams p) {
 
 // ------------------------------------------------------------ dQ
 template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(BwdParams p) {
   constexpr int QW = 32;
   constexpr int BM = kWaves * QW;
-  constexpr int BN = 64;
-  constexpr int RB = BN / 32;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int CH = D / 8;
-  constexpr int RPP = kThreads / CH;
-  constexpr int PASSES = BN / RPP;
+  using TC = TileCopyT<D, kT, kWaves>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[kNBuf][kT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[kNBuf][kT * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
+  const int lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int BH = p.B * p.H;
   const int n_qt = (p.Nq + BM - 1) / BM;
   const int t = blockIdx.x;
@@ -295,7 +283,22 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p) {
 
   const uint16_t* kp = p.k + b * p.sk.b + h * p.sk.h;
   const uint16_t* vp = p.v + b * p.sv.b + h * p.sv.h;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(kp, p.Nk, p.sk.s, D);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vp, p.Nk, p.sv.s, D);
+  const uint32_t krow = (uint32_t)(p.sk.s * 2), vrow = (uint32_t)(p.sv.s * 2);
 
+  int kend = p.Nk;
+  if (CAUSAL) kend = min(p.Nk, min(q0 + BM, p.Nq));
+  const int n_kt = (kend + kT - 1) / kT;
+
+  auto issue = [&](int j, int slot) {
+    TC::issue(krs, krow, (uint32_t)j * kT * krow, Ks[slot], lane, wave);
+    TC::issue(vrs, vrow, (uint32_t)j * kT * vrow, Vs[slot], lane, wave);
+  };
+  if (n_kt > 0) issue(0, 0);
+  if (n_kt > 1) issue(1, 1);
+
+  // Q^T and dO^T of this wave's queries as B operands (zeros past Nq).
   u32x4 qf[KS], of[KS];
   {
     const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h;
@@ -311,99 +314,53 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p) {
       of[ks] = y;
     }
   }
-  const float lse2 = qi < p.Nq ? p.lse[(int64_t)bh * p.Nq + qi] * kLog2e : __builtin_inff();
-  const float dsv = qi < p.Nq ? p.dsum[(int64_t)bh * p.Nq + qi] : 0.f;
-
-  int kend = p.Nk;
-  if (CAUSAL) kend = min(p.Nk, min(q0 + BM, p.Nq));
-  const int n_kt = (kend + BN - 1) / BN;
-
-  u32x4 kreg[PASSES], vreg[PASSES];
-  const int lrow = tid / CH, lch = tid % CH;
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int kk = j * BN + lrow + i * RPP;
-      u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
-      if (kk < p.Nk) {
-        x = *(const u32x4*)(kp + kk * p.sk.s + lch * 8);
-        y = *(const u32x4*)(vp + kk * p.sv.s + lch * 8);
-      }
-      kreg[i] = x;
-      vreg[i] = y;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int r = lrow + i * RPP;
-      const int off = r * D + ((lch ^ swz<D>(r)) << 3);
-      *(u32x4*)(&Ks[buf][off]) = kreg[i];
-      *(u32x4*)(&Vs[buf][off]) = vreg[i];
-    }
-  };
+  const int sst = stat_stride(p.Nq);
+  const float lse2 = qi < p.Nq ? p.lse2[(int64_t)bh * sst + qi] : __builtin_inff();
+  const float dsv = qi < p.Nq ? p.dsum[(int64_t)bh * sst + qi] : 0.f;
 
   f32x16 adq[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) adq[db] = f32x16{};
   const float c = p.c;
 
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  wait_loads();
+  lds_barrier();
 
+  int slot = 0;
   for (int j = 0; j < n_kt; ++j) {
-    const int buf = j & 1;
-    const int j0 = j * BN;
-    if (j + 1 < n_kt) load_tile(j + 1);
+    const int j0 = j * kT;
+    int nslot = slot + 2;
+    nslot = nslot >= kNBuf ? nslot - kNBuf : nslot;
+    if (j + 2 < n_kt) issue(j + 2, nslot);
+
     const bool active = qw0 < p.Nq && !(CAUSAL && j0 > qw0 + QW - 1);
     if (active) {
-      const uint16_t* Kt = Ks[buf];
-      const uint16_t* Vt = Vs[buf];
-      f32x16 s[RB], dp[RB];
+      const uint16_t* Kt = Ks[slot];
+      const uint16_t* Vt = Vs[slot];
+      // S^T = K Q^T and dP^T = V dO^T: rows are keys j0 + acc_row(half, r); column = this lane's query
+      f32x16 s = rows_times_regs<D, DT>(Kt, qf, col, half);
+      f32x16 dp = rows_times_regs<D, DT>(Vt, of, col, half);
+      const bool need_mask = (j0 + kT > p.Nk) || (CAUSAL && j0 + kT - 1 > qw0);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        s[rb] = f32x16{};
-        dp[rb] = f32x16{};
+      for (int r = 0; r < 16; ++r) {
+        float pv = exp2_fast(__builtin_fmaf(s[r], c, -lse2));
+        if (need_mask) {
+          const int kk = j0 + acc_row(half, r);
+          if (kk >= p.Nk || (CAUSAL && kk > qi)) pv = 0.f;
+        }
+        dp[r] = pv * (dp[r] - dsv);
       }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const u32x4 ak = load_rowmajor_op<D>(Kt, rb * 32 + col, ks, half);
-          const u32x4 av = load_rowmajor_op<D>(Vt, rb * 32 + col, ks, half);
-          s[rb] = mfma32<DT>(ak, qf[ks], s[rb]);
-          dp[rb] = mfma32<DT>(av, of[ks], dp[rb]);
-        }
-      const bool need_mask = (j0 + BN > p.Nk) || (CAUSAL && j0 + BN - 1 > qw0);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = exp2_fast(__builtin_fmaf(s[rb][r], c, -lse2));
-          if (need_mask) {
-            const int kk = j0 + rb * 32 + acc_row(half, r);
-            if (kk >= p.Nk || (CAUSAL && kk > qi)) pv = 0.f;
-          }
-          dp[rb][r] = pv * (dp[rb][r] - dsv);
-        }
-      // dQ^T += K^T dS^T  (k runs over this tile's keys)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const u32x4 bd = pack_acc8<DT>(dp[rb], kk);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const u32x4 ak = load_transposed_a<D>(Kt, lane, rb * 32 + kk * 16, db);
-            adq[db] = mfma32<DT>(ak, bd, adq[db]);
-          }
-        }
+      const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
+      tile_t_times<D, DT>(adq, Kt, bd, lane);  // dQ^T += K^T dS^T
     }
-    if (j + 1 < n_kt) store_tile(buf ^ 1);
-    __syncthreads();
+
+    if (j + 2 < n_kt) {
+      wait_vmcnt<2 * TC::NI>();
+    } else {
+      wait_loads();
+    }
+    lds_barrier();
+    slot = slot + 1 >= kNBuf ? 0 : slot + 1;
   }
 
   if (qi < p.Nq) store_rows<DT, DB>(p.dq + b * p.sdq.b + h * p.sdq.h + qi * p.sdq.s, adq, p.scale, half);
@@ -413,14 +370,14 @@ template <int D, int DT, bool CAUSAL>
 hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
   const int64_t BH = (int64_t)p.B * p.H;
   constexpr int RPB = kThreads / (D / 8);
-  const int64_t dsum_bpb = (p.Nq + RPB - 1) / RPB;
-  const int64_t g0 = dsum_bpb * BH;
+  const int64_t prep_bpb = (stat_stride(p.Nq) + RPB - 1) / RPB;
+  const int64_t g0 = prep_bpb * BH;
   const int64_t g1 = (int64_t)((p.Nk + 127) / 128) * BH;
   const int64_t g2 = (int64_t)((p.Nq + 127) / 128) * BH;
   if (g0 > 0x7fffffff || g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipError_t e = hipSuccess;
   if ((stages & 1) && g0 > 0) {  // Nq may be 0 (then dK = dV = 0 and there is no dQ)
-    hipLaunchKernelGGL((dsum_kernel<D, DT>), dim3((unsigned)g0), dim3(kThreads), 0, stream, p, (int)dsum_bpb);
+    hipLaunchKernelGGL((prep_kernel<D, DT>), dim3((unsigned)g0), dim3(kThreads), 0, stream, p, (int)prep_bpb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((stages & 2) && g1 > 0) {
@@ -440,6 +397,16 @@ hipError_t launch_dc(const BwdParams& p, bool causal, int stages, hipStream_t st
 }
 
 }  // namespace
+
+size_t bwd_workspace_bytes(int B, int H, int Nq) {
+  // D and lse*log2(e): two fp32 arrays of stat_stride(Nq) values per (b, h)
+  const size_t n = (size_t)B * (size_t)H * (size_t)stat_stride(Nq) * sizeof(float) * 2;
+  return (n + 255) & ~(size_t)255;
+}
+
+float* bwd_lse2_region(void* workspace, int B, int H, int Nq) {
+  return static_cast<float*>(workspace) + (size_t)B * (size_t)H * (size_t)stat_stride(Nq);
+}
 
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool causal, int stages, hipStream_t stream) {
   if (d == 64)

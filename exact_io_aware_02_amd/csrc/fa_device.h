@@ -129,4 +129,74 @@ __device__ __forceinline__ u32x4 pack_acc8(const f32x16& s, int kk) {
 __device__ __forceinline__ float max_pair32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float sum_pair32(float x) { return x + __shfl_xor(x, 32); }
 
+// ---------------------------------------------------------------- HBM -> LDS
+
+// Buffer resource over one head's rows of a [N][d] 16-bit tensor with row
+// stride `stride` elements: loads past row n-1 return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int n, int64_t stride, int d) {
+  const int bytes = (int)(((int64_t)(n - 1) * stride + d) * 2);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
+// Buffer resource over n fp32 values (zeros past the end).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f32_rsrc(const float* base, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n * 4, 0x00020000);
+}
+
+// Asynchronous copies of ROWS consecutive rows of one head's [N][D] tensor
+// into a swizzled [ROWS][D] LDS tile, spread over WAVES waves.  Each wave
+// instruction moves 1 KiB: lane i fills LDS bytes 16*i .. 16*i+15 of its
+// block, so it fetches the global 16-byte chunk whose swizzled home is that
+// slot (buffer_load ... lds; no registers are staged).
+template <int D, int ROWS, int WAVES>
+struct TileCopyT {
+  static constexpr int CH = D / 8;               // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;            // rows per wave instruction
+  static constexpr int NI = ROWS / RPI / WAVES;  // instructions per wave per tile
+  static_assert(NI >= 1 && NI * RPI * WAVES == ROWS, "tile must split evenly over the waves");
+
+  // row_bytes: the tensor's row stride in bytes; tile_byte_off: byte offset
+  // of the tile's first row (both wave-uniform).
+  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t tile_byte_off,
+                                               uint16_t* lds, int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (wave * NI + i) * RPI + lane / CH;
+      const int c = (lane % CH) ^ swz<D>(r);
+      const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(c * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds + (wave * NI + i) * RPI * D), 16, voff, tile_byte_off, 0,
+          0);
+    }
+  }
+};
+
+// Asynchronous copy of N fp32 values (N a multiple of 4, at most 256) into
+// LDS by one wave; lanes past N/4 are idle.
+template <int N>
+__device__ __forceinline__ void vec_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, float* lds, int lane) {
+  static_assert(N % 4 == 0 && N <= 256, "vector copy size");
+  if (lane < N / 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, lane * 16, byte_off,
+                                             0, 0);
+}
+
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+// vmcnt(n): wait until at most n vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those make every wave wait for all of its outstanding HBM->LDS copies,
+// including the prefetch that should stay in flight.  Ordering of the LDS
+// rings comes from the explicit vmcnt waits before it; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace fa

@@ -61,49 +61,8 @@ struct FwdTile {
 };
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
-// Asynchronous copies of key rows [j0, j0 + kBN) of one head's [N][D]
-// K or V into a swizzled LDS tile.  Each wave instruction moves 1 KiB:
-// lane i fills LDS bytes 16*i .. 16*i+15 of its block, so it fetches the
-// global 16-byte chunk whose swizzled home is that slot.  The buffer
-// resource bounds the head's rows, so rows past the end read as zeros.
 template <int D>
-struct TileCopy {
-  static constexpr int CH = D / 8;               // 16-byte chunks per row
-  static constexpr int RPI = 64 / CH;            // rows per wave instruction
-  static constexpr int NI = kBN / RPI / kWaves;  // instructions per wave per tile
-
-  // row_bytes: the tensor's row stride in bytes (uniform).
-  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t tile_byte_off,
-                                               uint16_t* lds, int lane, int wave) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = (wave * NI + i) * RPI + lane / CH;
-      const int c = (lane % CH) ^ swz<D>(r);
-      const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(c * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(lds + (wave * NI + i) * RPI * D), 16, voff, tile_byte_off, 0,
-          0);
-    }
-  }
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int n, int64_t stride, int d) {
-  const int bytes = (int)(((int64_t)(n - 1) * stride + d) * 2);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-
-// Workgroup barrier without the release/acquire fences of __syncthreads():
-// those make every wave wait for all of its outstanding HBM->LDS copies,
-// including the prefetch that should stay in flight.  Ordering of the LDS
-// ring comes from the explicit vmcnt waits before it; the empty asm
-// statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+using TileCopy = TileCopyT<D, kBN, kWaves>;
 
 template <int DT>
 __device__ __forceinline__ float dot2_sum(uint32_t packed, float acc);
@@ -251,7 +210,7 @@ __device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __rest
 
   // tile j+1 (issued one step earlier) must have landed; tile j+2 may fly on
   if (j + 2 < n_kt) {
-    __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * TC::NI));  // vmcnt(2*NI)
+    wait_vmcnt<2 * TC::NI>();
   } else {
     wait_loads();
   }

@@ -32,7 +32,8 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dsum;  // workspace: D_i = dO_i . O_i, fp32 [B][H][Nq]
+  float* dsum;  // workspace: D_i = dO_i . O_i, fp32, rows padded per (b, h)
+  float* lse2;  // workspace: lse_i * log2(e), same layout
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, Nq, Nk;
   float scale;  // the softmax scale as given
@@ -42,7 +43,11 @@ struct BwdParams {
 // Return hipSuccess or the launch error.  d in {64,128}, dtype 0 = fp16,
 // 1 = bf16; the caller has validated every argument.
 hipError_t launch_fwd(const FwdParams& p, int d, int dtype, bool causal, hipStream_t stream);
-// stages: OR of 1 (D = rowsum(dO*O)), 2 (dK, dV), 4 (dQ), run in that order.
+// Backward workspace: the two per-row statistics (D and lse * log2 e), each
+// B*H rows of Nq rounded up to 64 fp32 values.
+size_t bwd_workspace_bytes(int B, int H, int Nq);
+float* bwd_lse2_region(void* workspace, int B, int H, int Nq);
+// stages: OR of 1 (row statistics), 2 (dK, dV), 4 (dQ), run in that order.
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool causal, int stages, hipStream_t stream);
 
 }  // namespace fa
