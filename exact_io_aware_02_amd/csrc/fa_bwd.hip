@@ -104,11 +104,11 @@ __device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16 (&acc)[D
     }
 }
 
-// 32x32 accumulator = rows of a row-major LDS tile (32 rows) times B held in
-// registers, contracting over d.
+// 32x32 accumulator = init + rows of a row-major LDS tile (32 rows) times B
+// held in registers, contracting over d.
 template <int D, int DT>
-__device__ __forceinline__ f32x16 rows_times_regs(const uint16_t* tile, const u32x4 (&bf)[D / 16], int col, int half) {
-  f32x16 s = f32x16{};
+__device__ __forceinline__ f32x16 rows_times_regs(const uint16_t* tile, const u32x4 (&bf)[D / 16], int col, int half,
+                                                  f32x16 s = f32x16{}) {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) s = mfma32<DT>(load_rowmajor_op<D>(tile, col, ks, half), bf[ks], s);
   return s;
@@ -217,22 +217,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const uint16_t* Ot = Os[slot];
       // S = Q K^T and dP = dO V^T: rows are queries i0 + acc_row(half, r); column = this lane's key
       f32x16 s = rows_times_regs<D, DT>(Qt, kf, col, half);
-      f32x16 dp = rows_times_regs<D, DT>(Ot, vf, col, half);
+      // dP - D in one pass: the dP accumulator starts at -D of its row
+      f32x16 dinit;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 dv = *(const float4*)(&Dsm[slot][8 * g4 + 4 * half]);
+        dinit[4 * g4 + 0] = -dv.x;
+        dinit[4 * g4 + 1] = -dv.y;
+        dinit[4 * g4 + 2] = -dv.z;
+        dinit[4 * g4 + 3] = -dv.w;
+      }
+      f32x16 dp = rows_times_regs<D, DT>(Ot, vf, col, half, dinit);
       const bool need_mask = CAUSAL && (i0 < kw0 + KW - 1);
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int rq = 8 * g4 + 4 * half;
         const float4 lv = *(const float4*)(&Ls[slot][rq]);
-        const float4 dv = *(const float4*)(&Dsm[slot][rq]);
         const float lz[4] = {lv.x, lv.y, lv.z, lv.w};
-        const float dz[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
           float pv = exp2_fast(__builtin_fmaf(s[r], c, -lz[e]));
           if (need_mask && key > i0 + rq + e) pv = 0.f;
           s[r] = pv;
-          dp[r] = pv * (dp[r] - dz[e]);
+          dp[r] = pv * dp[r];
         }
       }
       const u32x4 bp[2] = {pack_acc8<DT>(s, 0), pack_acc8<DT>(s, 1)};
@@ -317,6 +325,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int sst = stat_stride(p.Nq);
   const float lse2 = qi < p.Nq ? p.lse2[(int64_t)bh * sst + qi] : __builtin_inff();
   const float dsv = qi < p.Nq ? p.dsum[(int64_t)bh * sst + qi] : 0.f;
+  f32x16 dinit;  // every dP^T accumulator starts at -D of this lane's query
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dinit[r] = -dsv;
 
   f32x16 adq[DB];
 #pragma unroll
@@ -339,7 +350,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const uint16_t* Vt = Vs[slot];
       // S^T = K Q^T and dP^T = V dO^T: rows are keys j0 + acc_row(half, r); column = this lane's query
       f32x16 s = rows_times_regs<D, DT>(Kt, qf, col, half);
-      f32x16 dp = rows_times_regs<D, DT>(Vt, of, col, half);
+      f32x16 dp = rows_times_regs<D, DT>(Vt, of, col, half, dinit);  // dP^T - D
       const bool need_mask = (j0 + kT > p.Nk) || (CAUSAL && j0 + kT - 1 > qw0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           const int kk = j0 + acc_row(half, r);
           if (kk >= p.Nk || (CAUSAL && kk > qi)) pv = 0.f;
         }
-        dp[r] = pv * (dp[r] - dsv);
+        dp[r] = pv * dp[r];
       }
       const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
       tile_t_times<D, DT>(adq, Kt, bd, lane);  // dQ^T += K^T dS^T
