@@ -107,10 +107,10 @@ __device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16 (&acc)[D
 // 32x32 accumulator = init + rows of a row-major LDS tile (32 rows) times B
 // held in registers, contracting over d.
 template <int D, int DT>
-__device__ __forceinline__ f32x16 rows_times_regs(const uint16_t* tile, const u32x4 (&bf)[D / 16], int col, int half,
-                                                  f32x16 s = f32x16{}) {
+__device__ __forceinline__ f32x16 rows_times_regs(const uint16_t* tile, const u32x4 (&bf)[D / 16],
+                                                  const TileAddr<D>& ta, f32x16 s = f32x16{}) {
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) s = mfma32<DT>(load_rowmajor_op<D>(tile, col, ks, half), bf[ks], s);
+  for (int ks = 0; ks < D / 16; ++ks) s = mfma32<DT>(lds_b128(tile, ta.rm[ks]), bf[ks], s);
   return s;
 }
 
@@ -118,12 +118,11 @@ __device__ __forceinline__ f32x16 rows_times_regs(const uint16_t* tile, const u3
 // 32, packed from a 32x32 accumulator in its register k order).
 template <int D, int DT>
 __device__ __forceinline__ void tile_t_times(f32x16 (&acc)[D / 32], const uint16_t* tile, const u32x4 (&bp)[2],
-                                             int lane) {
+                                             const TileAddr<D>& ta) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-      acc[db] = mfma32<DT>(load_transposed_a<D>(tile, lane, kk * 16, db), bp[kk], acc[db]);
+    for (int db = 0; db < D / 32; ++db) acc[db] = mfma32<DT>(lds_transposed_a<D>(tile, ta, kk, db), bp[kk], acc[db]);
 }
 
 // ------------------------------------------------------------ dK, dV
@@ -199,6 +198,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   const float c = p.c;
 
+  TileAddr<D> ta;
+  ta.init(lane);
+
   wait_loads();
   lds_barrier();
 
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const uint16_t* Qt = Qs[slot];
       const uint16_t* Ot = Os[slot];
       // S = Q K^T and dP = dO V^T: rows are queries i0 + acc_row(half, r); column = this lane's key
-      f32x16 s = rows_times_regs<D, DT>(Qt, kf, col, half);
+      f32x16 s = rows_times_regs<D, DT>(Qt, kf, ta);
       // dP - D in one pass: the dP accumulator starts at -D of its row
       f32x16 dinit;
 #pragma unroll
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         dinit[4 * g4 + 2] = -dv.z;
         dinit[4 * g4 + 3] = -dv.w;
       }
-      f32x16 dp = rows_times_regs<D, DT>(Ot, vf, col, half, dinit);
+      f32x16 dp = rows_times_regs<D, DT>(Ot, vf, ta, dinit);
       const bool need_mask = CAUSAL && (i0 < kw0 + KW - 1);
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -245,8 +247,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
       const u32x4 bp[2] = {pack_acc8<DT>(s, 0), pack_acc8<DT>(s, 1)};
       const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
-      tile_t_times<D, DT>(adv, Ot, bp, lane);  // dV^T += dO^T P
-      tile_t_times<D, DT>(adk, Qt, bd, lane);  // dK^T += Q^T dS
+      tile_t_times<D, DT>(adv, Ot, bp, ta);  // dV^T += dO^T P
+      tile_t_times<D, DT>(adk, Qt, bd, ta);  // dK^T += Q^T dS
     }
 
     if (it + 2 < n_qt) {
@@ -334,6 +336,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int db = 0; db < DB; ++db) adq[db] = f32x16{};
   const float c = p.c;
 
+  TileAddr<D> ta;
+  ta.init(lane);
+
   wait_loads();
   lds_barrier();
 
@@ -349,8 +354,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const uint16_t* Kt = Ks[slot];
       const uint16_t* Vt = Vs[slot];
       // S^T = K Q^T and dP^T = V dO^T: rows are keys j0 + acc_row(half, r); column = this lane's query
-      f32x16 s = rows_times_regs<D, DT>(Kt, qf, col, half);
-      f32x16 dp = rows_times_regs<D, DT>(Vt, of, col, half, dinit);  // dP^T - D
+      f32x16 s = rows_times_regs<D, DT>(Kt, qf, ta);
+      f32x16 dp = rows_times_regs<D, DT>(Vt, of, ta, dinit);  // dP^T - D
       const bool need_mask = (j0 + kT > p.Nk) || (CAUSAL && j0 + kT - 1 > qw0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         dp[r] = pv * dp[r];
       }
       const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
-      tile_t_times<D, DT>(adq, Kt, bd, lane);  // dQ^T += K^T dS^T
+      tile_t_times<D, DT>(adq, Kt, bd, ta);  // dQ^T += K^T dS^T
     }
 
     if (j + 2 < n_kt) {

@@ -115,6 +115,46 @@ __device__ __forceinline__ u32x4 load_rowmajor_op(const uint16_t* tile, int r, i
   return *(const u32x4*)(tile + r * D + ((c ^ swz<D>(r)) << 3));
 }
 
+// Per-lane LDS byte offsets of every operand read of a 32-row swizzled
+// [32][D] tile, computed once: the swizzle of the rows a lane touches
+// depends only on the lane (and the 8-row half), never on the k-step, so
+// the reads of any tile slot are `slot base + these offsets + immediates`.
+template <int D>
+struct TileAddr {
+  uint32_t rm[D / 16];     // row-major operand (row = lane % 32), k-step ks
+  uint32_t tr[D / 32][2];  // transposed operand, column block db, rows +0 / +8 (k-block 0)
+
+  __device__ __forceinline__ void init(int lane) {
+    const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) rm[ks] = 2u * (uint32_t)(col * D + (((2 * ks + half) ^ swz<D>(col)) << 3));
+    const int g = lane >> 4, p = lane & 15;
+    const int row0 = 4 * (g >> 1) + (p >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = db * 32 + 16 * (g & 1) + 4 * (p & 3);
+      tr[db][0] = 2u * (uint32_t)tile_off<D>(row0, c);
+      tr[db][1] = 2u * (uint32_t)tile_off<D>(row0 + 8, c);
+    }
+  }
+};
+
+// Byte distance between the two 16-row k-blocks of a transposed operand
+// read: the swizzle repeats every 16 rows, so it is a plain row offset.
+template <int D>
+constexpr uint32_t kTrKBlockBytes = 16u * D * 2u;
+
+__device__ __forceinline__ u32x4 lds_b128(const uint16_t* base, uint32_t byte_off) {
+  return *(const u32x4*)((const char*)base + byte_off);
+}
+template <int D>
+__device__ __forceinline__ u32x4 lds_transposed_a(const uint16_t* base, const TileAddr<D>& ta, int kk, int db) {
+  const char* b = (const char*)base + kk * kTrKBlockBytes<D>;
+  u32x2 lo = lds_read_tr16((const uint16_t*)(b + ta.tr[db][0]));
+  u32x2 hi = lds_read_tr16((const uint16_t*)(b + ta.tr[db][1]));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // Pack registers 8*kk .. 8*kk+7 of an fp32 accumulator into an MFMA operand.
 template <int DT>
 __device__ __forceinline__ u32x4 pack_acc8(const f32x16& s, int kk) {

@@ -81,14 +81,14 @@ __device__ __forceinline__ float dot2_sum<DT_BF16>(uint32_t packed, float acc) {
 // k-step per read) so at most LA + 1 K operands are live: the scheduler
 // would otherwise hoist all of them.
 template <int D, int DT, int kNQB, int LA = FwdTile<D>::QK_LOOKAHEAD>
-__device__ __forceinline__ void qk(f32x16 (&s)[kNQB], const uint16_t* Kt, const u32x4 (&qf)[kNQB][D / 16], int col,
-                                   int half) {
+__device__ __forceinline__ void qk(f32x16 (&s)[kNQB], const uint16_t* Kt, const u32x4 (&qf)[kNQB][D / 16],
+                                   const TileAddr<D>& ta) {
   constexpr int KS = D / 16;
 #pragma unroll
   for (int nb = 0; nb < kNQB; ++nb) s[nb] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const u32x4 a = load_rowmajor_op<D>(Kt, col, ks, half);
+    const u32x4 a = lds_b128(Kt, ta.rm[ks]);
 #pragma unroll
     for (int nb = 0; nb < kNQB; ++nb) s[nb] = mfma32<DT>(a, qf[nb][ks], s[nb]);
   }
@@ -117,7 +117,8 @@ __device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __rest
                                          uint16_t* __restrict__ Vdst, __amdgpu_buffer_rsrc_t krs,
                                          __amdgpu_buffer_rsrc_t vrs, uint32_t krow, uint32_t vrow, uint32_t ktb,
                                          uint32_t vtb, const u32x4 (&qf)[kNQB][D / 16], f32x16 (&acc)[D / 32][kNQB],
-                                         RowState<kNQB>& st, int Nk, int qw0, float c, int lane, int wave) {
+                                         RowState<kNQB>& st, int Nk, int qw0, float c, int lane, int wave,
+                                         const TileAddr<D>& ta) {
   using TC = TileCopy<D>;
   constexpr int DB = D / 32;
   const int j0 = j * kBN;
@@ -131,7 +132,7 @@ __device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __rest
 
   // ---- S^T = K Q^T
   f32x16 s[kNQB];
-  qk<D, DT, kNQB>(s, Kt, qf, col, half);
+  qk<D, DT, kNQB>(s, Kt, qf, ta);
 
   // ---- masks (only tiles crossing the key tail or this wave's diagonal)
   if ((j0 + kBN > Nk) || (CAUSAL && j0 + kBN - 1 > qw0)) {
@@ -203,7 +204,7 @@ __device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __rest
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const u32x4 a = load_transposed_a<D>(Vt, ln, kk * 16, db);
+      const u32x4 a = lds_transposed_a<D>(Vt, ta, kk, db);
 #pragma unroll
       for (int nb = 0; nb < kNQB; ++nb) acc[db][nb] = mfma32<DT>(a, pf[kk][nb], acc[db][nb]);
     }
@@ -296,6 +297,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   }
   const float c = p.c;
 
+  TileAddr<D> ta;
+  ta.init(lane);
+
   wait_loads();
   lds_barrier();
 
@@ -305,13 +309,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
     // constant, folded into the LDS instructions' offsets
     for (int j = 0; j < n_kt; j += 3) {
       fwd_iter<D, DT, CAUSAL>(j, n_kt, Ks[0], Vs[0], Ks[2], Vs[2], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk,
-                              qw0, c, lane, wave);
+                              qw0, c, lane, wave, ta);
       if (j + 1 >= n_kt) break;
       fwd_iter<D, DT, CAUSAL>(j + 1, n_kt, Ks[1], Vs[1], Ks[0], Vs[0], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st,
-                              p.Nk, qw0, c, lane, wave);
+                              p.Nk, qw0, c, lane, wave, ta);
       if (j + 2 >= n_kt) break;
       fwd_iter<D, DT, CAUSAL>(j + 2, n_kt, Ks[2], Vs[2], Ks[1], Vs[1], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st,
-                              p.Nk, qw0, c, lane, wave);
+                              p.Nk, qw0, c, lane, wave, ta);
     }
   } else {
     int buf = 0;
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
       int nbuf = buf + 2;
       nbuf = nbuf >= NBUF ? nbuf - NBUF : nbuf;
       fwd_iter<D, DT, CAUSAL>(j, n_kt, Ks[buf], Vs[buf], Ks[nbuf], Vs[nbuf], krs, vrs, krow, vrow, ktb, vtb, qf, acc,
-                              st, p.Nk, qw0, c, lane, wave);
+                              st, p.Nk, qw0, c, lane, wave, ta);
       buf = buf + 1 >= NBUF ? 0 : buf + 1;
     }
   }
