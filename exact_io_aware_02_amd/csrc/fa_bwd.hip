@@ -135,10 +135,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   using TC = TileCopyT<D, kT, kWaves>;
   constexpr int NLOADS = 2 * TC::NI + 2;  // per wave per tile: Q, dO, 8 lse2 and 8 D values
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Qs[kNBuf][kT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Os[kNBuf][kT * D];  // dO
-  __shared__ __attribute__((aligned(16))) float Ls[kNBuf][kT];           // lse * log2(e)
-  __shared__ __attribute__((aligned(16))) float Dsm[kNBuf][kT];          // D
+  // One LDS object (separate __shared__ variables get separate alias
+  // scopes, and the compiler then waits for every in-flight copy into a
+  // variable before reading any part of it).
+  struct Smem {
+    uint16_t q[kNBuf][kT * D];
+    uint16_t o[kNBuf][kT * D];  // dO
+    float l[kNBuf][kT];         // lse * log2(e)
+    float d[kNBuf][kT];         // D
+  };
+  __shared__ __attribute__((aligned(1024))) Smem sm;
+  auto& Qs = sm.q;
+  auto& Os = sm.o;
+  auto& Ls = sm.l;
+  auto& Dsm = sm.d;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -214,16 +224,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Queries past Nq read as zero rows with zero statistics, so they add
     // nothing to dK or dV; keys past Nk are never written.
     const bool active = kw0 < p.Nk && !(CAUSAL && i0 + kT - 1 < kw0);
-    if (active) {
-      const uint16_t* Qt = Qs[slot];
-      const uint16_t* Ot = Os[slot];
+    // The tile pointers are __restrict__ parameters of the inlined body so
+    // that its LDS reads carry alias scopes; the compiler then leaves the
+    // in-flight copy into another slot alone (the wait + barrier below
+    // order the ring).
+    auto body = [&](const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Ot, const float* __restrict__ Lt,
+                    const float* __restrict__ Dt) {
       // S = Q K^T and dP = dO V^T: rows are queries i0 + acc_row(half, r); column = this lane's key
       f32x16 s = rows_times_regs<D, DT>(Qt, kf, ta);
       // dP - D in one pass: the dP accumulator starts at -D of its row
       f32x16 dinit;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 dv = *(const float4*)(&Dsm[slot][8 * g4 + 4 * half]);
+        const float4 dv = *(const float4*)(&Dt[8 * g4 + 4 * half]);
         dinit[4 * g4 + 0] = -dv.x;
         dinit[4 * g4 + 1] = -dv.y;
         dinit[4 * g4 + 2] = -dv.z;
@@ -234,7 +247,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int rq = 8 * g4 + 4 * half;
-        const float4 lv = *(const float4*)(&Ls[slot][rq]);
+        const float4 lv = *(const float4*)(&Lt[rq]);
         const float lz[4] = {lv.x, lv.y, lv.z, lv.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -249,7 +262,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
       tile_t_times<D, DT>(adv, Ot, bp, ta);  // dV^T += dO^T P
       tile_t_times<D, DT>(adk, Qt, bd, ta);  // dK^T += Q^T dS
-    }
+    };
+    if (active) body(Qs[slot], Os[slot], Ls[slot], Dsm[slot]);
 
     if (it + 2 < n_qt) {
       wait_vmcnt<NLOADS>();
@@ -275,8 +289,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int DB = D / 32;
   using TC = TileCopyT<D, kT, kWaves>;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[kNBuf][kT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[kNBuf][kT * D];
+  struct Smem {  // one LDS object, as in dkdv_kernel
+    uint16_t k[kNBuf][kT * D];
+    uint16_t v[kNBuf][kT * D];
+  };
+  __shared__ __attribute__((aligned(1024))) Smem sm;
+  auto& Ks = sm.k;
+  auto& Vs = sm.v;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -350,9 +369,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (j + 2 < n_kt) issue(j + 2, nslot);
 
     const bool active = qw0 < p.Nq && !(CAUSAL && j0 > qw0 + QW - 1);
-    if (active) {
-      const uint16_t* Kt = Ks[slot];
-      const uint16_t* Vt = Vs[slot];
+    auto body = [&](const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ Vt) {  // as in dkdv_kernel
       // S^T = K Q^T and dP^T = V dO^T: rows are keys j0 + acc_row(half, r); column = this lane's query
       f32x16 s = rows_times_regs<D, DT>(Kt, qf, ta);
       f32x16 dp = rows_times_regs<D, DT>(Vt, of, ta, dinit);  // dP^T - D
@@ -368,7 +385,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
       const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
       tile_t_times<D, DT>(adq, Kt, bd, ta);  // dQ^T += K^T dS^T
-    }
+    };
+    if (active) body(Ks[slot], Vs[slot]);
 
     if (j + 2 < n_kt) {
       wait_vmcnt<2 * TC::NI>();

@@ -1,12 +1,12 @@
 // Forward attention kernel for gfx950.
 //
-// One workgroup of 4 waves owns BM = 256 query rows of one (batch, head);
-// each wave owns 64 of them (two 32-query MFMA column blocks) and their
-// softmax state, so the row max and row sum never leave the wave
-// (FlashAttention-2's point of less communication between warps, refbase
-// Q&A on FA2's improvements).  K/V tiles of BN = 64 keys stream from HBM
-// straight into LDS (global_load_lds_dwordx4, no staging registers),
-// double buffered.  Per tile and wave:
+// One workgroup of 4 waves owns BM query rows of one (batch, head); each
+// wave owns 32 of them at d = 128 (64, as two 32-query MFMA column blocks,
+// at d = 64) and their softmax state, so the row max and row sum never
+// leave the wave (FlashAttention-2's point of less communication between
+// warps, refbase Q&A on FA2's improvements).  K/V tiles of BN = 32 keys
+// stream from HBM straight into LDS (buffer_load ... lds, no staging
+// registers) through a 4-slot ring.  Per tile and wave:
 //
 //   S^T = K_j Q^T          32x32x16 MFMAs; A = K rows from LDS, B = Q held
 //                          in registers for the whole loop.  Each lane
@@ -24,11 +24,10 @@
 //                          untransposed V tile; B = P^T repacked in place
 //                          from the S^T accumulator (no LDS round trip).
 //
-// The loop is software pipelined: S for tile j+1 is computed by MFMA while
-// the VALU exponentiates tile j, so the matrix cores and the vector/
-// transcendental units work at the same time (the overlap FA3 gets from
-// asynchrony on Hopper, glossary article's FA-3 section, done here within
-// one wave).
+// The loop is software pipelined: the MFMAs for S of tile j+1 are issued
+// among the exponentials of tile j, so the matrix core and the VALU of a
+// SIMD work at the same time within one wave (the overlap FA3 gets from
+// asynchrony on Hopper, glossary article's FA-3 section).
 //
 // Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2.  Causal: tiles wholly
 // after a workgroup's last query are never loaded; tiles that cross a
@@ -56,8 +55,6 @@ struct FwdTile {
   static constexpr int QW = 32 * NQB;       // queries per wave
   static constexpr int BM = kWaves * QW;    // queries per workgroup
   static constexpr int WAVES_PER_SIMD = 2;
-  static constexpr bool UNROLL_RING = false;  // true: constant slot addresses (but spills at d=128)
-  static constexpr int QK_LOOKAHEAD = 4;     // K operand reads issued ahead of their MFMAs
 };
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
@@ -76,63 +73,39 @@ __device__ __forceinline__ float dot2_sum<DT_BF16>(uint32_t packed, float acc) {
                                          acc, false);
 }
 
-// S^T (32 keys x 64 queries) of one tile: A = K rows from LDS, B = Q^T.
-// The issue order is pinned (LA operand reads ahead, then the MFMAs of one
-// k-step per read) so at most LA + 1 K operands are live: the scheduler
-// would otherwise hoist all of them.
-template <int D, int DT, int kNQB, int LA = FwdTile<D>::QK_LOOKAHEAD>
-__device__ __forceinline__ void qk(f32x16 (&s)[kNQB], const uint16_t* Kt, const u32x4 (&qf)[kNQB][D / 16],
-                                   const TileAddr<D>& ta) {
-  constexpr int KS = D / 16;
-#pragma unroll
-  for (int nb = 0; nb < kNQB; ++nb) s[nb] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const u32x4 a = lds_b128(Kt, ta.rm[ks]);
-#pragma unroll
-    for (int nb = 0; nb < kNQB; ++nb) s[nb] = mfma32<DT>(a, qf[nb][ks], s[nb]);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS read x LA
-#pragma unroll
-  for (int i = 0; i < KS - LA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, kNQB, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, LA * kNQB, 0);
-}
-
 template <int kNQB>
 struct RowState {
   float m[kNQB];  // running max, log2 units (scaled by c)
   float l[kNQB];  // this lane's partial row sum (lane i^32 holds the rest)
 };
 
-// One K/V tile of the forward loop.  The __restrict__ tile pointers tell
-// the compiler the LDS reads of tile j never alias the asynchronous copy
-// into tile j+2's slot, so it does not wait for that copy before reading;
-// the explicit vmcnt wait + barrier at the end orders the ring.
+// One step of the software-pipelined loop: tile j's softmax and O += P V,
+// while the MFMAs form S for tile j+1 into `sn`.  A wave's issue stream
+// alternates those independent MFMAs with the exponentials of tile j, so
+// the matrix core and the VALU of one SIMD stay busy together even without
+// the other wave's help.  The LDS ring has four slots (tile t in slot
+// t mod 4): step j reads K(j+1) and V(j) and fills slot (j+3) mod 4.
+// The __restrict__ tile pointers tell the compiler the reads never alias
+// the in-flight copy, so it does not wait for that copy before reading;
+// the vmcnt wait and barrier at the end order the ring.
 template <int D, int DT, bool CAUSAL, int kNQB = FwdTile<D>::NQB>
-__device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __restrict__ Kt,
-                                         const uint16_t* __restrict__ Vt, uint16_t* __restrict__ Kdst,
-                                         uint16_t* __restrict__ Vdst, __amdgpu_buffer_rsrc_t krs,
-                                         __amdgpu_buffer_rsrc_t vrs, uint32_t krow, uint32_t vrow, uint32_t ktb,
-                                         uint32_t vtb, const u32x4 (&qf)[kNQB][D / 16], f32x16 (&acc)[D / 32][kNQB],
-                                         RowState<kNQB>& st, int Nk, int qw0, float c, int lane, int wave,
-                                         const TileAddr<D>& ta) {
+__device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32x16 (&sn)[kNQB],
+                                         const uint16_t* __restrict__ Kn, const uint16_t* __restrict__ Vt,
+                                         uint16_t* __restrict__ Kdst, uint16_t* __restrict__ Vdst,
+                                         __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, uint32_t krow,
+                                         uint32_t vrow, uint32_t ktb, uint32_t vtb, const u32x4 (&qf)[kNQB][D / 16],
+                                         f32x16 (&acc)[D / 32][kNQB], RowState<kNQB>& st, int Nk, int qw0, float c,
+                                         int lane, int wave, const TileAddr<D>& ta) {
   using TC = TileCopy<D>;
+  constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   const int j0 = j * kBN;
-  const int ln = lane;
-  const int col = ln & 31, half = ln >> 5;
+  const int col = lane & 31, half = lane >> 5;
 
-  if (j + 2 < n_kt) {
-    TC::issue(krs, krow, (uint32_t)(j + 2) * ktb, Kdst, ln, wave);
-    TC::issue(vrs, vrow, (uint32_t)(j + 2) * vtb, Vdst, ln, wave);
+  if (j + 3 < n_kt) {
+    TC::issue(krs, krow, (uint32_t)(j + 3) * ktb, Kdst, lane, wave);
+    TC::issue(vrs, vrow, (uint32_t)(j + 3) * vtb, Vdst, lane, wave);
   }
-
-  // ---- S^T = K Q^T
-  f32x16 s[kNQB];
-  qk<D, DT, kNQB>(s, Kt, qf, ta);
 
   // ---- masks (only tiles crossing the key tail or this wave's diagonal)
   if ((j0 + kBN > Nk) || (CAUSAL && j0 + kBN - 1 > qw0)) {
@@ -151,9 +124,9 @@ __device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __rest
   bool raise = false;
 #pragma unroll
   for (int nb = 0; nb < kNQB; ++nb) {
-    float mx = s[nb][0];
+    float mx = fmaxf(s[nb][0], s[nb][1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[nb][r]), s[nb][r + 1]);
     mx = max_pair32(mx);
     mxc[nb] = mx * c;
     raise |= mxc[nb] > st.m[nb] + kRescaleSlack;
@@ -169,12 +142,24 @@ __device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __rest
       for (int db = 0; db < DB; ++db) acc[db][nb] *= alpha;
     }
   }
-  // ---- P = 2^(S c - m) packed into the MFMA B operand; row sums from the packed values
+
+  // ---- S(j+1) = K(j+1) Q^T, issued first so the MFMAs run under the exponentials
+#pragma unroll
+  for (int nb = 0; nb < kNQB; ++nb) sn[nb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 a = lds_b128(Kn, ta.rm[ks]);
+#pragma unroll
+    for (int nb = 0; nb < kNQB; ++nb) sn[nb] = mfma32<DT>(a, qf[nb][ks], sn[nb]);
+  }
+
+  // ---- P = 2^(S c - m) packed into the MFMA B operand
   u32x4 pf[2][kNQB];
+  float ls[kNQB][2];
 #pragma unroll
   for (int nb = 0; nb < kNQB; ++nb) {
     const float mneg = -st.m[nb];
-    float ls0 = 0.f, ls1 = 0.f;
+    ls[nb][0] = ls[nb][1] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       uint32_t w[4];
@@ -185,19 +170,16 @@ __device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __rest
         const float p1 = exp2_fast(__builtin_fmaf(s[nb][r + 1], c, mneg));
         w[e] = pack2<DT>(p0, p1);
         if constexpr (DT == DT_BF16) {  // bf16 rounding (2^-9) is too coarse for the normaliser
-          ls0 = (r == 0) ? p0 : ls0 + p0;
-          ls1 = (r == 0) ? p1 : ls1 + p1;
+          ls[nb][0] = (r == 0) ? p0 : ls[nb][0] + p0;
+          ls[nb][1] = (r == 0) ? p1 : ls[nb][1] + p1;
         }
       }
       if constexpr (DT == DT_F16) {  // fp16-rounded P is accurate enough: sum pairs in one op
-        ls0 = dot2_sum<DT>(w[0], ls0);
-        ls1 = dot2_sum<DT>(w[1], ls1);
-        ls0 = dot2_sum<DT>(w[2], ls0);
-        ls1 = dot2_sum<DT>(w[3], ls1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ls[nb][e & 1] = dot2_sum<DT>(w[e], ls[nb][e & 1]);
       }
       pf[kk][nb] = u32x4{w[0], w[1], w[2], w[3]};
     }
-    st.l[nb] += ls0 + ls1;
   }
   // ---- O^T += V^T P^T
 #pragma unroll
@@ -208,14 +190,17 @@ __device__ __forceinline__ void fwd_iter(int j, int n_kt, const uint16_t* __rest
 #pragma unroll
       for (int nb = 0; nb < kNQB; ++nb) acc[db][nb] = mfma32<DT>(a, pf[kk][nb], acc[db][nb]);
     }
+#pragma unroll
+  for (int nb = 0; nb < kNQB; ++nb) st.l[nb] += ls[nb][0] + ls[nb][1];
 
-  // tile j+1 (issued one step earlier) must have landed; tile j+2 may fly on
-  if (j + 2 < n_kt) {
+  // tile j+2 must have landed (K read next step, V the step after); j+3 may fly on
+  if (j + 3 < n_kt) {
     wait_vmcnt<2 * TC::NI>();
   } else {
     wait_loads();
   }
   lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D, int DT, bool CAUSAL>
@@ -226,11 +211,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   constexpr int kBM = FwdTile<D>::BM;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NBUF = 3;  // K/V ring: tile j+2 loads while tile j is computed
+  constexpr int NBUF = 4;  // K/V ring (see fwd_step)
   constexpr int TILE = kBN * D;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[NBUF][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[NBUF][TILE];
+  // One LDS object for the whole ring: the compiler gives every separate
+  // __shared__ variable its own alias scope, and then makes each LDS read
+  // wait for the in-flight copies into the same variable, which would
+  // serialise the prefetch with the compute it is meant to hide under.
+  struct Smem {
+    uint16_t k[NBUF][TILE];
+    uint16_t v[NBUF][TILE];
+  };
+  __shared__ __attribute__((aligned(1024))) Smem sm;
+  auto& Ks = sm.k;
+  auto& Vs = sm.v;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -262,16 +256,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   const uint32_t ktb = kBN * krow, vtb = kBN * vrow;
   using TC = TileCopy<D>;
 
-  // prologue: tiles 0 and 1 in flight before Q is touched
-  TC::issue(krs, krow, 0, Ks[0], lane, wave);
-  TC::issue(vrs, vrow, 0, Vs[0], lane, wave);
-  if (n_kt > 1) {
-    TC::issue(krs, krow, ktb, Ks[1], lane, wave);
-    TC::issue(vrs, vrow, vtb, Vs[1], lane, wave);
-  }
-
   // Q^T as the B operand, resident in registers: lane holds
-  // Q[qw0 + 32*nb + col][16*ks + 8*half .. +7].
+  // Q[qw0 + 32*nb + col][16*ks + 8*half .. +7].  Its loads go first so the
+  // vmcnt wait below can leave tile 2 in flight.
   u32x4 qf[kNQB][KS];
 #pragma unroll
   for (int nb = 0; nb < kNQB; ++nb) {
@@ -280,9 +267,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 x = u32x4{0, 0, 0, 0};
       if (qi < p.Nq) x = *(const u32x4*)(qp + qi * p.sq.s + 16 * ks + 8 * half);
-      qf[nb][ks] = x ^ p.qflip;
+      qf[nb][ks] = x;
     }
   }
+  // prologue: tiles 0..2 in flight
+#pragma unroll
+  for (int t0 = 0; t0 < 3; ++t0)
+    if (t0 < n_kt) {
+      TC::issue(krs, krow, (uint32_t)t0 * ktb, Ks[t0], lane, wave);
+      TC::issue(vrs, vrow, (uint32_t)t0 * vtb, Vs[t0], lane, wave);
+    }
 
   f32x16 acc[DB][kNQB];
 #pragma unroll
@@ -300,33 +294,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   TileAddr<D> ta;
   ta.init(lane);
 
-  wait_loads();
+  if (n_kt > 2) {
+    wait_vmcnt<2 * TC::NI>();
+  } else {
+    wait_loads();
+  }
+#pragma unroll
+  for (int nb = 0; nb < kNQB; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[nb][ks] ^= p.qflip;
   lds_barrier();
 
-  static_assert(NBUF == 3, "the loops below assume a 3-slot ring");
-  if constexpr (FwdTile<D>::UNROLL_RING) {
-    // unrolled by the ring depth: every slot address is a compile-time
-    // constant, folded into the LDS instructions' offsets
-    for (int j = 0; j < n_kt; j += 3) {
-      fwd_iter<D, DT, CAUSAL>(j, n_kt, Ks[0], Vs[0], Ks[2], Vs[2], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk,
-                              qw0, c, lane, wave, ta);
-      if (j + 1 >= n_kt) break;
-      fwd_iter<D, DT, CAUSAL>(j + 1, n_kt, Ks[1], Vs[1], Ks[0], Vs[0], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st,
-                              p.Nk, qw0, c, lane, wave, ta);
-      if (j + 2 >= n_kt) break;
-      fwd_iter<D, DT, CAUSAL>(j + 2, n_kt, Ks[2], Vs[2], Ks[1], Vs[1], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st,
-                              p.Nk, qw0, c, lane, wave, ta);
-    }
-  } else {
-    int buf = 0;
-    for (int j = 0; j < n_kt; ++j) {
-      // prefetch tile j+2 into the slot tile j-1 used (free since the last barrier)
-      int nbuf = buf + 2;
-      nbuf = nbuf >= NBUF ? nbuf - NBUF : nbuf;
-      fwd_iter<D, DT, CAUSAL>(j, n_kt, Ks[buf], Vs[buf], Ks[nbuf], Vs[nbuf], krs, vrs, krow, vrow, ktb, vtb, qf, acc,
-                              st, p.Nk, qw0, c, lane, wave, ta);
-      buf = buf + 1 >= NBUF ? 0 : buf + 1;
-    }
+  // S(0)
+  f32x16 sa[kNQB], sb[kNQB];
+#pragma unroll
+  for (int nb = 0; nb < kNQB; ++nb) sa[nb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 a = lds_b128(Ks[0], ta.rm[ks]);
+#pragma unroll
+    for (int nb = 0; nb < kNQB; ++nb) sa[nb] = mfma32<DT>(a, qf[nb][ks], sa[nb]);
+  }
+
+  // (Unrolling by two so that S alternates between the two register sets
+  // without the copy costs ~60 more registers and spills at d = 64.)
+  for (int j = 0; j < n_kt; ++j) {
+    const int sl = j & 3;
+    fwd_step<D, DT, CAUSAL>(j, n_kt, sa, sb, Ks[(sl + 1) & 3], Vs[sl], Ks[(sl + 3) & 3], Vs[(sl + 3) & 3], krs, vrs,
+                            krow, vrow, ktb, vtb, qf, acc, st, p.Nk, qw0, c, lane, wave, ta);
+#pragma unroll
+    for (int nb = 0; nb < kNQB; ++nb) sa[nb] = sb[nb];
   }
 
   // ---- epilogue: O = O^T / l, LSE
