@@ -9,21 +9,26 @@
 //   dK = scale dS^T Q  dQ = scale dS K
 //
 // Three kernels, deterministic (no atomics):
-//   prep_kernel  D_i = dO_i . O_i and lse_i * log2(e) per query row, into
+//   prep_kernel  -D_i = -dO_i . O_i and lse_i * log2(e) per query row, into
 //                the workspace (HBM bound, tiny).
-//   dkdv_kernel  a workgroup owns 128 keys (32 per wave) with K and V held
-//                in registers; 32-query tiles of Q, dO and the two row
-//                statistics stream HBM -> LDS through a 3-slot ring.
-//                S = Q K^T and dP = dO V^T come out with a key per lane,
-//                which is the B-operand layout of dV^T += dO^T P and
-//                dK^T += Q^T dS; the transposed A operands (dO^T, Q^T) are
-//                read from the same untransposed LDS tiles with
-//                ds_read_b64_tr_b16.
+//   dkdv_kernel  a workgroup of eight waves owns 128 keys; the two waves
+//                of a pair share 32 keys and one SIMD and split the work by
+//                role (A: K in registers, S, P, dV; B: V in registers, dP,
+//                dS, dK, with P handed over through LDS), skewed so that
+//                one role's MFMAs run under the other's VALU work.
+//                32-query tiles of Q, dO and the two row statistics stream
+//                HBM -> LDS through a 4-slot ring.  S = Q K^T and dP = dO V^T
+//                come out with a key per lane, which is the B-operand
+//                layout of dV^T += dO^T P and dK^T += Q^T dS; the
+//                transposed A operands (dO^T, Q^T) are read from the same
+//                untransposed LDS tiles with ds_read_b64_tr_b16.
 //   dq_kernel    a workgroup owns 128 queries (32 per wave) with Q and dO
 //                in registers; 32-key tiles of K and V stream through a
-//                3-slot ring like the forward.  S^T and dP^T have a query
+//                3-slot ring.  S^T and dP^T have a query
 //                per lane (its lse and D are lane-local); dQ^T += K^T dS^T
 //                reads K^T transposed from the K tile.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -83,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(BwdParams p, int blocks_
   // queries with zero Q/dO rows, which contribute nothing
   if (ch == 0 && row < stat_stride(p.Nq)) {
     const int64_t o = (int64_t)bh * stat_stride(p.Nq) + row;
-    p.dsum[o] = acc;
+    p.dsum[o] = -acc;  // stored negated: it seeds the dP accumulators
     p.lse2[o] = row < p.Nq ? p.lse[(int64_t)bh * p.Nq + row] * kLog2e : 0.f;
   }
 }
@@ -125,158 +130,275 @@ __device__ __forceinline__ void tile_t_times(f32x16 (&acc)[D / 32], const uint16
     for (int db = 0; db < D / 32; ++db) acc[db] = mfma32<DT>(lds_transposed_a<D>(tile, ta, kk, db), bp[kk], acc[db]);
 }
 
+// Pin the issue order of a straight-line run of NM MFMAs fed by NR LDS
+// reads: the reads of the first kLA MFMAs go first, then each MFMA is
+// followed by an even share of the remaining reads, so an operand is read
+// about kLA MFMAs (kLA x 32 cycles) before its use and the LDS latency
+// hides under the matrix core.  Without this the scheduler issues each
+// read right before its MFMA.
+constexpr int kLA = 4;
+template <int NM, int NR>
+__device__ __forceinline__ void sched_reads_ahead() {
+  constexpr int first = NR * kLA / NM;
+  constexpr int rest = NR - first;
+  constexpr int per = (rest + NM - kLA - 1) / (NM - kLA);
+  __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < NM - kLA) __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+  }
+}
+
+// Wait until the ring tile just after the one being consumed has landed:
+// `later` tiles were requested after it (at most MAXT, each L loads per
+// wave), and vmcnt counts in request order, so leaving min(later, MAXT) * L
+// loads outstanding is enough.
+template <int MAXT, int L>
+__device__ __forceinline__ void wait_ring(int later) {
+  static_assert(MAXT * L < 64, "vmcnt range");
+  if (later >= MAXT) {
+    wait_vmcnt<MAXT * L>();
+    return;
+  }
+  switch (later) {
+#define FA_WAIT_CASE(n) \
+  case n:               \
+    if constexpr (n < MAXT) wait_vmcnt<n * L>(); \
+    break;
+    FA_WAIT_CASE(1) FA_WAIT_CASE(2) FA_WAIT_CASE(3) FA_WAIT_CASE(4) FA_WAIT_CASE(5) FA_WAIT_CASE(6)
+#undef FA_WAIT_CASE
+    default:
+      wait_loads();
+  }
+}
+
 // ------------------------------------------------------------ dK, dV
+// Eight waves in four pairs.  The two waves of a pair own the same 32 keys
+// and, with waves placed on SIMDs round-robin, the same SIMD; they split
+// the four contractions of a query tile by role:
+//   role A (waves 0-3): K rows in registers;  S = Q K^T, P = 2^(S c - lse2),
+//                       dV^T += dO^T P; P goes to its partner through LDS.
+//   role B (waves 4-7): V rows in registers;  dP - D = dO V^T - D,
+//                       dS = P (dP - D), dK^T += Q^T dS.
+// Each wave holds one operand set and one 32 x d accumulator instead of
+// two, and the loop is skewed so that within one phase the MFMAs of one
+// role run while the other role works on the VALU:
+//   phase 1: A  P(t) from S(t), hand P(t) over      B  dP(t); dK += .. dS(t-1)
+//   barrier
+//   phase 2: A  dV += .. P(t); S(t+1)               B  dS(t) = P(t) (dP(t) - D)
+// Query tiles (Q, dO and the two row statistics) stream HBM -> LDS through
+// a 4-slot ring; tile t+3 is requested in phase 2 of step t.
 template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(BwdParams p) {
-  constexpr int KW = 32;            // keys per wave
-  constexpr int BNK = kWaves * KW;  // keys per workgroup
+__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(BwdParams p) {
+  constexpr int KW = 32;            // keys per pair
+  constexpr int NPAIR = kWaves;     // pairs per workgroup
+  constexpr int BNK = NPAIR * KW;   // keys per workgroup
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  using TC = TileCopyT<D, kT, kWaves>;
-  constexpr int NLOADS = 2 * TC::NI + 2;  // per wave per tile: Q, dO, 8 lse2 and 8 D values
+  constexpr int NB = 4;             // ring slots (a power of two)
+  constexpr int PD = NB - 1;        // prefetch distance: tile t+PD is requested in step t
+  using TC = TileCopyT<D, kT, NPAIR>;  // a Q or dO tile over the four waves of one role
+  constexpr int NLOADS = TC::NI + 1;  // per wave per tile: its share of Q (A) or dO (B), 8 statistics
 
   // One LDS object (separate __shared__ variables get separate alias
   // scopes, and the compiler then waits for every in-flight copy into a
   // variable before reading any part of it).
   struct Smem {
-    uint16_t q[kNBuf][kT * D];
-    uint16_t o[kNBuf][kT * D];  // dO
-    float l[kNBuf][kT];         // lse * log2(e)
-    float d[kNBuf][kT];         // D
+    uint16_t q[NB][kT * D];
+    uint16_t o[NB][kT * D];  // dO
+    float l[NB][kT];         // lse * log2(e)
+    float d[NB][kT];         // -D
+    f32x4 x[2][NPAIR][4][64];  // fp32 P hand-over, double buffered: [step & 1][pair][register group][lane]
   };
   __shared__ __attribute__((aligned(1024))) Smem sm;
-  auto& Qs = sm.q;
-  auto& Os = sm.o;
-  auto& Ls = sm.l;
-  auto& Dsm = sm.d;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & (NPAIR - 1);
+  const bool role_a = wave < NPAIR;
   const int BH = p.B * p.H;
   const int t = blockIdx.x;
   const int kt = t / BH;  // ascending key tiles: the causal-heaviest first
   const int bh = t - kt * BH;
   const int b = bh / p.H, h = bh - b * p.H;
   const int k0 = kt * BNK;
-  const int kw0 = k0 + wave * KW;
+  const int kw0 = k0 + pair * KW;
   const int key = kw0 + col;
 
-  const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h;
-  const uint16_t* dop = p.dout + b * p.sdo.b + h * p.sdo.h;
-  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(qp, p.Nq, p.sq.s, D);
-  const __amdgpu_buffer_rsrc_t ors = head_rsrc(dop, p.Nq, p.sdo.s, D);
   const int sst = stat_stride(p.Nq);
-  const __amdgpu_buffer_rsrc_t lrs = f32_rsrc(p.lse2 + (int64_t)bh * sst, sst);
-  const __amdgpu_buffer_rsrc_t drs = f32_rsrc(p.dsum + (int64_t)bh * sst, sst);
-  const uint32_t qrow = (uint32_t)(p.sq.s * 2), orow = (uint32_t)(p.sdo.s * 2);
+  // role A streams Q and lse2, role B dO and -D
+  const uint16_t* tp = role_a ? p.q + b * p.sq.b + h * p.sq.h : p.dout + b * p.sdo.b + h * p.sdo.h;
+  const int64_t tstride = role_a ? p.sq.s : p.sdo.s;
+  const __amdgpu_buffer_rsrc_t trs = head_rsrc(tp, p.Nq, tstride, D);
+  const __amdgpu_buffer_rsrc_t srs = f32_rsrc((role_a ? p.lse2 : p.dsum) + (int64_t)bh * sst, sst);
+  const uint32_t trow = (uint32_t)(tstride * 2);
 
   const int qt0 = CAUSAL ? (k0 / kT) : 0;
   const int n_qt = (p.Nq + kT - 1) / kT;
 
   auto issue = [&](int it, int slot) {
-    TC::issue(qrs, qrow, (uint32_t)it * kT * qrow, Qs[slot], lane, wave);
-    TC::issue(ors, orow, (uint32_t)it * kT * orow, Os[slot], lane, wave);
-    vec_to_lds<8>(lrs, (uint32_t)(it * kT + 8 * wave) * 4, Ls[slot] + 8 * wave, lane);
-    vec_to_lds<8>(drs, (uint32_t)(it * kT + 8 * wave) * 4, Dsm[slot] + 8 * wave, lane);
+    TC::issue(trs, trow, (uint32_t)it * kT * trow, role_a ? sm.q[slot] : sm.o[slot], lane, pair);
+    vec_to_lds<8>(srs, (uint32_t)(it * kT + 8 * pair) * 4, (role_a ? sm.l[slot] : sm.d[slot]) + 8 * pair, lane);
   };
-  if (qt0 < n_qt) issue(qt0, 0);
-  if (qt0 + 1 < n_qt) issue(qt0 + 1, 1);
 
-  // K^T and V^T of this wave's keys as B operands: lane holds row `key`,
-  // columns 16*ks + 8*half .. +7 (zeros past Nk).
-  u32x4 kf[KS], vf[KS];
-  {
-    const uint16_t* kp = p.k + b * p.sk.b + h * p.sk.h;
-    const uint16_t* vp = p.v + b * p.sv.b + h * p.sv.h;
+  // The two roles run separate copies of the loop (one barrier per step in
+  // each, so they stay in step): a shared loop would merge the roles'
+  // registers through copies at every join.
+  auto run = [&](auto role_tag) {
+    constexpr bool A = decltype(role_tag)::value;
+    // K rows (A) or V rows (B) of the pair's keys as B operands: lane holds
+    // row `key`, columns 16*ks + 8*half .. +7 (zeros past Nk).
+    u32x4 kv[KS];
+    {
+      const uint16_t* rp = A ? p.k + b * p.sk.b + h * p.sk.h : p.v + b * p.sv.b + h * p.sv.h;
+      const int64_t rs = A ? p.sk.s : p.sv.s;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
-      if (key < p.Nk) {
-        x = *(const u32x4*)(kp + key * p.sk.s + 16 * ks + 8 * half);
-        y = *(const u32x4*)(vp + key * p.sv.s + 16 * ks + 8 * half);
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 x = u32x4{0, 0, 0, 0};
+        if (key < p.Nk) x = *(const u32x4*)(rp + key * rs + 16 * ks + 8 * half);
+        kv[ks] = x;
       }
-      kf[ks] = x;
-      vf[ks] = y;
     }
-  }
-  f32x16 adk[DB], adv[DB];
+    for (int i = 0; i < PD; ++i)
+      if (qt0 + i < n_qt) issue(qt0 + i, i);
+    // The slot before the first tile's (not loaded before tile qt0 + PD)
+    // is read by B's first dK update with dS = 0: make it finite zeros.
+    if constexpr (!A) {
+      u32x4* z = (u32x4*)sm.q[NB - 1];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    adk[db] = f32x16{};
-    adv[db] = f32x16{};
-  }
-  const float c = p.c;
-
-  TileAddr<D> ta;
-  ta.init(lane);
-
-  wait_loads();
-  lds_barrier();
-
-  int slot = 0;
-  for (int it = qt0; it < n_qt; ++it) {
-    const int i0 = it * kT;
-    int nslot = slot + 2;
-    nslot = nslot >= kNBuf ? nslot - kNBuf : nslot;
-    if (it + 2 < n_qt) issue(it + 2, nslot);
-
-    // Queries past Nq read as zero rows with zero statistics, so they add
-    // nothing to dK or dV; keys past Nk are never written.
-    const bool active = kw0 < p.Nk && !(CAUSAL && i0 + kT - 1 < kw0);
-    // The tile pointers are __restrict__ parameters of the inlined body so
-    // that its LDS reads carry alias scopes; the compiler then leaves the
-    // in-flight copy into another slot alone (the wait + barrier below
-    // order the ring).
-    auto body = [&](const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Ot, const float* __restrict__ Lt,
-                    const float* __restrict__ Dt) {
-      // S = Q K^T and dP = dO V^T: rows are queries i0 + acc_row(half, r); column = this lane's key
-      f32x16 s = rows_times_regs<D, DT>(Qt, kf, ta);
-      // dP - D in one pass: the dP accumulator starts at -D of its row
-      f32x16 dinit;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 dv = *(const float4*)(&Dt[8 * g4 + 4 * half]);
-        dinit[4 * g4 + 0] = -dv.x;
-        dinit[4 * g4 + 1] = -dv.y;
-        dinit[4 * g4 + 2] = -dv.z;
-        dinit[4 * g4 + 3] = -dv.w;
-      }
-      f32x16 dp = rows_times_regs<D, DT>(Ot, vf, ta, dinit);
-      const bool need_mask = CAUSAL && (i0 < kw0 + KW - 1);
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int rq = 8 * g4 + 4 * half;
-        const float4 lv = *(const float4*)(&Lt[rq]);
-        const float lz[4] = {lv.x, lv.y, lv.z, lv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float pv = exp2_fast(__builtin_fmaf(s[r], c, -lz[e]));
-          if (need_mask && key > i0 + rq + e) pv = 0.f;
-          s[r] = pv;
-          dp[r] = pv * dp[r];
-        }
-      }
-      const u32x4 bp[2] = {pack_acc8<DT>(s, 0), pack_acc8<DT>(s, 1)};
-      const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
-      tile_t_times<D, DT>(adv, Ot, bp, ta);  // dV^T += dO^T P
-      tile_t_times<D, DT>(adk, Qt, bd, ta);  // dK^T += Q^T dS
-    };
-    if (active) body(Qs[slot], Os[slot], Ls[slot], Dsm[slot]);
-
-    if (it + 2 < n_qt) {
-      wait_vmcnt<NLOADS>();
-    } else {
-      wait_loads();
+      for (int i = 0; i < kT * D / 8 / 256; ++i) z[(tid - 256) + 256 * i] = u32x4{0, 0, 0, 0};
     }
+
+    f32x16 acc[DB];  // dV^T (A) or dK^T (B)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    f32x16 sd = f32x16{};  // A: S of the next tile; B: dP - D of the current one
+    u32x4 pk[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};  // A: P; B: dS of the previous tile
+    const float c = p.c;
+
+    TileAddr<D> ta;
+    ta.init(lane);
+
+    // Tile pointers are __restrict__ parameters of inlined lambdas so that
+    // their LDS reads carry alias scopes; the compiler then leaves the
+    // in-flight copies into other slots alone (the vmcnt waits and barriers
+    // order the ring).  Tile qt0 + r lives in slot r mod NB.
+    wait_ring<PD - 2, NLOADS>(n_qt - 1 - (qt0 + 1));  // tiles qt0, qt0+1 landed
     lds_barrier();
-    slot = slot + 1 >= kNBuf ? 0 : slot + 1;
-  }
+    if constexpr (A) {
+      auto s_tile = [&](const uint16_t* __restrict__ Qt) { sd = rows_times_regs<D, DT>(Qt, kv, ta); };
+      if (qt0 < n_qt) s_tile(sm.q[0]);
+    }
 
-  if (key < p.Nk) {
-    store_rows<DT, DB>(p.dk + b * p.sdk.b + h * p.sdk.h + key * p.sdk.s, adk, p.scale, half);
-    store_rows<DT, DB>(p.dv + b * p.sdv.b + h * p.sdv.h + key * p.sdv.s, adv, 1.0f, half);
+    // One step.  (Unrolling by the ring depth would turn the slot bases
+    // into immediates, but makes this compiler spill role A's registers.)
+    auto step = [&](int it) {
+      const int SL = (it - qt0) & (NB - 1);
+      const int XB = SL & 1;
+      const int i0 = it * kT;
+
+      // ---------------- phase 1
+      if constexpr (A) {
+        auto phase = [&](const float* __restrict__ Lt, f32x4* __restrict__ X) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 lv = *(const float4*)(&Lt[8 * g4 + 4 * half]);
+            const float lz[4] = {lv.x, lv.y, lv.z, lv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sd[4 * g4 + e] = exp2_fast(__builtin_fmaf(sd[4 * g4 + e], c, -lz[e]));
+          }
+          if (CAUSAL && i0 < kw0 + KW - 1) {  // the tile crosses the pair's diagonal
+            // (the empty asm keeps this a branch: if-converted, the compares
+            // would run on every tile)
+            asm volatile("");
+            const int kd = key - i0 - 4 * half;  // query row of acc_row(half, r) is i0 + 4*half + (8*(r/4) + r%4)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (kd > ((r >> 2) << 3) + (r & 3)) sd[r] = 0.f;
+          }
+          pk[0] = pack_acc8<DT>(sd, 0);
+          pk[1] = pack_acc8<DT>(sd, 1);
+          // P in fp32 to the partner (exact dS, no unpacking there)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            X[64 * g4 + lane] = f32x4{sd[4 * g4], sd[4 * g4 + 1], sd[4 * g4 + 2], sd[4 * g4 + 3]};
+        };
+        phase(sm.l[SL], &sm.x[XB][pair][0][0]);
+      } else {
+        auto phase = [&](const uint16_t* __restrict__ Ot, const float* __restrict__ Dt,
+                         const uint16_t* __restrict__ Qprev) {
+          // dK^T += Q^T dS of the previous tile
+          tile_t_times<D, DT>(acc, Qprev, pk, ta);
+          // dP - D in one pass: the accumulator starts at -D of its row
+          f32x16 dinit;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 dv = *(const float4*)(&Dt[8 * g4 + 4 * half]);
+            dinit[4 * g4 + 0] = dv.x;
+            dinit[4 * g4 + 1] = dv.y;
+            dinit[4 * g4 + 2] = dv.z;
+            dinit[4 * g4 + 3] = dv.w;
+          }
+          sd = rows_times_regs<D, DT>(Ot, kv, ta, dinit);
+          // issue order: operand reads kLA MFMAs ahead of their use
+          sched_reads_ahead<2 * DB + KS, (4 * DB + 4 + KS)>();
+        };
+        // on the first step dS = 0 and the previous slot holds zeros
+        phase(sm.o[SL], sm.d[SL], sm.q[(SL + NB - 1) & (NB - 1)]);
+      }
+
+      // tile it+1 must have landed (A reads its Q rows next); the later
+      // requested ones fly on
+      wait_ring<PD - 2, NLOADS>(n_qt - 1 - (it + 1));
+      lds_barrier();
+      // tile it+PD's slot held tile it-1, whose last reader (B's dK)
+      // finished before the barrier
+      if (it + PD < n_qt) issue(it + PD, (SL + PD) & (NB - 1));
+
+      // ---------------- phase 2
+      if constexpr (A) {
+        auto phase = [&](const uint16_t* __restrict__ Ot, const uint16_t* __restrict__ Qn) {
+          tile_t_times<D, DT>(acc, Ot, pk, ta);  // dV^T += dO^T P
+          // S of the next tile (after the last tile this reads a stale slot
+          // and the result is never used)
+          sd = rows_times_regs<D, DT>(Qn, kv, ta);
+          sched_reads_ahead<2 * DB + KS, 4 * DB + KS>();
+        };
+        phase(sm.o[SL], sm.q[(SL + 1) & (NB - 1)]);
+      } else {
+        auto phase = [&](const f32x4* __restrict__ X) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 pv = X[64 * g4 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sd[4 * g4 + e] *= pv[e];
+          }
+          pk[0] = pack_acc8<DT>(sd, 0);
+          pk[1] = pack_acc8<DT>(sd, 1);
+        };
+        phase(&sm.x[XB][pair][0][0]);
+      }
+    };
+    for (int it = qt0; it < n_qt; ++it) step(it);
+    if constexpr (!A) {
+      auto last = [&](const uint16_t* __restrict__ Qt) { tile_t_times<D, DT>(acc, Qt, pk, ta); };
+      if (qt0 < n_qt) last(sm.q[(n_qt - 1 - qt0) & (NB - 1)]);
+    }
+
+    if (key < p.Nk) {
+      if constexpr (A) {
+        store_rows<DT, DB>(p.dv + b * p.sdv.b + h * p.sdv.h + key * p.sdv.s, acc, 1.0f, half);
+      } else {
+        store_rows<DT, DB>(p.dk + b * p.sdk.b + h * p.sdk.h + key * p.sdk.s, acc, p.scale, half);
+      }
+    }
+  };
+  if (role_a) {
+    run(std::true_type{});
+  } else {
+    run(std::false_type{});
   }
 }
 
@@ -345,10 +467,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   const int sst = stat_stride(p.Nq);
   const float lse2 = qi < p.Nq ? p.lse2[(int64_t)bh * sst + qi] : __builtin_inff();
-  const float dsv = qi < p.Nq ? p.dsum[(int64_t)bh * sst + qi] : 0.f;
+  const float ndsv = qi < p.Nq ? p.dsum[(int64_t)bh * sst + qi] : 0.f;  // -D
   f32x16 dinit;  // every dP^T accumulator starts at -D of this lane's query
 #pragma unroll
-  for (int r = 0; r < 16; ++r) dinit[r] = -dsv;
+  for (int r = 0; r < 16; ++r) dinit[r] = ndsv;
 
   f32x16 adq[DB];
 #pragma unroll
@@ -415,7 +537,7 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((stages & 2) && g1 > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<D, DT, CAUSAL>), dim3((unsigned)g1), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, DT, CAUSAL>), dim3((unsigned)g1), dim3(2 * kThreads), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((stages & 4) && g2 > 0) {

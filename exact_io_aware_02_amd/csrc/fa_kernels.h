@@ -32,7 +32,7 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dsum;  // workspace: D_i = dO_i . O_i, fp32, rows padded per (b, h)
+  float* dsum;  // workspace: -D_i = -(dO_i . O_i), fp32, rows padded per (b, h)
   float* lse2;  // workspace: lse_i * log2(e), same layout
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, Nq, Nk;

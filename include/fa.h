@@ -90,7 +90,9 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
                    void* stream);
 
 /* Bytes of device workspace fa_bwd needs for these sizes (0 if the sizes are
- * invalid).  Holds D_i = sum_d dO_i O_i (fp32 [B][H][Nq]). */
+ * invalid).  Holds two fp32 row statistics per (b, h): -D_i = -sum_d dO_i O_i
+ * and lse_i * log2(e), each with its rows padded to a multiple of 64
+ * (2 * B * H * round_up(Nq, 64) floats). */
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
 
 /* Backward of L = sum(O * dO): gradients of Q, K, V, BHSD contiguous.
@@ -119,8 +121,8 @@ int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, c
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stages of the backward, for callers that schedule them themselves.
- * fa_bwd_strided runs FA_BWD_ALL.  FA_BWD_PREP writes D_i = dO_i . O_i into
- * the workspace; FA_BWD_DKDV (dK, dV) and FA_BWD_DQ (dQ) read it and are
+ * fa_bwd_strided runs FA_BWD_ALL.  FA_BWD_PREP writes -D_i = -dO_i . O_i
+ * and lse_i * log2(e) into the workspace; FA_BWD_DKDV (dK, dV) and FA_BWD_DQ (dQ) read it and are
  * independent of each other, so after PREP has completed they may run on
  * two streams at once.  Stages in one call run in the order PREP, DKDV, DQ
  * on `stream`.  Same arguments and checks as fa_bwd_strided; `stages` is a
