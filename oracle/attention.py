@@ -30,6 +30,22 @@ What is computed, and where the pages define it:
   ``dK = scale * dS^T Q``.  Deliberately the ``rowsum(P*dP)`` form, not the
   ``rowsum(dO*O)`` identity a fast kernel uses, so parity tests that identity.
 
+* Fewer K/V heads (multi-query / grouped-query attention).  The skill
+  guide's Workflow 2, step 3 ("multi-query attention"): ``k`` and ``v`` may
+  carry fewer heads than ``q`` and the call handles it.  Reading taken (the
+  pages give no index map): ``H_kv`` divides ``H`` and query head ``h`` uses
+  K/V head ``h // (H // H_kv)``, so consecutive query heads share one K/V
+  head.  In the backward a K/V head's gradient is the sum over its query
+  heads.
+* Sliding window.  The same step ("sliding window attention"): a
+  ``window_size=(left, right)`` pair, ``(-1, -1)`` meaning no window
+  (Workflow 2, step 2), shown with ``causal=True``.  Reading taken: query i
+  sees key j iff ``j >= i - left`` (when left >= 0) and ``j <= i + right``
+  (when right >= 0), bounds inclusive, any negative value meaning that side
+  is unbounded, and causal additionally requires ``j <= i``; indices are
+  top-left aligned as for causal.  A row that sees no key at all has
+  output 0 and log-sum-exp -inf (and contributes no gradient).
+
 Layout of every array: ``[batch, heads, seq, dim]`` (``[B, H, N, d]``), float64.
 """
 import numpy as np
@@ -48,51 +64,81 @@ def _as64(x):
     return a
 
 
-def _scores(q2, k2, scale, causal, rows):
-    """s_ij = scale * q_i . k_j for the query rows ``rows`` (global indices);
-    masked entries (key j after query i) are -inf."""
-    s = scale * (q2 @ k2.T)
+def _allowed(rows, nk, causal, window):
+    """Boolean [len(rows), nk]: may query ``rows[r]`` attend key j (see the
+    module docstring for the reading of causal and the window)."""
+    left, right = int(window[0]), int(window[1])
+    keys = np.arange(nk)[None, :]
+    i = np.asarray(rows)[:, None]
+    ok = np.ones((len(rows), nk), dtype=bool)
     if causal:
-        keys = np.arange(k2.shape[0])
-        s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
-    return s
+        ok &= keys <= i
+    if left >= 0:
+        ok &= keys >= i - left
+    if right >= 0:
+        ok &= keys <= i + right
+    return ok
+
+
+def _scores(q2, k2, scale, causal, rows, window=(-1, -1)):
+    """s_ij = scale * q_i . k_j for the query rows ``rows`` (global indices);
+    entries the mask forbids are -inf."""
+    s = scale * (q2 @ k2.T)
+    return np.where(_allowed(rows, k2.shape[0], causal, window), s, -np.inf)
 
 
 def _softmax_rows(s):
     """Row softmax written out: p = exp(s - m) / sum exp(s - m) with
     m = row max (subtracting m changes nothing mathematically).  Also returns
-    lse = m + log(sum exp(s - m)) = log sum exp(s)."""
+    lse = m + log(sum exp(s - m)) = log sum exp(s).  A row of only -inf
+    (no allowed key) gets p = 0 and lse = -inf."""
     m = np.max(s, axis=1, keepdims=True)
+    empty = ~np.isfinite(m[:, 0])
+    m = np.where(np.isfinite(m), m, 0.0)
     e = np.exp(s - m)
     z = np.sum(e, axis=1, keepdims=True)
-    p = e / z
-    lse = (m + np.log(z))[:, 0]
+    p = e / np.where(z > 0, z, 1.0)
+    with np.errstate(divide="ignore"):
+        lse = (m + np.log(z))[:, 0]
+    lse[empty] = -np.inf
     return p, lse
 
 
-def attention_fwd64(q, k, v, scale, causal):
-    """O = softmax(scale * Q K^T [causal mask]) V and its log-sum-exp.
+def _kv_group(H, Hkv):
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("K/V heads (%d) must divide query heads (%d)" % (Hkv, H))
+    return H // Hkv
 
-    q: [B, H, Nq, d]; k, v: [B, H, Nk, d] (any float dtype, widened to fp64).
-    Returns (o [B, H, Nq, d], lse [B, H, Nq]) in float64.
+
+def _check(q, k, v):
+    B, H, Nq, d = q.shape
+    if k.shape[0] != B or v.shape != k.shape or k.shape[3] != d:
+        raise ValueError("shape mismatch q%r k%r v%r" % (q.shape, k.shape, v.shape))
+    return B, H, Nq, d, _kv_group(H, k.shape[1])
+
+
+def attention_fwd64(q, k, v, scale, causal, window=(-1, -1)):
+    """O = softmax(scale * Q K^T [mask]) V and its log-sum-exp.
+
+    q: [B, H, Nq, d]; k, v: [B, H_kv, Nk, d] with H_kv dividing H (any float
+    dtype, widened to fp64).  Returns (o [B, H, Nq, d], lse [B, H, Nq]) in
+    float64.
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
-    B, H, Nq, d = q.shape
-    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != d:
-        raise ValueError("shape mismatch q%r k%r v%r" % (q.shape, k.shape, v.shape))
+    B, H, Nq, d, G = _check(q, k, v)
     scale = float(scale)
     o = np.empty((B, H, Nq, d), dtype=np.float64)
     lse = np.empty((B, H, Nq), dtype=np.float64)
     rows = np.arange(Nq)
     for b in range(B):
         for h in range(H):
-            s = _scores(q[b, h], k[b, h], scale, causal, rows)
+            s = _scores(q[b, h], k[b, h // G], scale, causal, rows, window)
             p, lse[b, h] = _softmax_rows(s)
-            o[b, h] = p @ v[b, h]
+            o[b, h] = p @ v[b, h // G]
     return o, lse
 
 
-def attention_rows_fwd64(q, k, v, scale, causal, rows):
+def attention_rows_fwd64(q, k, v, scale, causal, rows, window=(-1, -1)):
     """The forward restricted to selected query rows (each against all keys).
 
     rows: int array [B, H, R] of query indices.  Returns
@@ -101,7 +147,7 @@ def attention_rows_fwd64(q, k, v, scale, causal, rows):
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     rows = np.asarray(rows, dtype=np.int64)
-    B, H, Nq, d = q.shape
+    B, H, Nq, d, G = _check(q, k, v)
     if rows.ndim != 3 or rows.shape[:2] != (B, H):
         raise ValueError("rows must be [B, H, R]")
     R = rows.shape[2]
@@ -110,35 +156,36 @@ def attention_rows_fwd64(q, k, v, scale, causal, rows):
     for b in range(B):
         for h in range(H):
             r = rows[b, h]
-            s = _scores(q[b, h][r], k[b, h], float(scale), causal, r)
+            s = _scores(q[b, h][r], k[b, h // G], float(scale), causal, r, window)
             p, lse[b, h] = _softmax_rows(s)
-            o[b, h] = p @ v[b, h]
+            o[b, h] = p @ v[b, h // G]
     return o, lse
 
 
-def attention_bwd64(q, k, v, do, scale, causal):
+def attention_bwd64(q, k, v, do, scale, causal, window=(-1, -1)):
     """Gradients of L = sum(O * dO) with respect to Q, K and V.
 
     Recomputes P from Q and K (its own P: nothing produced by a fast kernel
-    is used), then applies the chain rule listed in the module docstring.
+    is used), then applies the chain rule listed in the module docstring;
+    a K/V head accumulates the gradients of every query head that uses it.
     Returns (dq, dk, dv) with the shapes of q, k, v, in float64.
     """
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
-    B, H, Nq, d = q.shape
+    B, H, Nq, d, G = _check(q, k, v)
     if do.shape != q.shape:
         raise ValueError("dO must have the shape of Q")
     scale = float(scale)
     dq = np.empty_like(q)
-    dk = np.empty_like(k)
-    dv = np.empty_like(v)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
     rows = np.arange(Nq)
     for b in range(B):
         for h in range(H):
-            qq, kk, vv, g = q[b, h], k[b, h], v[b, h], do[b, h]
-            p, _ = _softmax_rows(_scores(qq, kk, scale, causal, rows))
-            dv[b, h] = p.T @ g
+            qq, kk, vv, g = q[b, h], k[b, h // G], v[b, h // G], do[b, h]
+            p, _ = _softmax_rows(_scores(qq, kk, scale, causal, rows, window))
+            dv[b, h // G] += p.T @ g
             dp = g @ vv.T
             ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
             dq[b, h] = scale * (ds @ kk)
-            dk[b, h] = scale * (ds.T @ qq)
+            dk[b, h // G] += scale * (ds.T @ qq)
     return dq, dk, dv
