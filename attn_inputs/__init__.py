@@ -59,17 +59,19 @@ def _shape(B, H, N, d, layout):
     raise ValueError("layout must be 'bhsd' or 'bshd'")
 
 
-def make_qkv(B, H, Nq, Nk, d, dtype, layout="bhsd", seed=0, in_scale=1.0, with_do=False):
+def make_qkv(B, H, Nq, Nk, d, dtype, layout="bhsd", seed=0, in_scale=1.0, with_do=False, Hkv=None):
     """Draw q, k, v (and dO) as described in the module docstring.
 
     Returns a dict of contiguous CPU torch tensors in the requested layout:
-    ``[B, H, N, d]`` for 'bhsd' or ``[B, N, H, d]`` for 'bshd'.
+    ``[B, H, N, d]`` for 'bhsd' or ``[B, N, H, d]`` for 'bshd'.  k and v get
+    ``Hkv`` heads (default H).
     """
     rng = np.random.default_rng(seed)
     td = torch_dtype(dtype)
+    hk = H if Hkv is None else Hkv
     out = {}
-    for name, n in (("q", Nq), ("k", Nk), ("v", Nk)) + ((("do", Nq),) if with_do else ()):
-        a = rng.standard_normal(_shape(B, H, n, d, layout), dtype=np.float32)
+    for name, n, hh in (("q", Nq, H), ("k", Nk, hk), ("v", Nk, hk)) + ((("do", Nq, H),) if with_do else ()):
+        a = rng.standard_normal(_shape(B, hh, n, d, layout), dtype=np.float32)
         if in_scale != 1.0:
             a *= np.float32(in_scale)
         out[name] = torch.from_numpy(a).to(td).contiguous()

@@ -1,9 +1,10 @@
 """Exact attention on MI355X: Python binding of libfa.so.
 
 Thin ctypes marshalling over the C ABI in ``include/fa.h``.  The functions
-named like the C entry points (``fa_fwd``, ``fa_fwd_strided``, ``fa_bwd``,
-``fa_bwd_strided``, ``fa_bwd_workspace_bytes``, ``fa_status_string``,
-``fa_last_error_message``) take torch tensors, read their sizes and strides,
+named like the C entry points (``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_ex``,
+``fa_bwd``, ``fa_bwd_strided``, ``fa_bwd_stages``, ``fa_bwd_ex``,
+``fa_bwd_workspace_bytes``, ``fa_status_string``, ``fa_last_error_message``)
+take torch tensors, read their sizes and strides,
 and call the library on the tensors' device and current stream.  Every step
 of the computation runs in the library's HIP kernels; there is no other
 implementation here, and nothing falls back: if libfa.so is missing or the
@@ -21,7 +22,8 @@ import torch
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_DEVICE", "FA_ERR_LAUNCH",
     "FA_FP16", "FA_BF16", "FaError", "lib_path", "load_library",
-    "fa_fwd", "fa_fwd_strided", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages", "fa_bwd_workspace_bytes",
+    "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages", "fa_bwd_ex",
+    "fa_bwd_workspace_bytes",
     "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
     "fa_status_string", "fa_last_error_message", "fa_abi_version",
     "attention_fwd", "attention_bwd", "EXPORTED_SYMBOLS",
@@ -32,8 +34,8 @@ FA_FP16, FA_BF16 = 0, 1
 FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED_SYMBOLS = (
-    "fa_fwd", "fa_fwd_strided", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
-    "fa_status_string", "fa_last_error_message", "fa_abi_version",
+    "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
+    "fa_bwd_ex", "fa_status_string", "fa_last_error_message", "fa_abi_version",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +79,10 @@ def load_library():
     lib.fa_bwd_strided.restype = _i
     lib.fa_bwd_stages.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i] + [_I64x3] * 8 + [_vp, _sz, _i, _vp]
     lib.fa_bwd_stages.restype = _i
+    lib.fa_fwd_ex.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _i, _i, _i] + [_I64x3] * 4 + [_vp]
+    lib.fa_fwd_ex.restype = _i
+    lib.fa_bwd_ex.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _i, _i, _i, _i] + [_I64x3] * 8 + [_vp, _sz, _i, _vp]
+    lib.fa_bwd_ex.restype = _i
     lib.fa_status_string.argtypes = [_i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error_message.argtypes = []
@@ -231,11 +237,50 @@ def fa_bwd_stages(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, sta
             _stream(q, stream)))
 
 
-def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None):
+def _window(window):
+    left, right = (-1, -1) if window is None else window
+    return int(left), int(right)
+
+
+def fa_fwd_ex(q, k, v, o, lse, scale, causal, window=(-1, -1), layout="bhsd", stream=None):
+    """C ``fa_fwd_ex``: k, v may have fewer heads than q (it must divide q's);
+    ``window`` = (left, right), a negative side unbounded."""
+    dt = _dtype_code(q)
+    _on_device(q, k, v, o, lse)
+    B, H, Nq, d = _dims(q, layout)
+    Hkv, Nk = _dims(k, layout)[1:3]
+    wl, wr = _window(window)
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_fwd_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+            wl, wr, dt, _strides(q, layout), _strides(k, layout), _strides(v, layout), _strides(o, layout),
+            _stream(q, stream)))
+
+
+def fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, window=(-1, -1), stages=FA_BWD_ALL,
+              layout="bhsd", stream=None):
+    """C ``fa_bwd_ex``: the backward of ``fa_fwd_ex`` (dk, dv shaped like k, v)."""
+    dt = _dtype_code(q)
+    _on_device(q, k, v, o, lse, do, dq, dk, dv, workspace)
+    B, H, Nq, d = _dims(q, layout)
+    Hkv, Nk = _dims(k, layout)[1:3]
+    wl, wr = _window(window)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = [_strides(t, layout) for t in (q, k, v, o, do, dq, dk, dv)]
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_bwd_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), wl, wr, dt, *st, _ptr(workspace), nbytes,
+            int(stages), _stream(q, stream)))
+
+
+def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None, window=None):
     """O = softmax(scale Q K^T) V (top-left causal mask if ``causal``).
 
     Allocates o (like q) and lse (fp32 [B,H,Nq]); returns (o, lse).  ``scale``
-    defaults to 1/sqrt(d).
+    defaults to 1/sqrt(d).  k and v may carry fewer heads than q (dividing
+    them); ``window`` = (left, right) restricts query i to keys
+    i - left .. i + right (negative: unbounded).
     """
     _dtype_code(q)
     _on_device(q, k, v)
@@ -243,24 +288,29 @@ def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None)
     s = _default_scale(d, scale)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if layout == "bhsd" and q.is_contiguous() and k.is_contiguous() and v.is_contiguous():
+    if _dims(k, layout)[1] != H or window is not None:
+        fa_fwd_ex(q, k, v, o, lse, s, causal, window, layout, stream)
+    elif layout == "bhsd" and q.is_contiguous() and k.is_contiguous() and v.is_contiguous():
         fa_fwd(q, k, v, o, lse, s, causal, stream)
     else:
         fa_fwd_strided(q, k, v, o, lse, s, causal, layout, stream)
     return o, lse
 
 
-def attention_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bhsd", stream=None):
-    """Gradients (dq, dk, dv) of sum(O * dO), recomputing P from ``lse``."""
+def attention_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bhsd", stream=None, window=None):
+    """Gradients (dq, dk, dv) of sum(O * dO), recomputing P from ``lse``
+    (fewer K/V heads and ``window`` as in ``attention_fwd``)."""
     _on_device(q, k, v, o, lse, do)
     B, H, Nq, d = _dims(q, layout)
-    Nk = _dims(k, layout)[2]
+    Hkv, Nk = _dims(k, layout)[1:3]
     s = _default_scale(d, scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nbytes = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, _dtype_code(q))
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     contiguous = all(t.is_contiguous() for t in (q, k, v, o, do))
-    if layout == "bhsd" and contiguous:
+    if Hkv != H or window is not None:
+        fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, window, FA_BWD_ALL, layout, stream)
+    elif layout == "bhsd" and contiguous:
         fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, stream)
     else:
         fa_bwd_strided(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, layout, stream)

@@ -102,6 +102,28 @@ int check_common(int B, int H, int Nq, int Nk, int d, float scale, int causal, i
   return FA_OK;
 }
 
+int check_heads(int B, int H, int H_kv) {
+  if (B == 0 || H == 0) return FA_OK;
+  if (H_kv < 1) return fail(FA_ERR_INVALID_ARG, "H_kv = %d must be >= 1", H_kv);
+  if (H % H_kv != 0) return fail(FA_ERR_INVALID_ARG, "H_kv = %d does not divide H = %d", H_kv, H);
+  return FA_OK;
+}
+
+// Admitted keys of query i: [i - wl, i + wr], a negative bound meaning none.
+// Causal is wr = 0 (and tighter than any right window).  A bound that
+// excludes nothing (wl >= Nq: i - wl < 0; wr >= Nk: i + wr >= Nk) is
+// dropped, which also keeps the kernels' index sums far from overflow.
+struct Band {
+  int wl, wr;
+  bool present() const { return wl >= 0 || wr >= 0; }
+};
+Band make_band(int causal, int window_left, int window_right, int Nq, int Nk) {
+  Band b;
+  b.wl = (window_left < 0 || window_left >= Nq) ? -1 : window_left;
+  b.wr = causal ? 0 : ((window_right < 0 || window_right >= Nk) ? -1 : window_right);
+  return b;
+}
+
 float softmax_c(float scale) {
   // |scale| * log2(e); a tiny floor keeps c > 0 so masked (-inf) scores stay
   // -inf after scaling.  For |scale| below it the weights are uniform to
@@ -120,7 +142,7 @@ void contiguous_strides(int H, int N, int d, int64_t st[3]) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 1; }
+int fa_abi_version(void) { return 2; }
 
 const char* fa_status_string(int status) {
   switch (status) {
@@ -135,19 +157,20 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error_message(void) { return g_msg; }
 
-int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
-                   int d, float scale, int causal, int dtype, const int64_t q_strides[3],
-                   const int64_t k_strides[3], const int64_t v_strides[3], const int64_t o_strides[3],
-                   void* stream) {
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int Nq,
+              int Nk, int d, float scale, int causal, int window_left, int window_right, int dtype,
+              const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+              const int64_t o_strides[3], void* stream) {
   g_msg[0] = '\0';
   int st = check_common(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st) return st;
+  if ((st = check_heads(B, H, H_kv))) return st;
   if (!q_strides || !k_strides || !v_strides || !o_strides) return fail(FA_ERR_INVALID_ARG, "a strides array is NULL");
   if (B == 0 || H == 0 || Nq == 0) return FA_OK;
   Extent eq, ek, ev, eo;
   if ((st = check_tensor("q", q, q_strides, B, H, Nq, d, &eq))) return st;
-  if ((st = check_tensor("k", k, k_strides, B, H, Nk, d, &ek))) return st;
-  if ((st = check_tensor("v", v, v_strides, B, H, Nk, d, &ev))) return st;
+  if ((st = check_tensor("k", k, k_strides, B, H_kv, Nk, d, &ek))) return st;
+  if ((st = check_tensor("v", v, v_strides, B, H_kv, Nk, d, &ev))) return st;
   if ((st = check_tensor("o", o, o_strides, B, H, Nq, d, &eo))) return st;
   if (!lse) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
@@ -172,11 +195,23 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
   p.H = H;
   p.Nq = Nq;
   p.Nk = Nk;
+  p.G = H / H_kv;
+  const Band band = make_band(causal, window_left, window_right, Nq, Nk);
+  p.wl = band.wl;
+  p.wr = band.wr;
   p.c = softmax_c(scale);
   p.qflip = std::signbit(scale) ? 0x80008000u : 0u;
-  hipError_t e = fa::launch_fwd(p, d, dtype, causal != 0, static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_fwd(p, d, dtype, band.present(), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, int dtype, const int64_t q_strides[3],
+                   const int64_t k_strides[3], const int64_t v_strides[3], const int64_t o_strides[3],
+                   void* stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, -1, -1, dtype, q_strides, k_strides, v_strides,
+                   o_strides, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
@@ -192,15 +227,16 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
   return fa::bwd_workspace_bytes(B, H, Nq);
 }
 
-int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                  void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                  int dtype, const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
-                  const int64_t o_strides[3], const int64_t do_strides[3], const int64_t dq_strides[3],
-                  const int64_t dk_strides[3], const int64_t dv_strides[3], void* workspace,
-                  size_t workspace_bytes, int stages, void* stream) {
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+              int window_left, int window_right, int dtype, const int64_t q_strides[3], const int64_t k_strides[3],
+              const int64_t v_strides[3], const int64_t o_strides[3], const int64_t do_strides[3],
+              const int64_t dq_strides[3], const int64_t dk_strides[3], const int64_t dv_strides[3],
+              void* workspace, size_t workspace_bytes, int stages, void* stream) {
   g_msg[0] = '\0';
   int st = check_common(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st) return st;
+  if ((st = check_heads(B, H, H_kv))) return st;
   if (stages <= 0 || (stages & ~FA_BWD_ALL)) return fail(FA_ERR_INVALID_ARG, "stages = %d is not a nonzero OR of FA_BWD_*", stages);
   if (!q_strides || !k_strides || !v_strides || !o_strides || !do_strides || !dq_strides || !dk_strides || !dv_strides)
     return fail(FA_ERR_INVALID_ARG, "a strides array is NULL");
@@ -208,13 +244,13 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
   if (Nq == 0 && Nk == 0) return FA_OK;  // with Nq = 0 and Nk > 0, dK = dV = 0 are written
   Extent eq, ek, ev, eo, edo, edq, edk, edv;
   if ((st = check_tensor("q", q, q_strides, B, H, Nq, d, &eq))) return st;
-  if ((st = check_tensor("k", k, k_strides, B, H, Nk, d, &ek))) return st;
-  if ((st = check_tensor("v", v, v_strides, B, H, Nk, d, &ev))) return st;
+  if ((st = check_tensor("k", k, k_strides, B, H_kv, Nk, d, &ek))) return st;
+  if ((st = check_tensor("v", v, v_strides, B, H_kv, Nk, d, &ev))) return st;
   if ((st = check_tensor("o", o, o_strides, B, H, Nq, d, &eo))) return st;
   if ((st = check_tensor("dout", dout, do_strides, B, H, Nq, d, &edo))) return st;
   if ((st = check_tensor("dq", dq, dq_strides, B, H, Nq, d, &edq))) return st;
-  if ((st = check_tensor("dk", dk, dk_strides, B, H, Nk, d, &edk))) return st;
-  if ((st = check_tensor("dv", dv, dv_strides, B, H, Nk, d, &edv))) return st;
+  if ((st = check_tensor("dk", dk, dk_strides, B, H_kv, Nk, d, &edk))) return st;
+  if ((st = check_tensor("dv", dv, dv_strides, B, H_kv, Nk, d, &edv))) return st;
   if (Nq > 0 && !lse) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   const size_t need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype);
@@ -260,11 +296,26 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
   p.H = H;
   p.Nq = Nq;
   p.Nk = Nk;
+  p.G = H / H_kv;
+  const Band band = make_band(causal, window_left, window_right, Nq, Nk);
+  p.wl = band.wl;
+  p.wr = band.wr;
   p.scale = scale;
   p.c = scale * 1.4426950408889634f;
-  hipError_t e = fa::launch_bwd(p, d, dtype, causal != 0, stages, static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_bwd(p, d, dtype, band.present(), stages, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                  int dtype, const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+                  const int64_t o_strides[3], const int64_t do_strides[3], const int64_t dq_strides[3],
+                  const int64_t dk_strides[3], const int64_t dv_strides[3], void* workspace,
+                  size_t workspace_bytes, int stages, void* stream) {
+  return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, Nq, Nk, d, scale, causal, -1, -1, dtype, q_strides,
+                   k_strides, v_strides, o_strides, do_strides, dq_strides, dk_strides, dv_strides, workspace,
+                   workspace_bytes, stages, stream);
 }
 
 int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -89,7 +89,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(BwdParams p, int blocks_
   if (ch == 0 && row < stat_stride(p.Nq)) {
     const int64_t o = (int64_t)bh * stat_stride(p.Nq) + row;
     p.dsum[o] = -acc;  // stored negated: it seeds the dP accumulators
-    p.lse2[o] = row < p.Nq ? p.lse[(int64_t)bh * p.Nq + row] * kLog2e : 0.f;
+    // a row that admitted no key has lse = -inf; +inf here makes its
+    // recomputed P = 2^(s c - lse2) zero
+    const float l = row < p.Nq ? p.lse[(int64_t)bh * p.Nq + row] : 0.f;
+    p.lse2[o] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
   }
 }
 
@@ -189,7 +192,7 @@ __device__ __forceinline__ void wait_ring(int later) {
 //   phase 2: A  dV += .. P(t); S(t+1)               B  dS(t) = P(t) (dP(t) - D)
 // Query tiles (Q, dO and the two row statistics) stream HBM -> LDS through
 // a 4-slot ring; tile t+3 is requested in phase 2 of step t.
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool BAND>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(BwdParams p) {
   constexpr int KW = 32;            // keys per pair
   constexpr int NPAIR = kWaves;     // pairs per workgroup
@@ -218,29 +221,46 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave & (NPAIR - 1);
   const bool role_a = wave < NPAIR;
-  const int BH = p.B * p.H;
+  const int Hkv = p.H / p.G;
+  const int BH = p.B * Hkv;  // workgroups per key tile: one per (batch, K/V head)
   const int t = blockIdx.x;
   const int kt = t / BH;  // ascending key tiles: the causal-heaviest first
-  const int bh = t - kt * BH;
-  const int b = bh / p.H, h = bh - b * p.H;
+  const int bhk = t - kt * BH;
+  const int b = bhk / Hkv, hk = bhk - b * Hkv;
   const int k0 = kt * BNK;
   const int kw0 = k0 + pair * KW;
   const int key = kw0 + col;
 
   const int sst = stat_stride(p.Nq);
-  // role A streams Q and lse2, role B dO and -D
-  const uint16_t* tp = role_a ? p.q + b * p.sq.b + h * p.sq.h : p.dout + b * p.sdo.b + h * p.sdo.h;
   const int64_t tstride = role_a ? p.sq.s : p.sdo.s;
-  const __amdgpu_buffer_rsrc_t trs = head_rsrc(tp, p.Nq, tstride, D);
-  const __amdgpu_buffer_rsrc_t srs = f32_rsrc((role_a ? p.lse2 : p.dsum) + (int64_t)bh * sst, sst);
   const uint32_t trow = (uint32_t)(tstride * 2);
 
-  const int qt0 = CAUSAL ? (k0 / kT) : 0;
+  // Query tiles [qlo, qhi) of each of the G query heads of K/V head hk:
+  // those with a query whose band admits a key of this workgroup.  The
+  // steps run over u = g * nq + (it - qlo) for head hk * G + g.
   const int n_qt = (p.Nq + kT - 1) / kT;
+  int qlo = 0, qhi = n_qt;
+  if (BAND) {
+    if (p.wr >= 0) qlo = max(0, k0 - p.wr) / kT;
+    if (p.wl >= 0) qhi = min(n_qt, (k0 + BNK - 1 + p.wl) / kT + 1);
+  }
+  const int nq = max(0, qhi - qlo);
+  const int U = p.G * nq;
 
-  auto issue = [&](int it, int slot) {
-    TC::issue(trs, trow, (uint32_t)it * kT * trow, role_a ? sm.q[slot] : sm.o[slot], lane, pair);
-    vec_to_lds<8>(srs, (uint32_t)(it * kT + 8 * pair) * 4, (role_a ? sm.l[slot] : sm.d[slot]) + 8 * pair, lane);
+  // requests go out in step order; (iss_h, iss_it) is the next one's tile
+  int iss_h = hk * p.G, iss_it = qlo;
+  auto issue = [&](int slot) {
+    // role A streams Q and lse2, role B dO and -D
+    const uint16_t* tp = role_a ? p.q + b * p.sq.b + iss_h * p.sq.h : p.dout + b * p.sdo.b + iss_h * p.sdo.h;
+    const __amdgpu_buffer_rsrc_t trs = head_rsrc(tp, p.Nq, tstride, D);
+    const __amdgpu_buffer_rsrc_t srs =
+        f32_rsrc((role_a ? p.lse2 : p.dsum) + ((int64_t)b * p.H + iss_h) * sst, sst);
+    TC::issue(trs, trow, (uint32_t)iss_it * kT * trow, role_a ? sm.q[slot] : sm.o[slot], lane, pair);
+    vec_to_lds<8>(srs, (uint32_t)(iss_it * kT + 8 * pair) * 4, (role_a ? sm.l[slot] : sm.d[slot]) + 8 * pair, lane);
+    if (++iss_it == qhi) {
+      iss_it = qlo;
+      ++iss_h;
+    }
   };
 
   // The two roles run separate copies of the loop (one barrier per step in
@@ -252,7 +272,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     // row `key`, columns 16*ks + 8*half .. +7 (zeros past Nk).
     u32x4 kv[KS];
     {
-      const uint16_t* rp = A ? p.k + b * p.sk.b + h * p.sk.h : p.v + b * p.sv.b + h * p.sv.h;
+      const uint16_t* rp = A ? p.k + b * p.sk.b + hk * p.sk.h : p.v + b * p.sv.b + hk * p.sv.h;
       const int64_t rs = A ? p.sk.s : p.sv.s;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -262,7 +282,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
       }
     }
     for (int i = 0; i < PD; ++i)
-      if (qt0 + i < n_qt) issue(qt0 + i, i);
+      if (i < U) issue(i);
     // The slot before the first tile's (not loaded before tile qt0 + PD)
     // is read by B's first dK update with dS = 0: make it finite zeros.
     if constexpr (!A) {
@@ -284,18 +304,19 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     // Tile pointers are __restrict__ parameters of inlined lambdas so that
     // their LDS reads carry alias scopes; the compiler then leaves the
     // in-flight copies into other slots alone (the vmcnt waits and barriers
-    // order the ring).  Tile qt0 + r lives in slot r mod NB.
-    wait_ring<PD - 2, NLOADS>(n_qt - 1 - (qt0 + 1));  // tiles qt0, qt0+1 landed
+    // order the ring).  The tile of step u lives in slot u mod NB.
+    wait_ring<PD - 2, NLOADS>(U - 2);  // the tiles of steps 0 and 1 landed
     lds_barrier();
     if constexpr (A) {
       auto s_tile = [&](const uint16_t* __restrict__ Qt) { sd = rows_times_regs<D, DT>(Qt, kv, ta); };
-      if (qt0 < n_qt) s_tile(sm.q[0]);
+      if (U > 0) s_tile(sm.q[0]);
     }
 
     // One step.  (Unrolling by the ring depth would turn the slot bases
     // into immediates, but makes this compiler spill role A's registers.)
-    auto step = [&](int it) {
-      const int SL = (it - qt0) & (NB - 1);
+    int it = qlo;  // query tile of the current step
+    auto step = [&](int u) {
+      const int SL = u & (NB - 1);
       const int XB = SL & 1;
       const int i0 = it * kT;
 
@@ -309,14 +330,19 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
             for (int e = 0; e < 4; ++e) sd[4 * g4 + e] = exp2_fast(__builtin_fmaf(sd[4 * g4 + e], c, -lz[e]));
           }
-          if (CAUSAL && i0 < kw0 + KW - 1) {  // the tile crosses the pair's diagonal
+          // tiles that cross an edge of the pair's band
+          if (BAND && ((p.wr >= 0 && i0 < kw0 + KW - 1 - p.wr) || (p.wl >= 0 && i0 + kT - 1 > kw0 + p.wl))) {
             // (the empty asm keeps this a branch: if-converted, the compares
             // would run on every tile)
             asm volatile("");
-            const int kd = key - i0 - 4 * half;  // query row of acc_row(half, r) is i0 + 4*half + (8*(r/4) + r%4)
+            // query of register r is i0 + 4*half + ro(r), ro(r) = 8*(r/4) + r%4;
+            // key > query + wr  <=>  kd - wr > ro;  key < query - wl  <=>  kd + wl < ro
+            const int kd = key - i0 - 4 * half;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (kd > ((r >> 2) << 3) + (r & 3)) sd[r] = 0.f;
+            for (int r = 0; r < 16; ++r) {
+              const int ro = ((r >> 2) << 3) + (r & 3);
+              if ((p.wr >= 0 && kd - p.wr > ro) || (p.wl >= 0 && kd + p.wl < ro)) sd[r] = 0.f;
+            }
           }
           pk[0] = pack_acc8<DT>(sd, 0);
           pk[1] = pack_acc8<DT>(sd, 1);
@@ -349,13 +375,13 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         phase(sm.o[SL], sm.d[SL], sm.q[(SL + NB - 1) & (NB - 1)]);
       }
 
-      // tile it+1 must have landed (A reads its Q rows next); the later
-      // requested ones fly on
-      wait_ring<PD - 2, NLOADS>(n_qt - 1 - (it + 1));
+      // step u+1's tile must have landed (A reads its Q rows next); the
+      // later requested ones fly on
+      wait_ring<PD - 2, NLOADS>(U - 1 - (u + 1));
       lds_barrier();
-      // tile it+PD's slot held tile it-1, whose last reader (B's dK)
+      // step u+PD's slot held step u-1's tile, whose last reader (B's dK)
       // finished before the barrier
-      if (it + PD < n_qt) issue(it + PD, (SL + PD) & (NB - 1));
+      if (u + PD < U) issue((SL + PD) & (NB - 1));
 
       // ---------------- phase 2
       if constexpr (A) {
@@ -380,18 +406,19 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         };
         phase(&sm.x[XB][pair][0][0]);
       }
+      if (++it == qhi) it = qlo;
     };
-    for (int it = qt0; it < n_qt; ++it) step(it);
+    for (int u = 0; u < U; ++u) step(u);
     if constexpr (!A) {
       auto last = [&](const uint16_t* __restrict__ Qt) { tile_t_times<D, DT>(acc, Qt, pk, ta); };
-      if (qt0 < n_qt) last(sm.q[(n_qt - 1 - qt0) & (NB - 1)]);
+      if (U > 0) last(sm.q[(U - 1) & (NB - 1)]);
     }
 
     if (key < p.Nk) {
       if constexpr (A) {
-        store_rows<DT, DB>(p.dv + b * p.sdv.b + h * p.sdv.h + key * p.sdv.s, acc, 1.0f, half);
+        store_rows<DT, DB>(p.dv + b * p.sdv.b + hk * p.sdv.h + key * p.sdv.s, acc, 1.0f, half);
       } else {
-        store_rows<DT, DB>(p.dk + b * p.sdk.b + h * p.sdk.h + key * p.sdk.s, acc, p.scale, half);
+        store_rows<DT, DB>(p.dk + b * p.sdk.b + hk * p.sdk.h + key * p.sdk.s, acc, p.scale, half);
       }
     }
   };
@@ -403,7 +430,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 }
 
 // ------------------------------------------------------------ dQ
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool BAND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(BwdParams p) {
   constexpr int QW = 32;
   constexpr int BM = kWaves * QW;
@@ -432,22 +459,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int qw0 = q0 + wave * QW;
   const int qi = qw0 + col;
 
-  const uint16_t* kp = p.k + b * p.sk.b + h * p.sk.h;
-  const uint16_t* vp = p.v + b * p.sv.b + h * p.sv.h;
+  const int hk = h / p.G;  // K/V head shared by p.G consecutive query heads
+  const uint16_t* kp = p.k + b * p.sk.b + hk * p.sk.h;
+  const uint16_t* vp = p.v + b * p.sv.b + hk * p.sv.h;
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(kp, p.Nk, p.sk.s, D);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vp, p.Nk, p.sv.s, D);
   const uint32_t krow = (uint32_t)(p.sk.s * 2), vrow = (uint32_t)(p.sv.s * 2);
 
-  int kend = p.Nk;
-  if (CAUSAL) kend = min(p.Nk, min(q0 + BM, p.Nq));
+  // key tiles [jt0, n_kt): those some query of the block admits
+  int kend = p.Nk, jt0 = 0;
+  if (BAND) {
+    const int qlast = min(q0 + BM, p.Nq) - 1;
+    if (p.wr >= 0) kend = min(p.Nk, qlast + p.wr + 1);
+    if (p.wl >= 0) jt0 = max(0, q0 - p.wl) / kT;
+  }
   const int n_kt = (kend + kT - 1) / kT;
 
   auto issue = [&](int j, int slot) {
     TC::issue(krs, krow, (uint32_t)j * kT * krow, Ks[slot], lane, wave);
     TC::issue(vrs, vrow, (uint32_t)j * kT * vrow, Vs[slot], lane, wave);
   };
-  if (n_kt > 0) issue(0, 0);
-  if (n_kt > 1) issue(1, 1);
+  if (jt0 < n_kt) issue(jt0, 0);
+  if (jt0 + 1 < n_kt) issue(jt0 + 1, 1);
 
   // Q^T and dO^T of this wave's queries as B operands (zeros past Nq).
   u32x4 qf[KS], of[KS];
@@ -484,24 +517,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   lds_barrier();
 
   int slot = 0;
-  for (int j = 0; j < n_kt; ++j) {
+  for (int j = jt0; j < n_kt; ++j) {
     const int j0 = j * kT;
     int nslot = slot + 2;
     nslot = nslot >= kNBuf ? nslot - kNBuf : nslot;
     if (j + 2 < n_kt) issue(j + 2, nslot);
 
-    const bool active = qw0 < p.Nq && !(CAUSAL && j0 > qw0 + QW - 1);
+    // skip tiles outside this wave's band
+    const bool active = qw0 < p.Nq && !(BAND && ((p.wr >= 0 && j0 > qw0 + QW - 1 + p.wr) ||
+                                                 (p.wl >= 0 && j0 + kT - 1 < qw0 - p.wl)));
     auto body = [&](const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ Vt) {  // as in dkdv_kernel
       // S^T = K Q^T and dP^T = V dO^T: rows are keys j0 + acc_row(half, r); column = this lane's query
       f32x16 s = rows_times_regs<D, DT>(Kt, qf, ta);
       f32x16 dp = rows_times_regs<D, DT>(Vt, of, ta, dinit);  // dP^T - D
-      const bool need_mask = (j0 + kT > p.Nk) || (CAUSAL && j0 + kT - 1 > qw0);
+      const bool need_mask = (j0 + kT > p.Nk) || (BAND && ((p.wr >= 0 && j0 + kT - 1 > qw0 + p.wr) ||
+                                                            (p.wl >= 0 && j0 < qw0 + QW - 1 - p.wl)));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = exp2_fast(__builtin_fmaf(s[r], c, -lse2));
         if (need_mask) {
           const int kk = j0 + acc_row(half, r);
-          if (kk >= p.Nk || (CAUSAL && kk > qi)) pv = 0.f;
+          if (kk >= p.Nk || (BAND && ((p.wr >= 0 && kk > qi + p.wr) || (p.wl >= 0 && kk < qi - p.wl)))) pv = 0.f;
         }
         dp[r] = pv * dp[r];
       }
@@ -522,13 +558,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   if (qi < p.Nq) store_rows<DT, DB>(p.dq + b * p.sdq.b + h * p.sdq.h + qi * p.sdq.s, adq, p.scale, half);
 }
 
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool BAND>
 hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
   const int64_t BH = (int64_t)p.B * p.H;
+  const int64_t BHkv = (int64_t)p.B * (p.H / p.G);
   constexpr int RPB = kThreads / (D / 8);
   const int64_t prep_bpb = (stat_stride(p.Nq) + RPB - 1) / RPB;
   const int64_t g0 = prep_bpb * BH;
-  const int64_t g1 = (int64_t)((p.Nk + 127) / 128) * BH;
+  const int64_t g1 = (int64_t)((p.Nk + 127) / 128) * BHkv;
   const int64_t g2 = (int64_t)((p.Nq + 127) / 128) * BH;
   if (g0 > 0x7fffffff || g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipError_t e = hipSuccess;
@@ -537,25 +574,25 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((stages & 2) && g1 > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<D, DT, CAUSAL>), dim3((unsigned)g1), dim3(2 * kThreads), 0, stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND>), dim3((unsigned)g1), dim3(2 * kThreads), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((stages & 4) && g2 > 0) {
-    hipLaunchKernelGGL((dq_kernel<D, DT, CAUSAL>), dim3((unsigned)g2), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((dq_kernel<D, DT, BAND>), dim3((unsigned)g2), dim3(kThreads), 0, stream, p);
     e = hipGetLastError();
   }
   return e;
 }
 
 template <int D, int DT>
-hipError_t launch_dc(const BwdParams& p, bool causal, int stages, hipStream_t stream) {
-  return causal ? launch_t<D, DT, true>(p, stages, stream) : launch_t<D, DT, false>(p, stages, stream);
+hipError_t launch_dc(const BwdParams& p, bool banded, int stages, hipStream_t stream) {
+  return banded ? launch_t<D, DT, true>(p, stages, stream) : launch_t<D, DT, false>(p, stages, stream);
 }
 
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int Nq) {
-  // D and lse*log2(e): two fp32 arrays of stat_stride(Nq) values per (b, h)
+  // -D and lse*log2(e): two fp32 arrays of stat_stride(Nq) values per (b, h)
   const size_t n = (size_t)B * (size_t)H * (size_t)stat_stride(Nq) * sizeof(float) * 2;
   return (n + 255) & ~(size_t)255;
 }
@@ -564,12 +601,12 @@ float* bwd_lse2_region(void* workspace, int B, int H, int Nq) {
   return static_cast<float*>(workspace) + (size_t)B * (size_t)H * (size_t)stat_stride(Nq);
 }
 
-hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool causal, int stages, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int stages, hipStream_t stream) {
   if (d == 64)
-    return dtype == DT_F16 ? launch_dc<64, DT_F16>(p, causal, stages, stream)
-                           : launch_dc<64, DT_BF16>(p, causal, stages, stream);
-  return dtype == DT_F16 ? launch_dc<128, DT_F16>(p, causal, stages, stream)
-                         : launch_dc<128, DT_BF16>(p, causal, stages, stream);
+    return dtype == DT_F16 ? launch_dc<64, DT_F16>(p, banded, stages, stream)
+                           : launch_dc<64, DT_BF16>(p, banded, stages, stream);
+  return dtype == DT_F16 ? launch_dc<128, DT_F16>(p, banded, stages, stream)
+                         : launch_dc<128, DT_BF16>(p, banded, stages, stream);
 }
 
 }  // namespace fa

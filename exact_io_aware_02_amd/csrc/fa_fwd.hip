@@ -29,9 +29,14 @@
 // SIMD work at the same time within one wave (the overlap FA3 gets from
 // asynchrony on Hopper, glossary article's FA-3 section).
 //
-// Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2.  Causal: tiles wholly
-// after a workgroup's last query are never loaded; tiles that cross a
-// wave's diagonal or the key tail are masked elementwise.
+// Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2 (O = 0, LSE = -inf for
+// a row that admits no key).  Masks: query i admits keys i - wl .. i + wr
+// (a negative bound is absent; causal is wr = 0; the skill guide's
+// Workflow 2 step 3 sliding window is (wl, wr)).  Key tiles outside every
+// query's band of the workgroup are never loaded; tiles that cross an edge
+// of a wave's band, or the key tail, are masked elementwise.  With fewer
+// K/V heads (the same step's multi-query attention) query head h reads
+// K/V head h / G.
 //
 // This is the blocking / online-softmax / single merged write-back
 // pipeline of the glossary article's "FlashAttention の仕組み" figure
@@ -88,13 +93,13 @@ struct RowState {
 // The __restrict__ tile pointers tell the compiler the reads never alias
 // the in-flight copy, so it does not wait for that copy before reading;
 // the vmcnt wait and barrier at the end order the ring.
-template <int D, int DT, bool CAUSAL, int kNQB = FwdTile<D>::NQB>
+template <int D, int DT, bool BAND, int kNQB = FwdTile<D>::NQB>
 __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32x16 (&sn)[kNQB],
                                          const uint16_t* __restrict__ Kn, const uint16_t* __restrict__ Vt,
                                          uint16_t* __restrict__ Kdst, uint16_t* __restrict__ Vdst,
                                          __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, uint32_t krow,
                                          uint32_t vrow, uint32_t ktb, uint32_t vtb, const u32x4 (&qf)[kNQB][D / 16],
-                                         f32x16 (&acc)[D / 32][kNQB], RowState<kNQB>& st, int Nk, int qw0, float c,
+                                         f32x16 (&acc)[D / 32][kNQB], RowState<kNQB>& st, int Nk, int wl, int wr, int qw0, float c,
                                          int lane, int wave, const TileAddr<D>& ta) {
   using TC = TileCopy<D>;
   constexpr int KS = D / 16;
@@ -107,15 +112,18 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
     TC::issue(vrs, vrow, (uint32_t)(j + 3) * vtb, Vdst, lane, wave);
   }
 
-  // ---- masks (only tiles crossing the key tail or this wave's diagonal)
-  if ((j0 + kBN > Nk) || (CAUSAL && j0 + kBN - 1 > qw0)) {
+  // ---- masks (only tiles crossing the key tail or an edge of this wave's band)
+  constexpr int QW = 32 * kNQB;
+  if ((j0 + kBN > Nk) ||
+      (BAND && ((wr >= 0 && j0 + kBN - 1 > qw0 + wr) || (wl >= 0 && j0 < qw0 + QW - 1 - wl)))) {
 #pragma unroll
     for (int nb = 0; nb < kNQB; ++nb) {
       const int qi = qw0 + 32 * nb + col;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + acc_row(half, r);
-        if (key >= Nk || (CAUSAL && key > qi)) s[nb][r] = -__builtin_inff();
+        if (key >= Nk || (BAND && ((wr >= 0 && key > qi + wr) || (wl >= 0 && key < qi - wl))))
+          s[nb][r] = -__builtin_inff();
       }
     }
   }
@@ -203,7 +211,7 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool BAND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTile<D>::WAVES_PER_SIMD,
                                                                           FwdTile<D>::WAVES_PER_SIMD))) void fwd_kernel(FwdParams p) {
   constexpr int kNQB = FwdTile<D>::NQB;
@@ -242,12 +250,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kQW;
 
+  const int hk = h / p.G;  // K/V head shared by p.G consecutive query heads
   const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h;
-  const uint16_t* kp = p.k + b * p.sk.b + h * p.sk.h;
-  const uint16_t* vp = p.v + b * p.sv.b + h * p.sv.h;
+  const uint16_t* kp = p.k + b * p.sk.b + hk * p.sk.h;
+  const uint16_t* vp = p.v + b * p.sv.b + hk * p.sv.h;
 
-  int kend = p.Nk;
-  if (CAUSAL) kend = min(p.Nk, min(q0 + kBM, p.Nq));
+  // key tiles [jt0, n_kt): those some query of the block admits
+  int kend = p.Nk, jt0 = 0;
+  if (BAND) {
+    const int qlast = min(q0 + kBM, p.Nq) - 1;
+    if (p.wr >= 0) kend = min(p.Nk, qlast + p.wr + 1);
+    if (p.wl >= 0) jt0 = max(0, q0 - p.wl) / kBN;
+  }
   const int n_kt = (kend + kBN - 1) / kBN;
 
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(kp, p.Nk, p.sk.s, D);
@@ -270,13 +284,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
       qf[nb][ks] = x;
     }
   }
-  // prologue: tiles 0..2 in flight
+  // prologue: tiles jt0 .. jt0+2 in flight (tile j lives in slot j mod 4)
 #pragma unroll
-  for (int t0 = 0; t0 < 3; ++t0)
-    if (t0 < n_kt) {
-      TC::issue(krs, krow, (uint32_t)t0 * ktb, Ks[t0], lane, wave);
-      TC::issue(vrs, vrow, (uint32_t)t0 * vtb, Vs[t0], lane, wave);
+  for (int t0 = 0; t0 < 3; ++t0) {
+    const int jj = jt0 + t0;
+    if (jj < n_kt) {
+      TC::issue(krs, krow, (uint32_t)jj * ktb, Ks[jj & 3], lane, wave);
+      TC::issue(vrs, vrow, (uint32_t)jj * vtb, Vs[jj & 3], lane, wave);
     }
+  }
 
   f32x16 acc[DB][kNQB];
 #pragma unroll
@@ -294,7 +310,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   TileAddr<D> ta;
   ta.init(lane);
 
-  if (n_kt > 2) {
+  if (n_kt - jt0 > 2) {
     wait_vmcnt<2 * TC::NI>();
   } else {
     wait_loads();
@@ -311,17 +327,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   for (int nb = 0; nb < kNQB; ++nb) sa[nb] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const u32x4 a = lds_b128(Ks[0], ta.rm[ks]);
+    const u32x4 a = lds_b128(Ks[jt0 & 3], ta.rm[ks]);
 #pragma unroll
     for (int nb = 0; nb < kNQB; ++nb) sa[nb] = mfma32<DT>(a, qf[nb][ks], sa[nb]);
   }
 
   // (Unrolling by two so that S alternates between the two register sets
   // without the copy costs ~60 more registers and spills at d = 64.)
-  for (int j = 0; j < n_kt; ++j) {
+  for (int j = jt0; j < n_kt; ++j) {
     const int sl = j & 3;
-    fwd_step<D, DT, CAUSAL>(j, n_kt, sa, sb, Ks[(sl + 1) & 3], Vs[sl], Ks[(sl + 3) & 3], Vs[(sl + 3) & 3], krs, vrs,
-                            krow, vrow, ktb, vtb, qf, acc, st, p.Nk, qw0, c, lane, wave, ta);
+    fwd_step<D, DT, BAND>(j, n_kt, sa, sb, Ks[(sl + 1) & 3], Vs[sl], Ks[(sl + 3) & 3], Vs[(sl + 3) & 3], krs, vrs,
+                          krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta);
 #pragma unroll
     for (int nb = 0; nb < kNQB; ++nb) sa[nb] = sb[nb];
   }
@@ -333,7 +349,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
     const float lt = sum_pair32(st.l[nb]);
     const int qi = qw0 + 32 * nb + col;
     if (qi < p.Nq) {
-      const float inv = 1.0f / lt;
+      // a row that admits no key: O = 0, LSE = -inf
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -344,31 +361,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
                           pack2<DT>(a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv)};
           *(u32x2*)(op + qi * p.so.s + d0) = w;
         }
-      if (half == 0) p.lse[(int64_t)bh * p.Nq + qi] = (st.m[nb] + log2_fast(lt)) * kLn2;
+      if (half == 0) p.lse[(int64_t)bh * p.Nq + qi] = lt > 0.f ? (st.m[nb] + log2_fast(lt)) * kLn2 : -__builtin_inff();
     }
   }
 }
 
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool BAND>
 hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   constexpr int kBM = FwdTile<D>::BM;
   const int n_qt = (p.Nq + kBM - 1) / kBM;
   const int64_t blocks = (int64_t)n_qt * p.B * p.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<D, DT, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, int DT>
-hipError_t launch_dc(const FwdParams& p, bool causal, hipStream_t stream) {
-  return causal ? launch_t<D, DT, true>(p, stream) : launch_t<D, DT, false>(p, stream);
+hipError_t launch_dc(const FwdParams& p, bool banded, hipStream_t stream) {
+  return banded ? launch_t<D, DT, true>(p, stream) : launch_t<D, DT, false>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams& p, int d, int dtype, bool causal, hipStream_t stream) {
-  if (d == 64) return dtype == DT_F16 ? launch_dc<64, DT_F16>(p, causal, stream) : launch_dc<64, DT_BF16>(p, causal, stream);
-  return dtype == DT_F16 ? launch_dc<128, DT_F16>(p, causal, stream) : launch_dc<128, DT_BF16>(p, causal, stream);
+hipError_t launch_fwd(const FwdParams& p, int d, int dtype, bool banded, hipStream_t stream) {
+  if (d == 64) return dtype == DT_F16 ? launch_dc<64, DT_F16>(p, banded, stream) : launch_dc<64, DT_BF16>(p, banded, stream);
+  return dtype == DT_F16 ? launch_dc<128, DT_F16>(p, banded, stream) : launch_dc<128, DT_BF16>(p, banded, stream);
 }
 
 }  // namespace fa

@@ -18,6 +18,8 @@ struct FwdParams {
   float* lse;
   Strides sq, sk, sv, so;
   int B, H, Nq, Nk;
+  int G;           // query heads per K/V head (K/V head of query head h is h / G)
+  int wl, wr;      // admitted keys of query i: [i - wl, i + wr]; a negative bound is absent
   float c;         // |scale| * log2(e), clamped away from 0
   uint32_t qflip;  // 0x80008000 when scale < 0 (Q is negated on load), else 0
 };
@@ -36,18 +38,21 @@ struct BwdParams {
   float* lse2;  // workspace: lse_i * log2(e), same layout
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, Nq, Nk;
+  int G;        // query heads per K/V head (as FwdParams)
+  int wl, wr;   // admitted-key band (as FwdParams)
   float scale;  // the softmax scale as given
   float c;      // scale * log2(e) (signed)
 };
 
 // Return hipSuccess or the launch error.  d in {64,128}, dtype 0 = fp16,
-// 1 = bf16; the caller has validated every argument.
-hipError_t launch_fwd(const FwdParams& p, int d, int dtype, bool causal, hipStream_t stream);
-// Backward workspace: the two per-row statistics (D and lse * log2 e), each
-// B*H rows of Nq rounded up to 64 fp32 values.
+// 1 = bf16; the caller has validated every argument.  `banded`: some bound
+// of the admitted-key band is present (causal is the band wr = 0).
+hipError_t launch_fwd(const FwdParams& p, int d, int dtype, bool banded, hipStream_t stream);
+// Backward workspace: the two per-row statistics (-D and lse * log2 e),
+// each B*H rows of Nq rounded up to 64 fp32 values (H = query heads).
 size_t bwd_workspace_bytes(int B, int H, int Nq);
 float* bwd_lse2_region(void* workspace, int B, int H, int Nq);
 // stages: OR of 1 (row statistics), 2 (dK, dV), 4 (dQ), run in that order.
-hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool causal, int stages, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int stages, hipStream_t stream);
 
 }  // namespace fa

@@ -89,6 +89,27 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
                    const int64_t v_strides[3], const int64_t o_strides[3],
                    void* stream);
 
+/* Forward with fewer K/V heads and/or a sliding window (the skill guide's
+ * Workflow 2, step 3: multi-query attention with K/V shared across heads,
+ * and sliding-window attention with window_size = (left, right)).
+ *   H_kv: heads of k and v, dividing H; query head h uses K/V head
+ *     h / (H / H_kv), so consecutive query heads share one (H_kv = H is
+ *     plain multi-head attention, H_kv = 1 multi-query attention).
+ *   window_left, window_right: query i admits keys i - window_left ..
+ *     i + window_right, bounds inclusive; a negative value leaves that
+ *     side unbounded ((-1, -1): no window).  causal = 1 additionally limits
+ *     keys to j <= i.  Positions are top-left aligned as for causal.
+ *   A query row that admits no key (possible with a window when Nq > Nk)
+ *   gets O = 0 and LSE = -inf.
+ *   k, v: [B][H_kv][Nk][d] through their strides; everything else as in
+ *   fa_fwd_strided. */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+              int window_left, int window_right, int dtype,
+              const int64_t q_strides[3], const int64_t k_strides[3],
+              const int64_t v_strides[3], const int64_t o_strides[3],
+              void* stream);
+
 /* Bytes of device workspace fa_bwd needs for these sizes (0 if the sizes are
  * invalid).  Holds two fp32 row statistics per (b, h): -D_i = -sum_d dO_i O_i
  * and lse_i * log2(e), each with its rows padded to a multiple of 64
@@ -136,6 +157,23 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
                   const int64_t do_strides[3], const int64_t dq_strides[3],
                   const int64_t dk_strides[3], const int64_t dv_strides[3],
                   void* workspace, size_t workspace_bytes, int stages, void* stream);
+
+/* Backward of fa_fwd_ex: the stages of fa_bwd_stages with fewer K/V heads
+ * and/or a sliding window, H_kv, window_left, window_right and causal as in
+ * fa_fwd_ex.  dk, dv are [B][H_kv][Nk][d] through their strides; a K/V
+ * head's gradients sum the contributions of all query heads that use it.
+ * The workspace is sized by fa_bwd_workspace_bytes(B, H, Nq, ...) with H
+ * the number of query heads.  lse must be what fa_fwd_ex wrote (-inf for a
+ * row that admits no key; such a row gets dq = 0). */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv,
+              int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+              int window_left, int window_right, int dtype,
+              const int64_t q_strides[3], const int64_t k_strides[3],
+              const int64_t v_strides[3], const int64_t o_strides[3],
+              const int64_t do_strides[3], const int64_t dq_strides[3],
+              const int64_t dk_strides[3], const int64_t dv_strides[3],
+              void* workspace, size_t workspace_bytes, int stages, void* stream);
 
 /* Static name of a status code ("FA_OK", ...); "FA_UNKNOWN_STATUS" otherwise. */
 const char* fa_status_string(int status);

@@ -46,7 +46,7 @@ def test_exported_dynamic_symbols_are_c_names():
 
 
 def test_status_strings_and_version():
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
     assert fa.fa_status_string(0) == "FA_OK"
     assert fa.fa_status_string(1) == "FA_ERR_INVALID_ARG"
     assert fa.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
@@ -182,3 +182,46 @@ def test_valid_call_without_device_reports_device_error():
     """Arguments are valid, so the call reaches the device check, which fails
     here; nothing is launched."""
     assert fwd() == fa.FA_ERR_DEVICE
+
+
+# --- fewer K/V heads and sliding window (fa_fwd_ex / fa_bwd_ex) ---------------
+
+def fwd_ex(H=4, Hkv=2, wl=-1, wr=-1, causal=0, Nq=16, Nk=16):
+    lib = fa.load_library()
+    I3 = ctypes.c_int64 * 3
+    sq = I3(H * Nq * 64, Nq * 64, 64)
+    sk = I3(Hkv * Nk * 64, Nk * 64, 64)
+    return lib.fa_fwd_ex(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), 1, H, Hkv, Nq, Nk, 64, 0.125, causal, wl, wr,
+                         0, sq, sk, sk, sq, None)
+
+
+def bwd_ex(H=4, Hkv=2, wl=-1, wr=-1, causal=0, dk=8 * A, stages=fa.FA_BWD_ALL):
+    lib = fa.load_library()
+    I3 = ctypes.c_int64 * 3
+    sq = I3(H * 16 * 64, 16 * 64, 64)
+    sk = I3(Hkv * 16 * 64, 16 * 64, 64)
+    st = [sq, sk, sk, sq, sq, sq, sk, sk]
+    return lib.fa_bwd_ex(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), P(6 * A), P(7 * A), P(dk), P(9 * A),
+                         1, H, Hkv, 16, 16, 64, 0.125, causal, wl, wr, 0, *st, P(10 * A), 1 << 16, stages, None)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 3), (4, 0), (4, -2), (3, 6)])
+def test_ex_rejects_heads_that_do_not_divide(H, Hkv):
+    assert fwd_ex(H=H, Hkv=Hkv) == fa.FA_ERR_INVALID_ARG
+    assert "H_kv" in fa.fa_last_error_message()
+    assert bwd_ex(H=H, Hkv=Hkv) == fa.FA_ERR_INVALID_ARG
+
+
+def test_ex_validates_kv_tensors_with_kv_heads():
+    # dk overlapping dv is detected with the K/V head count's extent
+    assert bwd_ex(H=4, Hkv=2, dk=9 * A - 64) == fa.FA_ERR_INVALID_ARG
+    assert bwd_ex(stages=0) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful where no HIP device exists")
+@pytest.mark.parametrize("wl,wr,causal", [(-1, -1, 0), (0, 0, 0), (5, -7, 1), (-3, 2, 0), (1 << 30, 1 << 30, 0)])
+def test_ex_accepts_any_window(wl, wr, causal):
+    """Any window value is valid (negative: that side unbounded), so a valid
+    call reaches the device check."""
+    assert fwd_ex(wl=wl, wr=wr, causal=causal) == fa.FA_ERR_DEVICE
+    assert bwd_ex(wl=wl, wr=wr, causal=causal) == fa.FA_ERR_DEVICE
