@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """One-GPU benchmark of the attention hot path (forward + recompute backward).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows-f]
 
 A step is one forward (fa_fwd) and one backward (fa_bwd: D = rowsum(dO*O),
 dK/dV, dQ) over the long-context workload: B=1, H=16, N=16384, d=128, bf16,
@@ -17,7 +17,11 @@ timed alone (K launches each, via fa_bwd_stages) so every kernel has its own
 event-measured average duration; the dominant one is reported as `roofline`
 (and the forward kernel, the long-context target, as `roofline_fwd`).
 
-cpu_baseline: the fp64 numpy oracle (test infrastructure) on one head of the
+rows_f: the same step for the two built extensions on the same inputs: 16
+query heads on 2 K/V heads (causal), and a causal sliding window of 256 keys
+(the skill guide's window example); FLOPs count admitted (query, key) pairs.
+
+cpu_baseline: the fp64 numpy oracle (test infrastructure) on four heads of the
 same workload, forward + backward, timed on the host cores.
 """
 import argparse
@@ -110,12 +114,73 @@ def cpu_baseline(inp, s, causal, gpu_out):
     }
 
 
+GQA_KV_HEADS = 2          # 16 query heads on 2 K/V heads (G = 8)
+WINDOW = (256, 256)       # the skill guide's sliding-window example, with causal
+
+
+def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
+    """Forward + backward of the two built 'next' rows on the same 16K inputs:
+    fewer K/V heads (the first GQA_KV_HEADS heads of k, v shared by all 16
+    query heads, causal) and a causal sliding window WINDOW.  FLOPs count the
+    admitted (query, key) pairs; the backward is 2.5x the forward."""
+    B, H, N, d = q.shape
+    res = {}
+    kg, vg = k[:, :GQA_KV_HEADS].contiguous(), v[:, :GQA_KV_HEADS].contiguous()
+    pairs_causal = N * (N + 1) / 2
+    lft = WINDOW[0]
+    pairs_win = sum(min(i, lft) + 1 for i in range(N))
+    cases = {
+        "gqa": dict(k=kg, v=vg, window=(-1, -1), pairs=pairs_causal,
+                    desc="B1 H16 H_kv%d N16384 d128 bf16 causal" % GQA_KV_HEADS),
+        "sliding_window": dict(k=k, v=v, window=WINDOW, pairs=pairs_win,
+                               desc="B1 H16 N16384 d128 bf16 causal, window %r" % (WINDOW,)),
+    }
+    for name, c in cases.items():
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(c["k"]), torch.empty_like(c["v"])
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_BF16), dtype=torch.uint8, device=q.device)
+
+        def fwd():
+            fa.fa_fwd_ex(q, c["k"], c["v"], o, lse, s, True, c["window"], "bhsd", stream)
+
+        def bwd():
+            fa.fa_bwd_ex(q, c["k"], c["v"], o, lse, do, dq, dk, dv, s, True, ws, c["window"], fa.FA_BWD_ALL,
+                         "bhsd", stream)
+
+        for _ in range(2):
+            fwd()
+            bwd()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        tf = tb = 0.0
+        for _ in range(steps):
+            ev[0].record(stream)
+            fwd()
+            ev[1].record(stream)
+            bwd()
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            tf += ev[0].elapsed_time(ev[1])
+            tb += ev[1].elapsed_time(ev[2])
+        tf, tb = tf / steps, tb / steps
+        ff = 4.0 * B * H * d * c["pairs"]
+        res[name] = {"workload": c["desc"], "fwd_ms": tf, "bwd_ms": tb,
+                     "fwd_tflops": ff / tf / 1e9, "bwd_tflops": 2.5 * ff / tb / 1e9,
+                     "step_tflops": 3.5 * ff / (tf + tb) / 1e9, "fwd_frac_of_peak": ff / tf / 1e9 / peak}
+        log("%s: fwd %.3f ms (%.1f TFLOP/s), bwd %.3f ms (%.1f TFLOP/s)" % (
+            name, tf, ff / tf / 1e9, tb, 2.5 * ff / tb / 1e9))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows-f", action="store_true",
+                    help="skip the GQA / sliding-window measurements (profiles of the main step use this, "
+                         "since those runs launch the same kernel instantiations)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 times), so a counter "
                          "profile of this command can calibrate FETCH_SIZE/WRITE_SIZE against known bytes")
@@ -247,6 +312,8 @@ def main():
         "roofline": roof(dominant),
         "roofline_fwd": roof("fwd"),
     }
+    if not args.no_rows_f:
+        out["rows_f"] = next_rows(fa, torch, q, k, v, do, s, stream, peak, min(K, 10))
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         gpu_out = (o.cpu(), lse.cpu(), dq.cpu(), dk.cpu(), dv.cpu())
