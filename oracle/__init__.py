@@ -7,18 +7,25 @@ or helper with the HIP library; the only thing both sides see is the seeded
 input generator in ``attn_inputs`` (random numbers and dtype casts, none of
 the method's arithmetic).
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` to closed
-forms, invariants, brute force and finite differences (see each docstring);
-none is "parity unpinned".
+Every function here is pinned by ``tests/test_oracle_pins*.py`` to closed
+forms, invariants, library special cases, published known-answer vectors,
+brute force and finite differences (see each docstring); none is "parity
+unpinned".
 """
 from .attention import (
     attention_fwd64,
     attention_rows_fwd64,
     attention_bwd64,
+    philox4x32_10,
+    dropout_threshold,
+    dropout_keep,
 )
 
 __all__ = [
     "attention_fwd64",
     "attention_rows_fwd64",
     "attention_bwd64",
+    "philox4x32_10",
+    "dropout_threshold",
+    "dropout_keep",
 ]

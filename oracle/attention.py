@@ -46,6 +46,21 @@ What is computed, and where the pages define it:
   top-left aligned as for causal.  A row that sees no key at all has
   output 0 and log-sum-exp -inf (and contributes no gradient).
 
+* Dropout.  The skill guide's Workflow 2, step 2 passes ``dropout_p=0.1``
+  to ``flash_attn_func`` but defines no random numbers.  Reading taken:
+  dropout acts on the attention weights after the softmax, as in
+  FlashAttention: ``O = (P * keep * s_keep) V`` with the log-sum-exp of the
+  undropped scores, ``s_keep`` restoring the expectation.  Both sides draw
+  from one counter-based generator, Philox4x32-10 (Salmon, Moraes, Dror and
+  Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11), implemented
+  here from that definition: element (b, h, i, j) (h a query head) uses the
+  counter ``(2*(j >> 5) + ((j >> 2) & 1), i, b*H + h, offset)`` and the key
+  ``(seed mod 2^32, seed >> 32)``; its byte is byte ``j & 3`` of output word
+  ``(j >> 3) & 3``; the element is kept iff byte >= thr with
+  ``thr = min(255, rint(256 p))`` (p quantised to 1/256), and
+  ``s_keep = 256 / (256 - thr)``.  (The counter layout lets one generator
+  call serve the 16 keys of a 32-key tile that one GPU lane owns.)
+
 Layout of every array: ``[batch, heads, seq, dim]`` (``[B, H, N, d]``), float64.
 """
 import numpy as np
@@ -54,7 +69,58 @@ __all__ = [
     "attention_fwd64",
     "attention_rows_fwd64",
     "attention_bwd64",
+    "philox4x32_10",
+    "dropout_threshold",
+    "dropout_keep",
 ]
+
+_M0, _M1, _W0, _W1 = 0xD2511F53, 0xCD9E8D57, 0x9E3779B9, 0xBB67AE85
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 on arrays: ``ctr`` uint32 [..., 4], ``key`` uint32
+    [..., 2] (broadcast).  Ten rounds; each multiplies words 0 and 2 by the
+    two round constants into 64-bit products, and the new words are
+    (hi(M1*x2) ^ x1 ^ k0, lo(M1*x2), hi(M0*x0) ^ x3 ^ k1, lo(M0*x0)); the key
+    is bumped by the two Weyl constants before every round but the first."""
+    c = np.asarray(ctr, dtype=np.uint64)
+    k = np.asarray(key, dtype=np.uint64)
+    x0, x1, x2, x3 = c[..., 0], c[..., 1], c[..., 2], c[..., 3]
+    k0, k1 = k[..., 0], k[..., 1]
+    m32 = np.uint64(0xFFFFFFFF)
+    for r in range(10):
+        if r > 0:
+            k0 = (k0 + np.uint64(_W0)) & m32
+            k1 = (k1 + np.uint64(_W1)) & m32
+        p0 = np.uint64(_M0) * x0
+        p1 = np.uint64(_M1) * x2
+        x0, x1, x2, x3 = (p1 >> np.uint64(32)) ^ x1 ^ k0, p1 & m32, (p0 >> np.uint64(32)) ^ x3 ^ k1, p0 & m32
+    return np.stack([x0, x1, x2, x3], axis=-1).astype(np.uint32)
+
+
+def dropout_threshold(p):
+    """(thr, s_keep) for dropout probability p in [0, 1) (see the module
+    docstring); p is taken as the float32 the kernels receive."""
+    p = float(np.float32(p))
+    if not 0.0 <= p < 1.0:
+        raise ValueError("dropout probability must be in [0, 1)")
+    thr = min(255, int(np.rint(p * 256.0)))
+    return thr, 256.0 / (256 - thr)
+
+
+def dropout_keep(b, h, H, rows, nk, p, seed, offset):
+    """Boolean keep mask [len(rows), nk] of query rows ``rows`` of (b, h)."""
+    thr, _ = dropout_threshold(p)
+    i = np.asarray(rows, dtype=np.uint64)[:, None]
+    j = np.arange(nk, dtype=np.uint64)[None, :]
+    ctr = np.stack(np.broadcast_arrays((j >> np.uint64(5)) * np.uint64(2) + ((j >> np.uint64(2)) & np.uint64(1)),
+                                       i, np.uint64(b * H + h), np.uint64(offset)), axis=-1)
+    seed = int(seed)
+    w = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))
+    word = np.take_along_axis(w, ((j >> np.uint64(3)) & np.uint64(3)).astype(np.int64)[..., None]
+                              .repeat(len(rows), axis=0), axis=-1)[..., 0]
+    byte = (word >> ((j & np.uint64(3)) * np.uint64(8)).astype(np.uint32)) & np.uint32(0xFF)
+    return byte >= thr
 
 
 def _as64(x):
@@ -104,6 +170,15 @@ def _softmax_rows(s):
     return p, lse
 
 
+def _dropped(x, b, h, H, rows, dropout):
+    """x * keep * s_keep for the rows of (b, h), or x without dropout."""
+    if dropout is None:
+        return x
+    p, seed, offset = dropout
+    _, s_keep = dropout_threshold(p)
+    return np.where(dropout_keep(b, h, H, rows, x.shape[1], p, seed, offset), x * s_keep, 0.0)
+
+
 def _kv_group(H, Hkv):
     if Hkv < 1 or H % Hkv:
         raise ValueError("K/V heads (%d) must divide query heads (%d)" % (Hkv, H))
@@ -117,7 +192,7 @@ def _check(q, k, v):
     return B, H, Nq, d, _kv_group(H, k.shape[1])
 
 
-def attention_fwd64(q, k, v, scale, causal, window=(-1, -1)):
+def attention_fwd64(q, k, v, scale, causal, window=(-1, -1), dropout=None):
     """O = softmax(scale * Q K^T [mask]) V and its log-sum-exp.
 
     q: [B, H, Nq, d]; k, v: [B, H_kv, Nk, d] with H_kv dividing H (any float
@@ -134,11 +209,11 @@ def attention_fwd64(q, k, v, scale, causal, window=(-1, -1)):
         for h in range(H):
             s = _scores(q[b, h], k[b, h // G], scale, causal, rows, window)
             p, lse[b, h] = _softmax_rows(s)
-            o[b, h] = p @ v[b, h // G]
+            o[b, h] = _dropped(p, b, h, H, rows, dropout) @ v[b, h // G]
     return o, lse
 
 
-def attention_rows_fwd64(q, k, v, scale, causal, rows, window=(-1, -1)):
+def attention_rows_fwd64(q, k, v, scale, causal, rows, window=(-1, -1), dropout=None):
     """The forward restricted to selected query rows (each against all keys).
 
     rows: int array [B, H, R] of query indices.  Returns
@@ -158,16 +233,18 @@ def attention_rows_fwd64(q, k, v, scale, causal, rows, window=(-1, -1)):
             r = rows[b, h]
             s = _scores(q[b, h][r], k[b, h // G], float(scale), causal, r, window)
             p, lse[b, h] = _softmax_rows(s)
-            o[b, h] = p @ v[b, h // G]
+            o[b, h] = _dropped(p, b, h, H, r, dropout) @ v[b, h // G]
     return o, lse
 
 
-def attention_bwd64(q, k, v, do, scale, causal, window=(-1, -1)):
+def attention_bwd64(q, k, v, do, scale, causal, window=(-1, -1), dropout=None):
     """Gradients of L = sum(O * dO) with respect to Q, K and V.
 
     Recomputes P from Q and K (its own P: nothing produced by a fast kernel
     is used), then applies the chain rule listed in the module docstring;
     a K/V head accumulates the gradients of every query head that uses it.
+    With dropout the weights W = P * keep * s_keep replace P in O = W V, so
+    dV = W^T dO and dS = P * (keep * s_keep * dP - rowsum(W * dP)).
     Returns (dq, dk, dv) with the shapes of q, k, v, in float64.
     """
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
@@ -183,9 +260,10 @@ def attention_bwd64(q, k, v, do, scale, causal, window=(-1, -1)):
         for h in range(H):
             qq, kk, vv, g = q[b, h], k[b, h // G], v[b, h // G], do[b, h]
             p, _ = _softmax_rows(_scores(qq, kk, scale, causal, rows, window))
-            dv[b, h // G] += p.T @ g
+            wgt = _dropped(p, b, h, H, rows, dropout)
+            dv[b, h // G] += wgt.T @ g
             dp = g @ vv.T
-            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            ds = p * (_dropped(dp, b, h, H, rows, dropout) - np.sum(wgt * dp, axis=1, keepdims=True))
             dq[b, h] = scale * (ds @ kk)
             dk[b, h // G] += scale * (ds.T @ qq)
     return dq, dk, dv
