@@ -17,9 +17,10 @@ timed alone (K launches each, via fa_bwd_stages) so every kernel has its own
 event-measured average duration; the dominant one is reported as `roofline`
 (and the forward kernel, the long-context target, as `roofline_fwd`).
 
-rows_f: the same step for the two built extensions on the same inputs: 16
-query heads on 2 K/V heads (causal), and a causal sliding window of 256 keys
-(the skill guide's window example); FLOPs count admitted (query, key) pairs.
+rows_f: the same step for the built extensions on the same inputs: 16 query
+heads on 2 K/V heads (causal), a causal sliding window of 256 keys (the skill
+guide's window example), and causal dropout with p = 0.1 (the skill guide's
+dropout_p); FLOPs count admitted (query, key) pairs.
 
 cpu_baseline: the fp64 numpy oracle (test infrastructure) on four heads of the
 same workload, forward + backward, timed on the host cores.
@@ -116,13 +117,15 @@ def cpu_baseline(inp, s, causal, gpu_out):
 
 GQA_KV_HEADS = 2          # 16 query heads on 2 K/V heads (G = 8)
 WINDOW = (256, 256)       # the skill guide's sliding-window example, with causal
+DROPOUT = (0.1, 2024, 0)  # the skill guide's dropout_p = 0.1 (seed, offset arbitrary)
 
 
 def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
-    """Forward + backward of the two built 'next' rows on the same 16K inputs:
+    """Forward + backward of the built 'next' rows on the same 16K inputs:
     fewer K/V heads (the first GQA_KV_HEADS heads of k, v shared by all 16
-    query heads, causal) and a causal sliding window WINDOW.  FLOPs count the
-    admitted (query, key) pairs; the backward is 2.5x the forward."""
+    query heads, causal), a causal sliding window WINDOW, and causal dropout
+    DROPOUT.  FLOPs count the admitted (query, key) pairs; the backward is
+    2.5x the forward."""
     B, H, N, d = q.shape
     res = {}
     kg, vg = k[:, :GQA_KV_HEADS].contiguous(), v[:, :GQA_KV_HEADS].contiguous()
@@ -130,10 +133,12 @@ def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
     lft = WINDOW[0]
     pairs_win = sum(min(i, lft) + 1 for i in range(N))
     cases = {
-        "gqa": dict(k=kg, v=vg, window=(-1, -1), pairs=pairs_causal,
+        "gqa": dict(k=kg, v=vg, window=(-1, -1), pairs=pairs_causal, dropout=None,
                     desc="B1 H16 H_kv%d N16384 d128 bf16 causal" % GQA_KV_HEADS),
-        "sliding_window": dict(k=k, v=v, window=WINDOW, pairs=pairs_win,
+        "sliding_window": dict(k=k, v=v, window=WINDOW, pairs=pairs_win, dropout=None,
                                desc="B1 H16 N16384 d128 bf16 causal, window %r" % (WINDOW,)),
+        "dropout": dict(k=k, v=v, window=(-1, -1), pairs=pairs_causal, dropout=DROPOUT,
+                        desc="B1 H16 N16384 d128 bf16 causal, dropout_p %g" % DROPOUT[0]),
     }
     for name, c in cases.items():
         o = torch.empty_like(q)
@@ -142,11 +147,11 @@ def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
         ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_BF16), dtype=torch.uint8, device=q.device)
 
         def fwd():
-            fa.fa_fwd_ex(q, c["k"], c["v"], o, lse, s, True, c["window"], "bhsd", stream)
+            fa.fa_fwd_ex(q, c["k"], c["v"], o, lse, s, True, c["window"], "bhsd", stream, c["dropout"])
 
         def bwd():
             fa.fa_bwd_ex(q, c["k"], c["v"], o, lse, do, dq, dk, dv, s, True, ws, c["window"], fa.FA_BWD_ALL,
-                         "bhsd", stream)
+                         "bhsd", stream, c["dropout"])
 
         for _ in range(2):
             fwd()

@@ -42,6 +42,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_u64, _u32 = ctypes.c_uint64, ctypes.c_uint32
 _I64x3 = ctypes.c_int64 * 3
 
 
@@ -79,9 +80,10 @@ def load_library():
     lib.fa_bwd_strided.restype = _i
     lib.fa_bwd_stages.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i] + [_I64x3] * 8 + [_vp, _sz, _i, _vp]
     lib.fa_bwd_stages.restype = _i
-    lib.fa_fwd_ex.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _i, _i, _i] + [_I64x3] * 4 + [_vp]
+    lib.fa_fwd_ex.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _i, _i, _f, _u64, _u32, _i] + [_I64x3] * 4 + [_vp]
     lib.fa_fwd_ex.restype = _i
-    lib.fa_bwd_ex.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _i, _i, _i, _i] + [_I64x3] * 8 + [_vp, _sz, _i, _vp]
+    lib.fa_bwd_ex.argtypes = ([_vp] * 9 + [_i] * 6 + [_f, _i, _i, _i, _f, _u64, _u32, _i] + [_I64x3] * 8 +
+                              [_vp, _sz, _i, _vp])
     lib.fa_bwd_ex.restype = _i
     lib.fa_status_string.argtypes = [_i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -242,45 +244,55 @@ def _window(window):
     return int(left), int(right)
 
 
-def fa_fwd_ex(q, k, v, o, lse, scale, causal, window=(-1, -1), layout="bhsd", stream=None):
+def _dropout(dropout):
+    p, seed, offset = (0.0, 0, 0) if dropout is None else dropout
+    return float(p), int(seed), int(offset)
+
+
+def fa_fwd_ex(q, k, v, o, lse, scale, causal, window=(-1, -1), layout="bhsd", stream=None, dropout=None):
     """C ``fa_fwd_ex``: k, v may have fewer heads than q (it must divide q's);
-    ``window`` = (left, right), a negative side unbounded."""
+    ``window`` = (left, right), a negative side unbounded; ``dropout`` =
+    (p, seed, offset) or None."""
     dt = _dtype_code(q)
     _on_device(q, k, v, o, lse)
     B, H, Nq, d = _dims(q, layout)
     Hkv, Nk = _dims(k, layout)[1:3]
     wl, wr = _window(window)
+    dp, seed, off = _dropout(dropout)
     with torch.cuda.device(q.device):
         _check(load_library().fa_fwd_ex(
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
-            wl, wr, dt, _strides(q, layout), _strides(k, layout), _strides(v, layout), _strides(o, layout),
-            _stream(q, stream)))
+            wl, wr, dp, seed, off, dt, _strides(q, layout), _strides(k, layout), _strides(v, layout),
+            _strides(o, layout), _stream(q, stream)))
 
 
 def fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, window=(-1, -1), stages=FA_BWD_ALL,
-              layout="bhsd", stream=None):
-    """C ``fa_bwd_ex``: the backward of ``fa_fwd_ex`` (dk, dv shaped like k, v)."""
+              layout="bhsd", stream=None, dropout=None):
+    """C ``fa_bwd_ex``: the backward of ``fa_fwd_ex`` (dk, dv shaped like k,
+    v; the same ``window`` and ``dropout``)."""
     dt = _dtype_code(q)
     _on_device(q, k, v, o, lse, do, dq, dk, dv, workspace)
     B, H, Nq, d = _dims(q, layout)
     Hkv, Nk = _dims(k, layout)[1:3]
     wl, wr = _window(window)
+    dp, seed, off = _dropout(dropout)
     nbytes = workspace.numel() * workspace.element_size()
     st = [_strides(t, layout) for t in (q, k, v, o, do, dq, dk, dv)]
     with torch.cuda.device(q.device):
         _check(load_library().fa_bwd_ex(
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-            B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), wl, wr, dt, *st, _ptr(workspace), nbytes,
-            int(stages), _stream(q, stream)))
+            B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), wl, wr, dp, seed, off, dt, *st,
+            _ptr(workspace), nbytes, int(stages), _stream(q, stream)))
 
 
-def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None, window=None):
+def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None, window=None, dropout=None):
     """O = softmax(scale Q K^T) V (top-left causal mask if ``causal``).
 
     Allocates o (like q) and lse (fp32 [B,H,Nq]); returns (o, lse).  ``scale``
     defaults to 1/sqrt(d).  k and v may carry fewer heads than q (dividing
     them); ``window`` = (left, right) restricts query i to keys
-    i - left .. i + right (negative: unbounded).
+    i - left .. i + right (negative: unbounded); ``dropout`` = (p, seed,
+    offset) drops attention weights (see ``include/fa.h``).
     """
     _dtype_code(q)
     _on_device(q, k, v)
@@ -288,8 +300,8 @@ def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None,
     s = _default_scale(d, scale)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if _dims(k, layout)[1] != H or window is not None:
-        fa_fwd_ex(q, k, v, o, lse, s, causal, window, layout, stream)
+    if _dims(k, layout)[1] != H or window is not None or dropout is not None:
+        fa_fwd_ex(q, k, v, o, lse, s, causal, window, layout, stream, dropout)
     elif layout == "bhsd" and q.is_contiguous() and k.is_contiguous() and v.is_contiguous():
         fa_fwd(q, k, v, o, lse, s, causal, stream)
     else:
@@ -297,9 +309,10 @@ def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None,
     return o, lse
 
 
-def attention_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bhsd", stream=None, window=None):
+def attention_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bhsd", stream=None, window=None,
+                  dropout=None):
     """Gradients (dq, dk, dv) of sum(O * dO), recomputing P from ``lse``
-    (fewer K/V heads and ``window`` as in ``attention_fwd``)."""
+    (fewer K/V heads, ``window`` and ``dropout`` as in ``attention_fwd``)."""
     _on_device(q, k, v, o, lse, do)
     B, H, Nq, d = _dims(q, layout)
     Hkv, Nk = _dims(k, layout)[1:3]
@@ -308,8 +321,8 @@ def attention_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bhsd", 
     nbytes = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, _dtype_code(q))
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     contiguous = all(t.is_contiguous() for t in (q, k, v, o, do))
-    if Hkv != H or window is not None:
-        fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, window, FA_BWD_ALL, layout, stream)
+    if Hkv != H or window is not None or dropout is not None:
+        fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, window, FA_BWD_ALL, layout, stream, dropout)
     elif layout == "bhsd" and contiguous:
         fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, stream)
     else:

@@ -124,6 +124,19 @@ Band make_band(int causal, int window_left, int window_right, int Nq, int Nk) {
   return b;
 }
 
+// Dropout probability p in [0, 1) -> keep iff random byte >= thr, with
+// thr = min(255, rint(256 p)) and kept weights scaled by 256 / (256 - thr).
+int make_dropout(float p, uint64_t seed, uint32_t offset, fa::DropoutParams* out) {
+  if (!(p >= 0.0f && p < 1.0f)) return fail(FA_ERR_INVALID_ARG, "dropout_p = %g is not in [0, 1)", (double)p);
+  const double t = std::nearbyint((double)p * 256.0);
+  out->thr = t > 255.0 ? 255u : (uint32_t)t;
+  out->scale = (float)(256.0 / (256.0 - (double)out->thr));
+  out->seed_lo = (uint32_t)seed;
+  out->seed_hi = (uint32_t)(seed >> 32);
+  out->offset = offset;
+  return FA_OK;
+}
+
 float softmax_c(float scale) {
   // |scale| * log2(e); a tiny floor keeps c > 0 so masked (-inf) scores stay
   // -inf after scaling.  For |scale| below it the weights are uniform to
@@ -158,13 +171,16 @@ const char* fa_status_string(int status) {
 const char* fa_last_error_message(void) { return g_msg; }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int Nq,
-              int Nk, int d, float scale, int causal, int window_left, int window_right, int dtype,
+              int Nk, int d, float scale, int causal, int window_left, int window_right, float dropout_p,
+              uint64_t seed, uint32_t offset, int dtype,
               const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
               const int64_t o_strides[3], void* stream) {
   g_msg[0] = '\0';
   int st = check_common(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st) return st;
   if ((st = check_heads(B, H, H_kv))) return st;
+  fa::DropoutParams drop;
+  if ((st = make_dropout(dropout_p, seed, offset, &drop))) return st;
   if (!q_strides || !k_strides || !v_strides || !o_strides) return fail(FA_ERR_INVALID_ARG, "a strides array is NULL");
   if (B == 0 || H == 0 || Nq == 0) return FA_OK;
   Extent eq, ek, ev, eo;
@@ -199,6 +215,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
   const Band band = make_band(causal, window_left, window_right, Nq, Nk);
   p.wl = band.wl;
   p.wr = band.wr;
+  p.drop = drop;
   p.c = softmax_c(scale);
   p.qflip = std::signbit(scale) ? 0x80008000u : 0u;
   hipError_t e = fa::launch_fwd(p, d, dtype, band.present(), static_cast<hipStream_t>(stream));
@@ -210,8 +227,8 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
                    int d, float scale, int causal, int dtype, const int64_t q_strides[3],
                    const int64_t k_strides[3], const int64_t v_strides[3], const int64_t o_strides[3],
                    void* stream) {
-  return fa_fwd_ex(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, -1, -1, dtype, q_strides, k_strides, v_strides,
-                   o_strides, stream);
+  return fa_fwd_ex(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, -1, -1, 0.0f, 0, 0, dtype, q_strides, k_strides,
+                   v_strides, o_strides, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
@@ -229,7 +246,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
 
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
               void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
-              int window_left, int window_right, int dtype, const int64_t q_strides[3], const int64_t k_strides[3],
+              int window_left, int window_right, float dropout_p, uint64_t seed, uint32_t offset, int dtype,
+              const int64_t q_strides[3], const int64_t k_strides[3],
               const int64_t v_strides[3], const int64_t o_strides[3], const int64_t do_strides[3],
               const int64_t dq_strides[3], const int64_t dk_strides[3], const int64_t dv_strides[3],
               void* workspace, size_t workspace_bytes, int stages, void* stream) {
@@ -237,6 +255,8 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   int st = check_common(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st) return st;
   if ((st = check_heads(B, H, H_kv))) return st;
+  fa::DropoutParams drop;
+  if ((st = make_dropout(dropout_p, seed, offset, &drop))) return st;
   if (stages <= 0 || (stages & ~FA_BWD_ALL)) return fail(FA_ERR_INVALID_ARG, "stages = %d is not a nonzero OR of FA_BWD_*", stages);
   if (!q_strides || !k_strides || !v_strides || !o_strides || !do_strides || !dq_strides || !dk_strides || !dv_strides)
     return fail(FA_ERR_INVALID_ARG, "a strides array is NULL");
@@ -300,6 +320,7 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   const Band band = make_band(causal, window_left, window_right, Nq, Nk);
   p.wl = band.wl;
   p.wr = band.wr;
+  p.drop = drop;
   p.scale = scale;
   p.c = scale * 1.4426950408889634f;
   hipError_t e = fa::launch_bwd(p, d, dtype, band.present(), stages, static_cast<hipStream_t>(stream));
@@ -313,7 +334,8 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
                   const int64_t o_strides[3], const int64_t do_strides[3], const int64_t dq_strides[3],
                   const int64_t dk_strides[3], const int64_t dv_strides[3], void* workspace,
                   size_t workspace_bytes, int stages, void* stream) {
-  return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, Nq, Nk, d, scale, causal, -1, -1, dtype, q_strides,
+  return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, Nq, Nk, d, scale, causal, -1, -1, 0.0f, 0, 0, dtype,
+                   q_strides,
                    k_strides, v_strides, o_strides, do_strides, dq_strides, dk_strides, dv_strides, workspace,
                    workspace_bytes, stages, stream);
 }

@@ -192,7 +192,7 @@ __device__ __forceinline__ void wait_ring(int later) {
 //   phase 2: A  dV += .. P(t); S(t+1)               B  dS(t) = P(t) (dP(t) - D)
 // Query tiles (Q, dO and the two row statistics) stream HBM -> LDS through
 // a 4-slot ring; tile t+3 is requested in phase 2 of step t.
-template <int D, int DT, bool BAND>
+template <int D, int DT, bool BAND, bool DROP>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(BwdParams p) {
   constexpr int KW = 32;            // keys per pair
   constexpr int NPAIR = kWaves;     // pairs per workgroup
@@ -213,6 +213,8 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     float l[NB][kT];         // lse * log2(e)
     float d[NB][kT];         // -D
     f32x4 x[2][NPAIR][4][64];  // fp32 P hand-over, double buffered: [step & 1][pair][register group][lane]
+    // dropout keep bytes of a pair's 32 keys x 32 queries, [step & 1][pair][key][query]
+    uint8_t mk[DROP ? 2 : 1][NPAIR][KW * kT];
   };
   __shared__ __attribute__((aligned(1024))) Smem sm;
 
@@ -314,7 +316,8 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 
     // One step.  (Unrolling by the ring depth would turn the slot bases
     // into immediates, but makes this compiler spill role A's registers.)
-    int it = qlo;  // query tile of the current step
+    int it = qlo;            // query tile of the current step
+    int hcur = hk * p.G;     // its query head
     auto step = [&](int u) {
       const int SL = u & (NB - 1);
       const int XB = SL & 1;
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 
       // ---------------- phase 1
       if constexpr (A) {
-        auto phase = [&](const float* __restrict__ Lt, f32x4* __restrict__ X) {
+        auto phase = [&](const float* __restrict__ Lt, f32x4* __restrict__ X, uint8_t* Mk) {
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const float4 lv = *(const float4*)(&Lt[8 * g4 + 4 * half]);
@@ -344,28 +347,51 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
               if ((p.wr >= 0 && kd - p.wr > ro) || (p.wl >= 0 && kd + p.wl < ro)) sd[r] = 0.f;
             }
           }
-          pk[0] = pack_acc8<DT>(sd, 0);
-          pk[1] = pack_acc8<DT>(sd, 1);
           // P in fp32 to the partner (exact dS, no unpacking there)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4)
             X[64 * g4 + lane] = f32x4{sd[4 * g4], sd[4 * g4 + 1], sd[4 * g4 + 2], sd[4 * g4 + 3]};
+          if constexpr (DROP) {
+            // The forward's draw for query i0 + col and the 16 keys of the
+            // pair with key bit 2 = half (one call per lane), turned to a
+            // key-major byte matrix in LDS; then this lane (key col) reads
+            // the bytes of its 16 queries back, four per word.
+            const u32x4 rnd = philox4x32_10(2u * (uint32_t)(kw0 >> 5) + (uint32_t)half, (uint32_t)(i0 + col),
+                                            (uint32_t)(b * p.H + hcur), p.drop.offset, p.drop.seed_lo,
+                                            p.drop.seed_hi);
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+              for (int bb = 0; bb < 4; ++bb) Mk[(8 * a + 4 * half + bb) * kT + col] = (uint8_t)(rnd[a] >> (8 * bb));
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const uint32_t kw = *(const uint32_t*)&Mk[col * kT + 8 * g4 + 4 * half];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (((kw >> (8 * e)) & 0xffu) < p.drop.thr) sd[4 * g4 + e] = 0.f;
+            }
+          }
+          pk[0] = pack_acc8<DT>(sd, 0);  // P (kept P with dropout) for dV
+          pk[1] = pack_acc8<DT>(sd, 1);
         };
-        phase(sm.l[SL], &sm.x[XB][pair][0][0]);
+        phase(sm.l[SL], &sm.x[XB][pair][0][0], &sm.mk[DROP ? XB : 0][pair][0]);
       } else {
         auto phase = [&](const uint16_t* __restrict__ Ot, const float* __restrict__ Dt,
                          const uint16_t* __restrict__ Qprev) {
           // dK^T += Q^T dS of the previous tile
           tile_t_times<D, DT>(acc, Qprev, pk, ta);
           // dP - D in one pass: the accumulator starts at -D of its row
-          f32x16 dinit;
+          // (with dropout at 0: -D is added after the mask)
+          f32x16 dinit = f32x16{};
+          if constexpr (!DROP) {
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const float4 dv = *(const float4*)(&Dt[8 * g4 + 4 * half]);
-            dinit[4 * g4 + 0] = dv.x;
-            dinit[4 * g4 + 1] = dv.y;
-            dinit[4 * g4 + 2] = dv.z;
-            dinit[4 * g4 + 3] = dv.w;
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const float4 dv = *(const float4*)(&Dt[8 * g4 + 4 * half]);
+              dinit[4 * g4 + 0] = dv.x;
+              dinit[4 * g4 + 1] = dv.y;
+              dinit[4 * g4 + 2] = dv.z;
+              dinit[4 * g4 + 3] = dv.w;
+            }
           }
           sd = rows_times_regs<D, DT>(Ot, kv, ta, dinit);
           // issue order: operand reads kLA MFMAs ahead of their use
@@ -394,19 +420,33 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         };
         phase(sm.o[SL], sm.q[(SL + 1) & (NB - 1)]);
       } else {
-        auto phase = [&](const f32x4* __restrict__ X) {
+        auto phase = [&](const f32x4* __restrict__ X, const uint8_t* __restrict__ Mk, const float* __restrict__ Dt) {
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const f32x4 pv = X[64 * g4 + lane];
+            if constexpr (DROP) {  // dS = P (keep * scale * dP - D)
+              const uint32_t kw = *(const uint32_t*)&Mk[col * kT + 8 * g4 + 4 * half];
+              const float4 nd = *(const float4*)(&Dt[8 * g4 + 4 * half]);
+              const float ndv[4] = {nd.x, nd.y, nd.z, nd.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sd[4 * g4 + e] *= pv[e];
+              for (int e = 0; e < 4; ++e) {
+                const float m = ((kw >> (8 * e)) & 0xffu) >= p.drop.thr ? p.drop.scale : 0.f;
+                sd[4 * g4 + e] = pv[e] * __builtin_fmaf(m, sd[4 * g4 + e], ndv[e]);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sd[4 * g4 + e] *= pv[e];
+            }
           }
           pk[0] = pack_acc8<DT>(sd, 0);
           pk[1] = pack_acc8<DT>(sd, 1);
         };
-        phase(&sm.x[XB][pair][0][0]);
+        phase(&sm.x[XB][pair][0][0], &sm.mk[DROP ? XB : 0][pair][0], sm.d[SL]);
       }
-      if (++it == qhi) it = qlo;
+      if (++it == qhi) {
+        it = qlo;
+        ++hcur;
+      }
     };
     for (int u = 0; u < U; ++u) step(u);
     if constexpr (!A) {
@@ -416,7 +456,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 
     if (key < p.Nk) {
       if constexpr (A) {
-        store_rows<DT, DB>(p.dv + b * p.sdv.b + hk * p.sdv.h + key * p.sdv.s, acc, 1.0f, half);
+        store_rows<DT, DB>(p.dv + b * p.sdv.b + hk * p.sdv.h + key * p.sdv.s, acc, DROP ? p.drop.scale : 1.0f, half);
       } else {
         store_rows<DT, DB>(p.dk + b * p.sdk.b + hk * p.sdk.h + key * p.sdk.s, acc, p.scale, half);
       }
@@ -430,7 +470,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 }
 
 // ------------------------------------------------------------ dQ
-template <int D, int DT, bool BAND>
+template <int D, int DT, bool BAND, bool DROP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(BwdParams p) {
   constexpr int QW = 32;
   constexpr int BM = kWaves * QW;
@@ -503,7 +543,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float ndsv = qi < p.Nq ? p.dsum[(int64_t)bh * sst + qi] : 0.f;  // -D
   f32x16 dinit;  // every dP^T accumulator starts at -D of this lane's query
 #pragma unroll
-  for (int r = 0; r < 16; ++r) dinit[r] = ndsv;
+  for (int r = 0; r < 16; ++r) dinit[r] = DROP ? 0.f : ndsv;  // with dropout -D is added after the mask
 
   f32x16 adq[DB];
 #pragma unroll
@@ -529,7 +569,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto body = [&](const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ Vt) {  // as in dkdv_kernel
       // S^T = K Q^T and dP^T = V dO^T: rows are keys j0 + acc_row(half, r); column = this lane's query
       f32x16 s = rows_times_regs<D, DT>(Kt, qf, ta);
-      f32x16 dp = rows_times_regs<D, DT>(Vt, of, ta, dinit);  // dP^T - D
+      f32x16 dp = rows_times_regs<D, DT>(Vt, of, ta, dinit);  // dP^T - D (dP^T with dropout)
+      u32x4 rnd = u32x4{0, 0, 0, 0};
+      if constexpr (DROP)  // the forward's draw for this query and the lane's 16 keys of tile j
+        rnd = philox4x32_10(2u * (uint32_t)j + (uint32_t)half, (uint32_t)qi, (uint32_t)bh, p.drop.offset,
+                            p.drop.seed_lo, p.drop.seed_hi);
       const bool need_mask = (j0 + kT > p.Nk) || (BAND && ((p.wr >= 0 && j0 + kT - 1 > qw0 + p.wr) ||
                                                             (p.wl >= 0 && j0 < qw0 + QW - 1 - p.wl)));
 #pragma unroll
@@ -539,7 +583,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           const int kk = j0 + acc_row(half, r);
           if (kk >= p.Nk || (BAND && ((p.wr >= 0 && kk > qi + p.wr) || (p.wl >= 0 && kk < qi - p.wl)))) pv = 0.f;
         }
-        dp[r] = pv * dp[r];
+        if constexpr (DROP) {  // dS = P (keep * scale * dP - D)
+          const float m = ((rnd[r >> 2] >> (8 * (r & 3))) & 0xffu) >= p.drop.thr ? p.drop.scale : 0.f;
+          dp[r] = pv * __builtin_fmaf(m, dp[r], ndsv);
+        } else {
+          dp[r] = pv * dp[r];
+        }
       }
       const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
       tile_t_times<D, DT>(adq, Kt, bd, ta);  // dQ^T += K^T dS^T
@@ -558,7 +607,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   if (qi < p.Nq) store_rows<DT, DB>(p.dq + b * p.sdq.b + h * p.sdq.h + qi * p.sdq.s, adq, p.scale, half);
 }
 
-template <int D, int DT, bool BAND>
+template <int D, int DT, bool BAND, bool DROP>
 hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
   const int64_t BH = (int64_t)p.B * p.H;
   const int64_t BHkv = (int64_t)p.B * (p.H / p.G);
@@ -574,11 +623,11 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((stages & 2) && g1 > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND>), dim3((unsigned)g1), dim3(2 * kThreads), 0, stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP>), dim3((unsigned)g1), dim3(2 * kThreads), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((stages & 4) && g2 > 0) {
-    hipLaunchKernelGGL((dq_kernel<D, DT, BAND>), dim3((unsigned)g2), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((dq_kernel<D, DT, BAND, DROP>), dim3((unsigned)g2), dim3(kThreads), 0, stream, p);
     e = hipGetLastError();
   }
   return e;
@@ -586,7 +635,9 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
 
 template <int D, int DT>
 hipError_t launch_dc(const BwdParams& p, bool banded, int stages, hipStream_t stream) {
-  return banded ? launch_t<D, DT, true>(p, stages, stream) : launch_t<D, DT, false>(p, stages, stream);
+  if (p.drop.thr > 0)
+    return banded ? launch_t<D, DT, true, true>(p, stages, stream) : launch_t<D, DT, false, true>(p, stages, stream);
+  return banded ? launch_t<D, DT, true, false>(p, stages, stream) : launch_t<D, DT, false, false>(p, stages, stream);
 }
 
 }  // namespace

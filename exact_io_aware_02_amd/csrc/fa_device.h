@@ -164,6 +164,30 @@ __device__ __forceinline__ u32x4 pack_acc8(const f32x16& s, int kk) {
                pack2<DT>(s[o + 6], s[o + 7])};
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11): ten rounds of two 32x32->64-bit products and
+// xors, the key bumped by the two Weyl constants between rounds.  Dropout
+// draws one call per (query row, 16 keys of a 32-key tile).
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t a = (uint64_t)0xD2511F53u * c0;
+    const uint64_t b = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(b >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(a >> 32) ^ c3 ^ k1;
+    c0 = n0;
+    c1 = (uint32_t)b;
+    c2 = n2;
+    c3 = (uint32_t)a;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
 // Combine lane i with lane i^32.  (v_permlane32_swap would avoid the LDS
 // round trip of ds_bpermute, but this compiler maps the builtin's second
 // result onto the first one's register, so it cannot be used for this.)

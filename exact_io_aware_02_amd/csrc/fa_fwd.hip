@@ -93,14 +93,15 @@ struct RowState {
 // The __restrict__ tile pointers tell the compiler the reads never alias
 // the in-flight copy, so it does not wait for that copy before reading;
 // the vmcnt wait and barrier at the end order the ring.
-template <int D, int DT, bool BAND, int kNQB = FwdTile<D>::NQB>
+template <int D, int DT, bool BAND, bool DROP, int kNQB = FwdTile<D>::NQB>
 __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32x16 (&sn)[kNQB],
                                          const uint16_t* __restrict__ Kn, const uint16_t* __restrict__ Vt,
                                          uint16_t* __restrict__ Kdst, uint16_t* __restrict__ Vdst,
                                          __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, uint32_t krow,
                                          uint32_t vrow, uint32_t ktb, uint32_t vtb, const u32x4 (&qf)[kNQB][D / 16],
                                          f32x16 (&acc)[D / 32][kNQB], RowState<kNQB>& st, int Nk, int wl, int wr, int qw0, float c,
-                                         int lane, int wave, const TileAddr<D>& ta) {
+                                         int lane, int wave, const TileAddr<D>& ta, const DropoutParams& dp,
+                                         uint32_t bh) {
   using TC = TileCopy<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -161,28 +162,38 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
     for (int nb = 0; nb < kNQB; ++nb) sn[nb] = mfma32<DT>(a, qf[nb][ks], sn[nb]);
   }
 
-  // ---- P = 2^(S c - m) packed into the MFMA B operand
+  // ---- P = 2^(S c - m) packed into the MFMA B operand (after dropout:
+  // the normaliser sums the undropped weights, the kept ones are rescaled
+  // once in the epilogue)
   u32x4 pf[2][kNQB];
   float ls[kNQB][2];
 #pragma unroll
   for (int nb = 0; nb < kNQB; ++nb) {
     const float mneg = -st.m[nb];
     ls[nb][0] = ls[nb][1] = 0.f;
+    u32x4 rnd = u32x4{0, 0, 0, 0};
+    if constexpr (DROP)  // this lane's 16 keys of tile j: one generator call
+      rnd = philox4x32_10(2u * (uint32_t)j + (uint32_t)half, (uint32_t)(qw0 + 32 * nb + col), bh, dp.offset,
+                          dp.seed_lo, dp.seed_hi);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 8 * kk + 2 * e;
-        const float p0 = exp2_fast(__builtin_fmaf(s[nb][r], c, mneg));
-        const float p1 = exp2_fast(__builtin_fmaf(s[nb][r + 1], c, mneg));
-        w[e] = pack2<DT>(p0, p1);
-        if constexpr (DT == DT_BF16) {  // bf16 rounding (2^-9) is too coarse for the normaliser
+        float p0 = exp2_fast(__builtin_fmaf(s[nb][r], c, mneg));
+        float p1 = exp2_fast(__builtin_fmaf(s[nb][r + 1], c, mneg));
+        if constexpr (DT == DT_BF16 || DROP) {  // bf16 rounding (2^-9) is too coarse for the normaliser
           ls[nb][0] = (r == 0) ? p0 : ls[nb][0] + p0;
           ls[nb][1] = (r == 0) ? p1 : ls[nb][1] + p1;
         }
+        if constexpr (DROP) {  // register r holds key 8*(r/4) + 4*half + r%4 of the tile
+          if (((rnd[r >> 2] >> (8 * (r & 3))) & 0xffu) < dp.thr) p0 = 0.f;
+          if (((rnd[(r + 1) >> 2] >> (8 * ((r + 1) & 3))) & 0xffu) < dp.thr) p1 = 0.f;
+        }
+        w[e] = pack2<DT>(p0, p1);
       }
-      if constexpr (DT == DT_F16) {  // fp16-rounded P is accurate enough: sum pairs in one op
+      if constexpr (DT == DT_F16 && !DROP) {  // fp16-rounded P is accurate enough: sum pairs in one op
 #pragma unroll
         for (int e = 0; e < 4; ++e) ls[nb][e & 1] = dot2_sum<DT>(w[e], ls[nb][e & 1]);
       }
@@ -211,7 +222,7 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int DT, bool BAND>
+template <int D, int DT, bool BAND, bool DROP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTile<D>::WAVES_PER_SIMD,
                                                                           FwdTile<D>::WAVES_PER_SIMD))) void fwd_kernel(FwdParams p) {
   constexpr int kNQB = FwdTile<D>::NQB;
@@ -336,8 +347,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   // without the copy costs ~60 more registers and spills at d = 64.)
   for (int j = jt0; j < n_kt; ++j) {
     const int sl = j & 3;
-    fwd_step<D, DT, BAND>(j, n_kt, sa, sb, Ks[(sl + 1) & 3], Vs[sl], Ks[(sl + 3) & 3], Vs[(sl + 3) & 3], krs, vrs,
-                          krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta);
+    fwd_step<D, DT, BAND, DROP>(j, n_kt, sa, sb, Ks[(sl + 1) & 3], Vs[sl], Ks[(sl + 3) & 3], Vs[(sl + 3) & 3], krs,
+                                vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta,
+                                p.drop, (uint32_t)bh);
 #pragma unroll
     for (int nb = 0; nb < kNQB; ++nb) sa[nb] = sb[nb];
   }
@@ -350,7 +362,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
     const int qi = qw0 + 32 * nb + col;
     if (qi < p.Nq) {
       // a row that admits no key: O = 0, LSE = -inf
-      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      const float inv = lt > 0.f ? (DROP ? p.drop.scale : 1.0f) / lt : 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -366,19 +378,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   }
 }
 
-template <int D, int DT, bool BAND>
+template <int D, int DT, bool BAND, bool DROP>
 hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   constexpr int kBM = FwdTile<D>::BM;
   const int n_qt = (p.Nq + kBM - 1) / kBM;
   const int64_t blocks = (int64_t)n_qt * p.B * p.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND, DROP>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, int DT>
 hipError_t launch_dc(const FwdParams& p, bool banded, hipStream_t stream) {
-  return banded ? launch_t<D, DT, true>(p, stream) : launch_t<D, DT, false>(p, stream);
+  if (p.drop.thr > 0) return banded ? launch_t<D, DT, true, true>(p, stream) : launch_t<D, DT, false, true>(p, stream);
+  return banded ? launch_t<D, DT, true, false>(p, stream) : launch_t<D, DT, false, false>(p, stream);
 }
 
 }  // namespace

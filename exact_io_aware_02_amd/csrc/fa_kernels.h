@@ -5,6 +5,12 @@
 
 namespace fa {
 
+struct DropoutParams {
+  uint32_t thr;    // keep iff the element's random byte >= thr (0: no dropout)
+  float scale;     // 256 / (256 - thr), applied to the kept weights
+  uint32_t seed_lo, seed_hi, offset;
+};
+
 // Element strides {batch, head, seq}; the d dimension is contiguous.
 struct Strides {
   int64_t b, h, s;
@@ -20,6 +26,7 @@ struct FwdParams {
   int B, H, Nq, Nk;
   int G;           // query heads per K/V head (K/V head of query head h is h / G)
   int wl, wr;      // admitted keys of query i: [i - wl, i + wr]; a negative bound is absent
+  DropoutParams drop;
   float c;         // |scale| * log2(e), clamped away from 0
   uint32_t qflip;  // 0x80008000 when scale < 0 (Q is negated on load), else 0
 };
@@ -40,6 +47,7 @@ struct BwdParams {
   int B, H, Nq, Nk;
   int G;        // query heads per K/V head (as FwdParams)
   int wl, wr;   // admitted-key band (as FwdParams)
+  DropoutParams drop;
   float scale;  // the softmax scale as given
   float c;      // scale * log2(e) (signed)
 };

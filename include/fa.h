@@ -89,9 +89,10 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
                    const int64_t v_strides[3], const int64_t o_strides[3],
                    void* stream);
 
-/* Forward with fewer K/V heads and/or a sliding window (the skill guide's
- * Workflow 2, step 3: multi-query attention with K/V shared across heads,
- * and sliding-window attention with window_size = (left, right)).
+/* Forward with fewer K/V heads, a sliding window and/or dropout (the skill
+ * guide's Workflow 2: step 3's multi-query attention with K/V shared across
+ * heads and sliding-window attention with window_size = (left, right), and
+ * step 2's dropout_p argument of flash_attn_func).
  *   H_kv: heads of k and v, dividing H; query head h uses K/V head
  *     h / (H / H_kv), so consecutive query heads share one (H_kv = H is
  *     plain multi-head attention, H_kv = 1 multi-query attention).
@@ -101,11 +102,19 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
  *     keys to j <= i.  Positions are top-left aligned as for causal.
  *   A query row that admits no key (possible with a window when Nq > Nk)
  *   gets O = 0 and LSE = -inf.
+ *   dropout_p in [0, 1): each attention weight (after the softmax) is
+ *     dropped with probability thr/256, thr = min(255, rint(256 dropout_p)),
+ *     and kept ones are scaled by 256/(256 - thr); LSE is that of the
+ *     undropped scores.  Element (b, h, i, j) (h a query head) is kept iff
+ *     byte (j & 3) of word ((j >> 3) & 3) of Philox4x32-10 (Salmon et al.,
+ *     SC'11) at counter {2*(j >> 5) + ((j >> 2) & 1), i, b*H + h, offset}
+ *     with key {seed mod 2^32, seed >> 32} is >= thr.  The same (seed,
+ *     offset) in fa_bwd_ex reproduces the mask.  dropout_p = 0: no dropout.
  *   k, v: [B][H_kv][Nk][d] through their strides; everything else as in
  *   fa_fwd_strided. */
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
-              int window_left, int window_right, int dtype,
+              int window_left, int window_right, float dropout_p, uint64_t seed, uint32_t offset, int dtype,
               const int64_t q_strides[3], const int64_t k_strides[3],
               const int64_t v_strides[3], const int64_t o_strides[3],
               void* stream);
@@ -158,9 +167,10 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
                   const int64_t dk_strides[3], const int64_t dv_strides[3],
                   void* workspace, size_t workspace_bytes, int stages, void* stream);
 
-/* Backward of fa_fwd_ex: the stages of fa_bwd_stages with fewer K/V heads
- * and/or a sliding window, H_kv, window_left, window_right and causal as in
- * fa_fwd_ex.  dk, dv are [B][H_kv][Nk][d] through their strides; a K/V
+/* Backward of fa_fwd_ex: the stages of fa_bwd_stages with fewer K/V heads,
+ * a sliding window and/or dropout; H_kv, window_left, window_right, causal,
+ * dropout_p, seed and offset as in the fa_fwd_ex call that produced o and
+ * lse.  dk, dv are [B][H_kv][Nk][d] through their strides; a K/V
  * head's gradients sum the contributions of all query heads that use it.
  * The workspace is sized by fa_bwd_workspace_bytes(B, H, Nq, ...) with H
  * the number of query heads.  lse must be what fa_fwd_ex wrote (-inf for a
@@ -168,7 +178,7 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
               const void* dout, void* dq, void* dk, void* dv,
               int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
-              int window_left, int window_right, int dtype,
+              int window_left, int window_right, float dropout_p, uint64_t seed, uint32_t offset, int dtype,
               const int64_t q_strides[3], const int64_t k_strides[3],
               const int64_t v_strides[3], const int64_t o_strides[3],
               const int64_t do_strides[3], const int64_t dq_strides[3],

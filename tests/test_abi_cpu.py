@@ -186,23 +186,24 @@ def test_valid_call_without_device_reports_device_error():
 
 # --- fewer K/V heads and sliding window (fa_fwd_ex / fa_bwd_ex) ---------------
 
-def fwd_ex(H=4, Hkv=2, wl=-1, wr=-1, causal=0, Nq=16, Nk=16):
+def fwd_ex(H=4, Hkv=2, wl=-1, wr=-1, causal=0, Nq=16, Nk=16, dropout=0.0):
     lib = fa.load_library()
     I3 = ctypes.c_int64 * 3
     sq = I3(H * Nq * 64, Nq * 64, 64)
     sk = I3(Hkv * Nk * 64, Nk * 64, 64)
     return lib.fa_fwd_ex(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), 1, H, Hkv, Nq, Nk, 64, 0.125, causal, wl, wr,
-                         0, sq, sk, sk, sq, None)
+                         dropout, 7, 0, 0, sq, sk, sk, sq, None)
 
 
-def bwd_ex(H=4, Hkv=2, wl=-1, wr=-1, causal=0, dk=8 * A, stages=fa.FA_BWD_ALL):
+def bwd_ex(H=4, Hkv=2, wl=-1, wr=-1, causal=0, dk=8 * A, stages=fa.FA_BWD_ALL, dropout=0.0):
     lib = fa.load_library()
     I3 = ctypes.c_int64 * 3
     sq = I3(H * 16 * 64, 16 * 64, 64)
     sk = I3(Hkv * 16 * 64, 16 * 64, 64)
     st = [sq, sk, sk, sq, sq, sq, sk, sk]
     return lib.fa_bwd_ex(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), P(6 * A), P(7 * A), P(dk), P(9 * A),
-                         1, H, Hkv, 16, 16, 64, 0.125, causal, wl, wr, 0, *st, P(10 * A), 1 << 16, stages, None)
+                         1, H, Hkv, 16, 16, 64, 0.125, causal, wl, wr, dropout, 7, 0, 0, *st, P(10 * A), 1 << 16,
+                         stages, None)
 
 
 @pytest.mark.parametrize("H,Hkv", [(4, 3), (4, 0), (4, -2), (3, 6)])
@@ -225,3 +226,17 @@ def test_ex_accepts_any_window(wl, wr, causal):
     call reaches the device check."""
     assert fwd_ex(wl=wl, wr=wr, causal=causal) == fa.FA_ERR_DEVICE
     assert bwd_ex(wl=wl, wr=wr, causal=causal) == fa.FA_ERR_DEVICE
+
+
+@pytest.mark.parametrize("p", [-0.1, 1.0, 2.0, float("nan"), float("inf")])
+def test_ex_rejects_bad_dropout(p):
+    assert fwd_ex(dropout=p) == fa.FA_ERR_INVALID_ARG
+    assert "dropout" in fa.fa_last_error_message()
+    assert bwd_ex(dropout=p) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful where no HIP device exists")
+@pytest.mark.parametrize("p", [0.0, 0.1, 0.5, 0.999])
+def test_ex_accepts_dropout(p):
+    assert fwd_ex(dropout=p) == fa.FA_ERR_DEVICE
+    assert bwd_ex(dropout=p) == fa.FA_ERR_DEVICE
