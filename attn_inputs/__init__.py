@@ -9,7 +9,9 @@ Recipe: numpy ``default_rng(seed)`` (PCG64) draws float32 ``standard_normal``
 arrays in the workload's own memory layout, in the order q, k, v, then dO
 when a backward is needed; an optional constant factor (0.5 for the 16K
 workload, exact in binary) is applied in float32; the result is rounded to
-fp16/bf16 with round-to-nearest-even (torch ``.to``).  The pages' workloads
+fp16/bf16 with round-to-nearest-even (torch ``.to``), or to float8_e4m3fn
+(torch's round-to-nearest-even cast) for the fp8 forward, whose pages cast
+torch.randn tensors the same way.  The pages' workloads
 are ``torch.randn`` tensors of fixed shapes ("Flash Attention" skill guide
 quick start and Workflows 1-2; glossary article quick start), which these
 stand in for.
@@ -21,7 +23,7 @@ __all__ = ["WORKLOADS", "Workload", "make_qkv", "to_bhsd64", "sample_rows", "tor
 
 
 def torch_dtype(name):
-    return {"fp16": torch.float16, "bf16": torch.bfloat16}[name]
+    return {"fp16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[name]
 
 
 class Workload:
@@ -84,6 +86,15 @@ def workload_inputs(w, seed=None):
                     w.in_scale, with_do=w.backward)
 
 
+def fp8_bytes(t, layout="bhsd"):
+    """The bytes of a float8_e4m3fn CPU tensor as a uint8 numpy array in
+    [B, H, N, d] order."""
+    a = t.detach().to("cpu").view(torch.uint8).numpy()
+    if layout == "bshd":
+        a = np.ascontiguousarray(a.transpose(0, 2, 1, 3))
+    return a
+
+
 def to_bhsd64(t, layout="bhsd"):
     """Widen a CPU tensor to a float64 numpy array in [B, H, N, d] order."""
     a = t.detach().to("cpu").to(torch.float64).numpy()
@@ -108,4 +119,4 @@ def sample_rows(B, H, N, R, seed):
     return out
 
 
-__all__.append("workload_inputs")
+__all__ += ["workload_inputs", "fp8_bytes"]

@@ -20,6 +20,7 @@ from .attention import (
     dropout_threshold,
     dropout_keep,
 )
+from .fp8 import e4m3fn_to_float64, attention_fp8_fwd64, attention_fp8_rows_fwd64, fp8_rounding_model
 
 __all__ = [
     "attention_fwd64",
@@ -28,4 +29,8 @@ __all__ = [
     "philox4x32_10",
     "dropout_threshold",
     "dropout_keep",
+    "e4m3fn_to_float64",
+    "attention_fp8_fwd64",
+    "attention_fp8_rows_fwd64",
+    "fp8_rounding_model",
 ]
