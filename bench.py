@@ -20,7 +20,9 @@ event-measured average duration; the dominant one is reported as `roofline`
 rows_f: the same step for the built extensions on the same inputs: 16 query
 heads on 2 K/V heads (causal), a causal sliding window of 256 keys (the skill
 guide's window example), and causal dropout with p = 0.1 (the skill guide's
-dropout_p); FLOPs count admitted (query, key) pairs.
+dropout_p); plus the fp8 forward alone on the inputs cast to float8_e4m3fn
+(priced against the fp8 MFMA peak, 5.0 PFLOP/s).  FLOPs count admitted
+(query, key) pairs.
 
 cpu_baseline: the fp64 numpy oracle (test infrastructure) on four heads of the
 same workload, forward + backward, timed on the host cores.
@@ -36,7 +38,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # MI355X dense MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "fwd_causal_b1h16_n16384_d128_bf16_bhsd"
 METRIC = "attention fwd/bwd TFLOP/s + % of MFMA peak (fp16/bf16, causal & not)"
@@ -124,8 +126,9 @@ def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
     """Forward + backward of the built 'next' rows on the same 16K inputs:
     fewer K/V heads (the first GQA_KV_HEADS heads of k, v shared by all 16
     query heads, causal), a causal sliding window WINDOW, and causal dropout
-    DROPOUT.  FLOPs count the admitted (query, key) pairs; the backward is
-    2.5x the forward."""
+    DROPOUT; and the fp8 forward (forward only) on the inputs cast to
+    float8_e4m3fn, against the fp8 MFMA peak.  FLOPs count the admitted
+    (query, key) pairs; the backward is 2.5x the forward."""
     B, H, N, d = q.shape
     res = {}
     kg, vg = k[:, :GQA_KV_HEADS].contiguous(), v[:, :GQA_KV_HEADS].contiguous()
@@ -174,6 +177,29 @@ def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
                      "step_tflops": 3.5 * ff / (tf + tb) / 1e9, "fwd_frac_of_peak": ff / tf / 1e9 / peak}
         log("%s: fwd %.3f ms (%.1f TFLOP/s), bwd %.3f ms (%.1f TFLOP/s)" % (
             name, tf, ff / tf / 1e9, tb, 2.5 * ff / tb / 1e9))
+
+    q8, k8, v8 = (t.to(torch.float8_e4m3fn) for t in (q, k, v))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+
+    def fwd8():
+        fa.fa_fwd_fp8(q8, k8, v8, o, lse, s, True, (-1, -1), (1.0, 1.0, 1.0), "bhsd", stream)
+
+    for _ in range(3):
+        fwd8()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        fwd8()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    tf = ev[0].elapsed_time(ev[1]) / steps
+    ff = 4.0 * B * H * d * pairs_causal
+    res["fp8_fwd"] = {"workload": "B1 H16 N16384 d128 float8_e4m3fn causal (the bf16 inputs cast), bf16 out",
+                      "fwd_ms": tf, "fwd_tflops": ff / tf / 1e9, "peak": PEAK_TFLOPS["fp8"],
+                      "fwd_frac_of_peak": ff / tf / 1e9 / PEAK_TFLOPS["fp8"]}
+    log("fp8_fwd: fwd %.3f ms (%.1f TFLOP/s, %.1f%% of the fp8 peak)" % (
+        tf, ff / tf / 1e9, 100 * ff / tf / 1e9 / PEAK_TFLOPS["fp8"]))
     return res
 
 

@@ -2,7 +2,7 @@
 
 Thin ctypes marshalling over the C ABI in ``include/fa.h``.  The functions
 named like the C entry points (``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_ex``,
-``fa_bwd``, ``fa_bwd_strided``, ``fa_bwd_stages``, ``fa_bwd_ex``,
+``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_strided``, ``fa_bwd_stages``, ``fa_bwd_ex``,
 ``fa_bwd_workspace_bytes``, ``fa_status_string``, ``fa_last_error_message``)
 take torch tensors, read their sizes and strides,
 and call the library on the tensors' device and current stream.  Every step
@@ -10,7 +10,7 @@ of the computation runs in the library's HIP kernels; there is no other
 implementation here, and nothing falls back: if libfa.so is missing or the
 device is not gfx950, calls raise.
 
-``attention_fwd`` / ``attention_bwd`` are conveniences that allocate the
+``attention_fwd`` / ``attention_bwd`` / ``attention_fwd_fp8`` are conveniences that allocate the
 outputs (and the backward workspace) with torch, then call the entry points.
 """
 import ctypes
@@ -22,11 +22,11 @@ import torch
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_DEVICE", "FA_ERR_LAUNCH",
     "FA_FP16", "FA_BF16", "FaError", "lib_path", "load_library",
-    "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages", "fa_bwd_ex",
-    "fa_bwd_workspace_bytes",
+    "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_fwd_fp8", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
+    "fa_bwd_ex", "fa_bwd_workspace_bytes",
     "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
     "fa_status_string", "fa_last_error_message", "fa_abi_version",
-    "attention_fwd", "attention_bwd", "EXPORTED_SYMBOLS",
+    "attention_fwd", "attention_bwd", "attention_fwd_fp8", "EXPORTED_SYMBOLS",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_DEVICE, FA_ERR_LAUNCH = 0, 1, 2, 3, 4
@@ -35,7 +35,7 @@ FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED_SYMBOLS = (
     "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
-    "fa_bwd_ex", "fa_status_string", "fa_last_error_message", "fa_abi_version",
+    "fa_bwd_ex", "fa_fwd_fp8", "fa_status_string", "fa_last_error_message", "fa_abi_version",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +85,8 @@ def load_library():
     lib.fa_bwd_ex.argtypes = ([_vp] * 9 + [_i] * 6 + [_f, _i, _i, _i, _f, _u64, _u32, _i] + [_I64x3] * 8 +
                               [_vp, _sz, _i, _vp])
     lib.fa_bwd_ex.restype = _i
+    lib.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _i, _i, _f, _f, _f] + [_I64x3] * 4 + [_vp]
+    lib.fa_fwd_fp8.restype = _i
     lib.fa_status_string.argtypes = [_i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error_message.argtypes = []
@@ -283,6 +285,47 @@ def fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, window=
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
             B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), wl, wr, dp, seed, off, dt, *st,
             _ptr(workspace), nbytes, int(stages), _stream(q, stream)))
+
+
+def _fp8_input(*ts):
+    for t in ts:
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise FaError(FA_ERR_UNSUPPORTED, "fp8 inputs must be float8_e4m3fn (or its bytes as uint8), got %s"
+                          % t.dtype)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, scale, causal, window=(-1, -1), descale=(1.0, 1.0, 1.0), layout="bhsd",
+               stream=None):
+    """C ``fa_fwd_fp8``: q, k, v float8_e4m3fn (k, v may have fewer heads),
+    o bf16 shaped like q, lse fp32 [B,H,Nq]; ``descale`` = (q, k, v)
+    per-tensor factors."""
+    _fp8_input(q, k, v)
+    if o.dtype != torch.bfloat16:
+        raise FaError(FA_ERR_UNSUPPORTED, "fp8 forward writes a bfloat16 o, got %s" % o.dtype)
+    _on_device(q, k, v, o, lse)
+    B, H, Nq, d = _dims(q, layout)
+    Hkv, Nk = _dims(k, layout)[1:3]
+    wl, wr = _window(window)
+    qd, kd, vd = (float(x) for x in descale)
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_fwd_fp8(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+            wl, wr, qd, kd, vd, _strides(q, layout), _strides(k, layout), _strides(v, layout),
+            _strides(o, layout), _stream(q, stream)))
+
+
+def attention_fwd_fp8(q, k, v, causal=False, scale=None, layout="bhsd", stream=None, window=None,
+                      descale=(1.0, 1.0, 1.0)):
+    """Forward on float8_e4m3fn q, k, v; allocates o (bf16, q's shape) and
+    lse (fp32 [B,H,Nq]); returns (o, lse).  No backward exists for fp8."""
+    _fp8_input(q, k, v)
+    _on_device(q, k, v)
+    B, H, Nq, d = _dims(q, layout)
+    s = _default_scale(d, scale)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(q, k, v, o, lse, s, causal, window, descale, layout, stream)
+    return o, lse
 
 
 def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None, window=None, dropout=None):

@@ -61,16 +61,21 @@ struct Extent {
   int64_t lo_bytes, hi_bytes;  // [lo, hi) byte range relative to the base pointer
 };
 
-int check_tensor(const char* name, const void* ptr, const int64_t st[3], int B, int H, int N, int d, Extent* ext) {
+// elem: bytes per element (2, or 1 for fp8); strides must keep every row
+// 16-byte aligned.
+int check_tensor(const char* name, const void* ptr, const int64_t st[3], int B, int H, int N, int d, Extent* ext,
+                 int elem = 2) {
   ext->lo_bytes = 0;
   ext->hi_bytes = 0;
   if (N == 0) return FA_OK;  // empty tensor: never dereferenced
   if (!ptr) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
   if (!aligned16(ptr)) return fail(FA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  const int unit = 16 / elem;
   for (int i = 0; i < 3; ++i) {
     if (st[i] < 0) return fail(FA_ERR_INVALID_ARG, "%s stride[%d] = %lld is negative", name, i, (long long)st[i]);
-    if (st[i] % 8 != 0)
-      return fail(FA_ERR_INVALID_ARG, "%s stride[%d] = %lld is not a multiple of 8 elements", name, i, (long long)st[i]);
+    if (st[i] % unit != 0)
+      return fail(FA_ERR_INVALID_ARG, "%s stride[%d] = %lld is not a multiple of %d elements", name, i,
+                  (long long)st[i], unit);
   }
   if (N > 1 && st[2] < d) return fail(FA_ERR_INVALID_ARG, "%s seq stride %lld < d = %d (rows overlap)", name, (long long)st[2], d);
   // within one (b, h) slice the kernels use 32-bit-safe offsets
@@ -79,7 +84,7 @@ int check_tensor(const char* name, const void* ptr, const int64_t st[3], int B, 
   const int64_t last = (int64_t)(B - 1) * st[0] + (int64_t)(H - 1) * st[1] + (int64_t)(N - 1) * st[2] + d;
   if (last > (INT64_MAX / 4)) return fail(FA_ERR_INVALID_ARG, "%s: extent overflows", name);
   ext->lo_bytes = 0;
-  ext->hi_bytes = last * 2;
+  ext->hi_bytes = last * elem;
   return FA_OK;
 }
 
@@ -155,7 +160,7 @@ void contiguous_strides(int H, int N, int d, int64_t st[3]) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 2; }
+int fa_abi_version(void) { return 3; }
 
 const char* fa_status_string(int status) {
   switch (status) {
@@ -237,6 +242,61 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   contiguous_strides(H, Nq, d, sq);
   contiguous_strides(H, Nk, d, sk);
   return fa_fwd_strided(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, sq, sk, sk, sq, stream);
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int Nq,
+               int Nk, int d, float scale, int causal, int window_left, int window_right, float q_descale,
+               float k_descale, float v_descale, const int64_t q_strides[3], const int64_t k_strides[3],
+               const int64_t v_strides[3], const int64_t o_strides[3], void* stream) {
+  g_msg[0] = '\0';
+  int st = check_common(B, H, Nq, Nk, d, scale, causal, FA_BF16);
+  if (st) return st;
+  if ((st = check_heads(B, H, H_kv))) return st;
+  if (!std::isfinite(q_descale) || !std::isfinite(k_descale) || !std::isfinite(v_descale))
+    return fail(FA_ERR_INVALID_ARG, "a descale factor is not finite");
+  const double cs = (double)scale * (double)q_descale * (double)k_descale;
+  if (!std::isfinite(cs) || std::fabs(cs) > 3.0e38)
+    return fail(FA_ERR_INVALID_ARG, "scale * q_descale * k_descale overflows fp32");
+  if (!q_strides || !k_strides || !v_strides || !o_strides) return fail(FA_ERR_INVALID_ARG, "a strides array is NULL");
+  if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+  Extent eq, ek, ev, eo;
+  if ((st = check_tensor("q", q, q_strides, B, H, Nq, d, &eq, 1))) return st;
+  if ((st = check_tensor("k", k, k_strides, B, H_kv, Nk, d, &ek, 1))) return st;
+  if ((st = check_tensor("v", v, v_strides, B, H_kv, Nk, d, &ev, 1))) return st;
+  if ((st = check_tensor("o", o, o_strides, B, H, Nq, d, &eo))) return st;
+  if (!lse) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  Extent el{0, (int64_t)B * H * Nq * 4};
+  if (overlaps(o, eo, q, eq) || overlaps(o, eo, k, ek) || overlaps(o, eo, v, ev))
+    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+  if (overlaps(lse, el, q, eq) || overlaps(lse, el, k, ek) || overlaps(lse, el, v, ev) || overlaps(lse, el, o, eo))
+    return fail(FA_ERR_INVALID_ARG, "lse overlaps another tensor");
+  if ((st = check_device())) return st;
+
+  fa::Fp8Params p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.sq = {q_strides[0], q_strides[1], q_strides[2]};
+  p.sk = {k_strides[0], k_strides[1], k_strides[2]};
+  p.sv = {v_strides[0], v_strides[1], v_strides[2]};
+  p.so = {o_strides[0], o_strides[1], o_strides[2]};
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.G = H / H_kv;
+  const Band band = make_band(causal, window_left, window_right, Nq, Nk);
+  p.wl = band.wl;
+  p.wr = band.wr;
+  p.c = softmax_c((float)cs);
+  p.qflip = std::signbit((float)cs) ? 0x80808080u : 0u;
+  p.vscale = v_descale;
+  hipError_t e = fa::launch_fwd_fp8(p, d, band.present(), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "fp8 forward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {

@@ -1,0 +1,325 @@
+// Forward attention with fp8 (OCP e4m3fn) Q, K and V on gfx950.
+//
+// The skill guide's Workflow 3 (FlashAttention-3's FP8 forward): inputs cast
+// to float8_e4m3fn, forward only.  Both contractions run on
+// v_mfma_f32_32x32x64_f8f6f4 (fp8 in, fp32 accumulate):
+//
+//   S^T = K_j Q^T      A = K rows from LDS (32 bytes of d per lane), B = Q
+//                      held in registers; scores scaled by
+//                      scale * q_descale * k_descale.
+//   online softmax     as the 16-bit kernel (running max in log2 units,
+//                      lazy rescale by 2^8, fp32 row sums of the unrounded
+//                      weights).
+//   O^T += V_j^T P^T   P (<= 2^8, inside e4m3's range) rounded to e4m3fn
+//                      with v_cvt_pk_fp8_f32 straight from the S^T
+//                      accumulator into the B operand; V^T read from the
+//                      untransposed V tile with ds_read_b64_tr_b8.
+//
+// O = O^T * v_descale / l in bf16, LSE fp32.  One workgroup of 4 waves owns
+// 128 queries (32 per wave, a query per lane); key tiles of 64 stream
+// HBM -> LDS through a 4-slot ring.  Causal masks, sliding windows and
+// fewer K/V heads work as in the 16-bit forward.
+//
+// Operand layouts (measured on gfx950): the A and B operands of the fp8 MFMA
+// use the same k order per lane half, so any consistent assignment of keys
+// (or d) to the 32 byte slots of a lane works.  ds_read_b64_tr_b8 gives, in
+// each group of 16 lanes, lane l as element j the byte l % 8 of the 8-byte
+// word addressed by lane 2j + l / 8 of the group.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kW8 = 4;         // waves per workgroup
+constexpr int kT8 = 64 * kW8;  // threads
+constexpr int kBN8 = 64;       // keys per tile: one 64-deep k step of P V
+constexpr int kQW8 = 32;       // queries per wave
+constexpr int kBM8 = kW8 * kQW8;
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// LDS tile [64 rows][D bytes]: 16-byte chunk c of row r lives at chunk
+// c ^ swz8(r), which keeps 16 consecutive rows at one chunk (the K operand
+// reads) and the transposing reads' 8 rows free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int swz8(int r) {
+  if constexpr (D == 128) {
+    return (r >> 1) & 7;
+  } else {
+    return (r >> 2) & 3;
+  }
+}
+template <int D>
+__device__ __forceinline__ int off8(int r, int byte) {
+  return r * D + ((((byte >> 4) ^ swz8<D>(r)) << 4) | (byte & 15));
+}
+
+// 64 rows of a [N][D]-byte tensor into the swizzled tile; lane i of a wave
+// instruction fills LDS bytes 16*i .. 16*i+15 of its block (1 KiB).
+template <int D>
+struct Tile8Copy {
+  static constexpr int CH = D / 16;
+  static constexpr int RPI = 64 / CH;
+  static constexpr int NI = kBN8 / RPI / kW8;
+  static_assert(NI >= 1 && NI * RPI * kW8 == kBN8, "tile split");
+  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t tile_off,
+                                               uint8_t* lds, int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (wave * NI + i) * RPI + lane / CH;
+      const int c = (lane % CH) ^ swz8<D>(r);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + (wave * NI + i) * RPI * D),
+                                               16, (uint32_t)r * row_bytes + (uint32_t)(c * 16), tile_off, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc8(const uint8_t* base, int n, int64_t stride, int d) {
+  const int bytes = (int)((int64_t)(n - 1) * stride + d);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 lds16(const uint8_t* base, int off) { return *(const u32x4*)(base + off); }
+__device__ __forceinline__ i32x2 lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+}
+
+// One K/V tile.  The __restrict__ tile pointers keep the compiler from
+// waiting for the in-flight copy into another slot before reading these.
+template <int D, bool BAND>
+__device__ __forceinline__ void fwd8_tile(int j, int n_kt, const uint8_t* __restrict__ Kt,
+                                          const uint8_t* __restrict__ Vt, uint8_t* __restrict__ Kdst,
+                                          uint8_t* __restrict__ Vdst, __amdgpu_buffer_rsrc_t krs,
+                                          __amdgpu_buffer_rsrc_t vrs, uint32_t krow, uint32_t vrow,
+                                          const i32x8 (&qf)[D / 64], f32x16 (&acc)[D / 32], float& m, float& l,
+                                          int Nk, int wl, int wr, int qw0, float c, int lane, int wave) {
+  using TC = Tile8Copy<D>;
+  constexpr int KS = D / 64;
+  constexpr int DB = D / 32;
+  const int j0 = j * kBN8;
+  const int col = lane & 31, half = lane >> 5;
+  const int qi = qw0 + col;
+
+  if (j + 3 < n_kt) {
+    TC::issue(krs, krow, (uint32_t)(j + 3) * kBN8 * krow, Kdst, lane, wave);
+    TC::issue(vrs, vrow, (uint32_t)(j + 3) * kBN8 * vrow, Vdst, lane, wave);
+  }
+
+  // ---- S^T = K Q^T for keys j0 + 32 mb + acc_row(half, r)
+  f32x16 s[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    s[mb] = f32x16{};
+    const int row = 32 * mb + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 lo = lds16(Kt, off8<D>(row, 64 * ks + 32 * half));
+      const u32x4 hi = lds16(Kt, off8<D>(row, 64 * ks + 32 * half + 16));
+      const i32x8 a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                            (int)hi[3]};
+      s[mb] = mfma_fp8(a, qf[ks], s[mb]);
+    }
+  }
+
+  // ---- masks
+  if ((j0 + kBN8 > Nk) ||
+      (BAND && ((wr >= 0 && j0 + kBN8 - 1 > qw0 + wr) || (wl >= 0 && j0 < qw0 + kQW8 - 1 - wl)))) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * mb + acc_row(half, r);
+        if (key >= Nk || (BAND && ((wr >= 0 && key > qi + wr) || (wl >= 0 && key < qi - wl))))
+          s[mb][r] = -__builtin_inff();
+      }
+  }
+
+  // ---- online softmax
+  float mx = s[0][0];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+  const float mxc = max_pair32(mx) * c;
+  if (__any(mxc > m + 8.0f)) {
+    const float mnew = fmaxf(m, mxc);
+    const float alpha = exp2_fast(m - mnew);
+    m = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+  }
+  // P <= 2^8 (inside e4m3's 448), rounded into the B operand: byte 16 mb + r
+  // of the lane holds the key of accumulator register r of block mb
+  i32x8 pf;
+  const float mneg = -m;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 4) {
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = exp2_fast(__builtin_fmaf(s[mb][r + e], c, mneg));
+        l += p[e];
+      }
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+      pf[4 * mb + r / 4] = w;
+    }
+
+  // ---- O^T += V^T P^T: slot 8u + e of a lane holds key
+  // 32(u/2) + 16(u%2) + 8(e/4) + 4 half + e%4, the key P's byte 8u + e holds
+  const int g = lane >> 4, pl = lane & 15, je = pl >> 1;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    i32x8 a;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = 32 * (u >> 1) + 16 * (u & 1) + 8 * (je >> 2) + 4 * half + (je & 3);
+      const int cb = 32 * db + 16 * (g & 1) + 8 * (pl & 1);
+      const i32x2 t = lds_tr8(Vt + off8<D>(row, cb));
+      a[2 * u] = t[0];
+      a[2 * u + 1] = t[1];
+    }
+    acc[db] = mfma_fp8(a, pf, acc[db]);
+  }
+
+  // tile j+1 must have landed; the later ones fly on
+  if (j + 3 < n_kt) {
+    wait_vmcnt<4 * TC::NI>();
+  } else if (j + 2 < n_kt) {
+    wait_vmcnt<2 * TC::NI>();
+  } else {
+    wait_loads();
+  }
+  lds_barrier();
+}
+
+template <int D, bool BAND>
+__global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_fp8_kernel(Fp8Params p) {
+  constexpr int KS = D / 64;
+  constexpr int DB = D / 32;
+  constexpr int TILE = kBN8 * D;
+  using TC = Tile8Copy<D>;
+
+  struct Smem {  // one LDS object (see the 16-bit forward)
+    uint8_t k[4][TILE];
+    uint8_t v[4][TILE];
+  };
+  __shared__ __attribute__((aligned(1024))) Smem sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int BH = p.B * p.H;
+  const int n_qt = (p.Nq + kBM8 - 1) / kBM8;
+  const int t = blockIdx.x;
+  const int qt = n_qt - 1 - t / BH;  // heaviest query tiles first
+  const int bh = t - (t / BH) * BH;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int hk = h / p.G;
+  const int q0 = qt * kBM8;
+  const int qw0 = q0 + wave * kQW8;
+  const int qi = qw0 + col;
+
+  const uint8_t* qp = p.q + b * p.sq.b + h * p.sq.h;
+  const uint8_t* kp = p.k + b * p.sk.b + hk * p.sk.h;
+  const uint8_t* vp = p.v + b * p.sv.b + hk * p.sv.h;
+
+  int kend = p.Nk, jt0 = 0;
+  if (BAND) {
+    const int qlast = min(q0 + kBM8, p.Nq) - 1;
+    if (p.wr >= 0) kend = min(p.Nk, qlast + p.wr + 1);
+    if (p.wl >= 0) jt0 = max(0, q0 - p.wl) / kBN8;
+  }
+  const int n_kt = (kend + kBN8 - 1) / kBN8;
+
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc8(kp, p.Nk, p.sk.s, D);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc8(vp, p.Nk, p.sv.s, D);
+  const uint32_t krow = (uint32_t)p.sk.s, vrow = (uint32_t)p.sv.s;
+
+  // Q^T as the B operand: lane holds Q[qi][64 ks + 32 half .. +31]
+  i32x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 lo = u32x4{0, 0, 0, 0}, hi = u32x4{0, 0, 0, 0};
+    if (qi < p.Nq) {
+      lo = *(const u32x4*)(qp + qi * p.sq.s + 64 * ks + 32 * half);
+      hi = *(const u32x4*)(qp + qi * p.sq.s + 64 * ks + 32 * half + 16);
+    }
+    qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+#pragma unroll
+  for (int t0 = 0; t0 < 3; ++t0) {
+    const int jj = jt0 + t0;
+    if (jj < n_kt) {
+      TC::issue(krs, krow, (uint32_t)jj * kBN8 * krow, sm.k[jj & 3], lane, wave);
+      TC::issue(vrs, vrow, (uint32_t)jj * kBN8 * vrow, sm.v[jj & 3], lane, wave);
+    }
+  }
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m = -1e30f, l = 0.f;
+  const float c = p.c;
+
+  if (n_kt - jt0 > 2) {
+    wait_vmcnt<4 * TC::NI>();
+  } else if (n_kt - jt0 > 1) {
+    wait_vmcnt<2 * TC::NI>();
+  } else {
+    wait_loads();
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] ^= (int)p.qflip;
+  lds_barrier();
+
+  for (int j = jt0; j < n_kt; ++j) {
+    const int sl = j & 3;
+    fwd8_tile<D, BAND>(j, n_kt, sm.k[sl], sm.v[sl], sm.k[(sl + 3) & 3], sm.v[(sl + 3) & 3], krs, vrs, krow, vrow,
+                       qf, acc, m, l, p.Nk, p.wl, p.wr, qw0, c, lane, wave);
+  }
+
+  // ---- epilogue: O = O^T * v_descale / l in bf16, LSE
+  const float lt = sum_pair32(l);
+  if (qi < p.Nq) {
+    uint16_t* op = p.o + b * p.so.b + h * p.so.h + qi * p.so.s;
+    const float f = lt > 0.f ? p.vscale / lt : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * half;
+        const f32x16& a = acc[db];
+        *(u32x2*)(op + d0) = u32x2{pack2<DT_BF16>(a[4 * g4 + 0] * f, a[4 * g4 + 1] * f),
+                                   pack2<DT_BF16>(a[4 * g4 + 2] * f, a[4 * g4 + 3] * f)};
+      }
+    if (half == 0) p.lse[(int64_t)bh * p.Nq + qi] = lt > 0.f ? (m + log2_fast(lt)) * kLn2 : -__builtin_inff();
+  }
+}
+
+template <int D, bool BAND>
+hipError_t launch8(const Fp8Params& p, hipStream_t stream) {
+  const int n_qt = (p.Nq + kBM8 - 1) / kBM8;
+  const int64_t blocks = (int64_t)n_qt * p.B * p.H;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, BAND>), dim3((unsigned)blocks), dim3(kT8), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, bool banded, hipStream_t stream) {
+  if (d == 64) return banded ? launch8<64, true>(p, stream) : launch8<64, false>(p, stream);
+  return banded ? launch8<128, true>(p, stream) : launch8<128, false>(p, stream);
+}
+
+}  // namespace fa

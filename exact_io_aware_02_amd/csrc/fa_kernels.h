@@ -52,6 +52,23 @@ struct BwdParams {
   float c;      // scale * log2(e) (signed)
 };
 
+// fp8 (OCP e4m3fn) forward: q, k, v are bytes, o is bf16.
+struct Fp8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  uint16_t* o;
+  float* lse;
+  Strides sq, sk, sv, so;  // elements (bytes for q, k, v)
+  int B, H, Nq, Nk;
+  int G;           // query heads per K/V head
+  int wl, wr;      // admitted-key band (as FwdParams)
+  float c;         // |scale * q_descale * k_descale| * log2(e), clamped away from 0
+  uint32_t qflip;  // 0x80808080 when that product is negative (Q negated on load), else 0
+  float vscale;    // v_descale
+};
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, bool banded, hipStream_t stream);
+
 // Return hipSuccess or the launch error.  d in {64,128}, dtype 0 = fp16,
 // 1 = bf16; the caller has validated every argument.  `banded`: some bound
 // of the admitted-key band is present (causal is the band wr = 0).

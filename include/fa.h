@@ -119,6 +119,41 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               const int64_t v_strides[3], const int64_t o_strides[3],
               void* stream);
 
+/* Forward with fp8 inputs (the skill guide's Workflow 3, step 3:
+ * FlashAttention-3's FP8 path, forward only, q, k and v cast to
+ * float8_e4m3fn).
+ *   q, k, v: OCP FP8 E4M3 "fn" bytes (1 sign, 4 exponent bits with bias 7,
+ *     3 mantissa bits; no infinities, 0x7f/0xff are NaN, largest finite
+ *     448), the layout of fa_fwd_ex with strides in elements = bytes;
+ *     k, v have H_kv heads.
+ *   q_descale, k_descale, v_descale: per-tensor factors the stored values
+ *     are multiplied by, so the attention computed is that of
+ *     q_descale*q, k_descale*k, v_descale*v (1.0 for a plain cast).
+ *   o: bf16 [B][H][Nq][d] through o_strides, O = softmax(scale QK^T) V of
+ *     the descaled inputs; lse: fp32 [B][H][Nq] natural log as fa_fwd_ex.
+ *   H_kv, causal, window_left, window_right: as fa_fwd_ex; no dropout.
+ * Arithmetic: Q K^T on the fp8 matrix cores with fp32 accumulation; the
+ * softmax in fp32; the weights p_j = exp(s_j - m) (each <= 2^8, the running
+ * maximum m lagging the row maximum by at most 8 in log2 units) rounded to
+ * e4m3fn (nearest even) for the P V product, the normaliser l summed from
+ * the unrounded weights in fp32.  Rounding the weights dominates the
+ * error: per element of O, |error| <= 2^-4 sum_j w_j |v_j| +
+ * 2^-10 sum_j |v_j| / L, plus bf16 rounding, where w_j are the exact
+ * softmax weights and L = sum_j exp(s_j - max s) >= 1 (each weight is off
+ * by at most 2^-4 of itself, or 2^-10 below e4m3fn's normal range).  LSE is
+ * as accurate as fa_fwd_ex's.
+ * Inputs must hold no NaN bytes (0x7f, 0xff); the result for
+ * them is unspecified.
+ * Strides must be multiples of 16 elements; pointers 16-byte aligned.
+ * scale * q_descale * k_descale must be finite in fp32.  There is no
+ * backward for fp8. */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+               int window_left, int window_right, float q_descale, float k_descale, float v_descale,
+               const int64_t q_strides[3], const int64_t k_strides[3],
+               const int64_t v_strides[3], const int64_t o_strides[3],
+               void* stream);
+
 /* Bytes of device workspace fa_bwd needs for these sizes (0 if the sizes are
  * invalid).  Holds two fp32 row statistics per (b, h): -D_i = -sum_d dO_i O_i
  * and lse_i * log2(e), each with its rows padded to a multiple of 64
@@ -191,7 +226,7 @@ const char* fa_status_string(int status);
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* fa_last_error_message(void);
 
-/* Library ABI version, currently 1. */
+/* Library ABI version, currently 3 (3 added fa_fwd_fp8). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

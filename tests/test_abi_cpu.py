@@ -46,7 +46,7 @@ def test_exported_dynamic_symbols_are_c_names():
 
 
 def test_status_strings_and_version():
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
     assert fa.fa_status_string(0) == "FA_OK"
     assert fa.fa_status_string(1) == "FA_ERR_INVALID_ARG"
     assert fa.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
@@ -240,3 +240,56 @@ def test_ex_rejects_bad_dropout(p):
 def test_ex_accepts_dropout(p):
     assert fwd_ex(dropout=p) == fa.FA_ERR_DEVICE
     assert bwd_ex(dropout=p) == fa.FA_ERR_DEVICE
+
+
+# --- fp8 forward (fa_fwd_fp8) ---------------------------------------------------
+
+def fwd_fp8(H=4, Hkv=2, Nq=16, Nk=16, d=64, scale=0.125, descale=(1.0, 1.0, 1.0), sq=None, sk=None, so=None,
+            q=A, o=4 * A):
+    lib = fa.load_library()
+    I3 = ctypes.c_int64 * 3
+    sq = I3(*(sq or (H * Nq * d, Nq * d, d)))
+    sk = I3(*(sk or (Hkv * Nk * d, Nk * d, d)))
+    so = I3(*(so or (H * Nq * d, Nq * d, d)))
+    return lib.fa_fwd_fp8(P(q), P(2 * A), P(3 * A), P(o), P(5 * A), 1, H, Hkv, Nq, Nk, d, scale, 1, -1, -1,
+                          *descale, sq, sk, sk, so, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(H=4, Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(descale=(1.0, float("inf"), 1.0)), fa.FA_ERR_INVALID_ARG),
+    (dict(descale=(float("nan"), 1.0, 1.0)), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=1e30, descale=(1e10, 1e10, 1.0)), fa.FA_ERR_INVALID_ARG),
+    # fp8 rows must stay 16-byte aligned: strides in multiples of 16 bytes
+    (dict(sq=(4 * 16 * 64, 16 * 64, 72)), fa.FA_ERR_INVALID_ARG),
+    (dict(sk=(2 * 16 * 64, 16 * 64 + 8, 64)), fa.FA_ERR_INVALID_ARG),
+    (dict(q=A + 8), fa.FA_ERR_INVALID_ARG),
+    # o is bf16: 8-element strides are fine there, 4 are not
+    (dict(so=(4 * 16 * 64, 16 * 64, 68)), fa.FA_ERR_INVALID_ARG),
+    # o overlapping q (q's extent counted in bytes)
+    (dict(o=A + 4 * 16 * 64 - 16), fa.FA_ERR_INVALID_ARG),
+])
+def test_fwd_fp8_rejects(kw, code):
+    assert fwd_fp8(**kw) == code
+
+
+def test_fwd_fp8_empty_is_ok():
+    assert fwd_fp8(Nq=0) == fa.FA_OK
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful where no HIP device exists")
+@pytest.mark.parametrize("kw", [dict(), dict(d=128), dict(sq=(4 * 16 * 80, 16 * 80, 80)),
+                                dict(o=A + 4 * 16 * 64), dict(scale=-0.5, descale=(2.0, -3.0, 0.25))])
+def test_fwd_fp8_valid_call_reaches_device_check(kw):
+    assert fwd_fp8(**kw) == fa.FA_ERR_DEVICE
+
+
+def test_python_fp8_binding_checks_dtypes():
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(fa.FaError) as e:
+        fa.attention_fwd_fp8(q, q, q)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED

@@ -1,0 +1,163 @@
+"""GPU parity of the fp8 (e4m3fn) forward (fa_fwd_fp8) against the fp64 oracle.
+
+The kernel rounds the attention weights to e4m3fn for the P V product, so O
+is compared with the exact attention of the decoded inputs under the
+tolerance that rounding implies (oracle ``fp8_rounding_model``):
+
+* every element within the rigorous bound, and
+* the mean of (error / model standard deviation)^2 at most 1.5 (the model
+  is an upper bound in expectation; wrong keys, values or rounding push it
+  far higher).
+
+LSE uses the 16-bit path's tolerance (1e-3): the scores are exact fp8
+products accumulated in fp32.  A second family of cases has integer scores
+and scale ln 2, so every weight is a power of two that e4m3fn holds exactly;
+there O must match the oracle to bf16 rounding (2^-8 relative).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_02_amd as fa
+from attn_inputs import fp8_bytes, make_qkv, sample_rows, to_bhsd64
+from oracle import attention_fp8_fwd64, attention_fp8_rows_fwd64, fp8_rounding_model
+
+pytestmark = pytest.mark.gpu
+
+TOL_LSE = 1e-3
+TOL_Z2 = 1.5
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def check(name, got_o, got_l, o_ref, lse_ref, bound, sigma):
+    live = np.isfinite(lse_ref)
+    assert np.isfinite(got_o).all()
+    np.testing.assert_array_equal(np.isneginf(got_l), ~live)
+    err = got_o - o_ref
+    ratio = np.abs(err) / np.where(bound > 0, bound, 1e-30)
+    livem = np.broadcast_to(live[..., None], err.shape)
+    # sigma = 0 where nothing can round (one admitted key whose value is 0)
+    flat = livem & (sigma == 0)
+    assert np.all(err[flat] == 0.0)
+    sm = livem & (sigma > 0)
+    z2 = np.mean((err[sm] / sigma[sm]) ** 2) if sm.any() else 0.0
+    err_l = np.abs(got_l[live] - lse_ref[live]).max() if live.any() else 0.0
+    say("  %s: O max-abs %.3e, max err/bound %.3f, mean z^2 %.3f; LSE max-abs %.3e"
+        % (name, np.abs(err).max(), ratio.max(), z2, err_l))
+    assert np.all(got_o[~livem] == 0.0)
+    assert ratio.max() <= 1.0
+    assert z2 <= TOL_Z2
+    assert err_l <= TOL_LSE
+
+
+CASES = [
+    # name, B, H, Hkv, Nq, Nk, d, layout, causal, window, descale, scale
+    ("d64", 1, 2, 2, 256, 256, 64, "bhsd", False, None, (1.0, 1.0, 1.0), None),
+    ("d128_causal", 1, 4, 4, 333, 333, 128, "bhsd", True, None, (1.0, 1.0, 1.0), None),
+    ("ragged_bshd", 2, 4, 4, 200, 300, 64, "bshd", False, None, (1.0, 1.0, 1.0), None),
+    ("gqa_causal_d128", 1, 8, 2, 257, 257, 128, "bhsd", True, None, (1.0, 1.0, 1.0), None),
+    ("mqa_window", 1, 4, 1, 400, 400, 64, "bhsd", False, (64, 32), (1.0, 1.0, 1.0), None),
+    ("win_causal_d128_bshd", 1, 2, 2, 700, 700, 128, "bshd", True, (100, -1), (1.0, 1.0, 1.0), None),
+    ("empty_rows_window", 1, 2, 2, 300, 100, 64, "bhsd", False, (10, 10), (1.0, 1.0, 1.0), None),
+    ("descales_negative_product", 1, 2, 2, 190, 190, 128, "bhsd", False, None, (0.5, -2.0, 3.0), None),
+    ("large_scale_rescales", 1, 2, 2, 320, 320, 64, "bhsd", True, None, (1.0, 1.0, 1.0), 1.5),
+    ("one_key", 1, 2, 2, 5, 1, 64, "bhsd", False, None, (1.0, 1.0, 1.0), None),
+    ("one_tile", 1, 2, 1, 64, 64, 128, "bhsd", True, None, (1.0, 1.0, 0.5), None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fp8_fwd_matches_oracle(case):
+    name, B, H, Hkv, Nq, Nk, d, layout, causal, window, descale, scale = case
+    say("case %s" % name)
+    inp = make_qkv(B, H, Nq, Nk, d, "fp8", layout, seed=88, Hkv=Hkv)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    o, lse = fa.attention_fwd_fp8(q, k, v, causal=causal, scale=scale, layout=layout, window=window,
+                                  descale=descale)
+    torch.cuda.synchronize()
+    w = window if window is not None else (-1, -1)
+    q8, k8, v8 = (fp8_bytes(inp[x], layout) for x in ("q", "k", "v"))
+    o_ref, lse_ref = attention_fp8_fwd64(q8, k8, v8, scale, causal, window=w, descale=descale)
+    rows = np.tile(np.arange(Nq), (B, H, 1))
+    bound, sigma = fp8_rounding_model(q8, k8, v8, scale, causal, rows, window=w, descale=descale)
+    check(name, to_bhsd64(o.cpu(), layout), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, bound, sigma)
+
+
+def integer_score_inputs(B, H, Hkv, Nq, Nk, d, seed):
+    """q rows with four entries of +-1, k entries in {-1, 0, 1}: every score
+    q.k is an integer in [-4, 4]; v random e4m3fn."""
+    rng = np.random.default_rng(seed)
+    q = np.zeros((B, H, Nq, d), dtype=np.float32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Nq):
+                pos = rng.choice(d, size=4, replace=False)
+                q[b, h, i, pos] = rng.choice([-1.0, 1.0], size=4)
+    k = rng.choice(np.array([-1.0, 0.0, 0.0, 1.0], dtype=np.float32), size=(B, Hkv, Nk, d))
+    v = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    return [torch.from_numpy(x).to(torch.float8_e4m3fn) for x in (q, k, v)]
+
+
+@pytest.mark.parametrize("d,causal,Hkv", [(64, False, 2), (128, True, 2), (128, False, 1), (64, True, 4)])
+def test_fp8_fwd_exact_weights(d, causal, Hkv):
+    """scale * q_descale * k_descale = ln 2 makes each weight 2^(n - m) with
+    integers n, m in [-4, 4]: exact in e4m3fn, so only fp32 accumulation and
+    the bf16 output round."""
+    B, H, Nq, Nk = 1, 4, 320, 333
+    say("case exact_weights d=%d causal=%d Hkv=%d" % (d, causal, Hkv))
+    q, k, v = integer_score_inputs(B, H, Hkv, Nq, Nk, d, seed=d + Hkv)
+    descale = (0.5, 4.0, 1.0)
+    scale = math.log(2.0) / (descale[0] * descale[1])
+    o, lse = fa.attention_fwd_fp8(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale, descale=descale)
+    torch.cuda.synchronize()
+    q8, k8, v8 = (fp8_bytes(x) for x in (q, k, v))
+    o_ref, lse_ref = attention_fp8_fwd64(q8, k8, v8, scale, causal, descale=descale)
+    got = o.cpu().to(torch.float64).numpy()
+    err = np.abs(got - o_ref)
+    tol = 2.0 ** -8 * np.abs(o_ref) + 1e-4
+    say("  O max err/tol %.3f, LSE max-abs %.3e" % ((err / tol).max(), np.abs(lse.cpu().numpy() - lse_ref).max()))
+    assert np.all(err <= tol)
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= TOL_LSE
+
+
+def test_fp8_fwd_16k_causal_sampled_rows():
+    """The 16K-token causal d=128 shape (B=1, H=16, inputs 0.5 N(0,1) cast to
+    e4m3fn) in the launch the benchmark times, checked on sampled rows."""
+    B, H, N, d = 1, 16, 16384, 128
+    say("case fp8_16k_causal (sampled rows)")
+    inp = make_qkv(B, H, N, N, d, "fp8", "bhsd", seed=3, in_scale=0.5)
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd_fp8(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(B, H, N, 12, seed=5)
+    q8, k8, v8 = (fp8_bytes(inp[x]) for x in ("q", "k", "v"))
+    o_ref, lse_ref = attention_fp8_rows_fwd64(q8, k8, v8, scale, True, rows)
+    bound, sigma = fp8_rounding_model(q8, k8, v8, scale, True, rows)
+    got_o = o.cpu().to(torch.float64).numpy()
+    got_l = lse.cpu().numpy().astype(np.float64)
+    go = np.stack([np.stack([got_o[0, h][rows[0, h]] for h in range(H)])])
+    gl = np.stack([np.stack([got_l[0, h][rows[0, h]] for h in range(H)])])
+    check("16k", go, gl, o_ref, lse_ref, bound, sigma)
+
+
+def test_fp8_fwd_gqa_equals_repeated_heads():
+    """Sharing a K/V head gives bit-for-bit the result of repeating it."""
+    say("case fp8_gqa_vs_repeat")
+    inp = make_qkv(1, 8, 300, 300, 128, "fp8", "bhsd", seed=9, Hkv=2)
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    o1, l1 = fa.attention_fwd_fp8(q, k, v, causal=True)
+    kr = k.view(torch.uint8).repeat_interleave(4, dim=1).view(torch.float8_e4m3fn)
+    vr = v.view(torch.uint8).repeat_interleave(4, dim=1).view(torch.float8_e4m3fn)
+    o2, l2 = fa.attention_fwd_fp8(q, kr, vr, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
