@@ -7,13 +7,19 @@
 //   S^T = K_j Q^T      A = K rows from LDS (32 bytes of d per lane), B = Q
 //                      held in registers; scores scaled by
 //                      scale * q_descale * k_descale.
-//   online softmax     as the 16-bit kernel (running max in log2 units,
-//                      lazy rescale by 2^8, fp32 row sums of the unrounded
-//                      weights).
-//   O^T += V_j^T P^T   P (<= 2^8, inside e4m3's range) rounded to e4m3fn
-//                      with v_cvt_pk_fp8_f32 straight from the S^T
-//                      accumulator into the B operand; V^T read from the
-//                      untransposed V tile with ds_read_b64_tr_b8.
+//   online softmax     running max m in log2 units, weights
+//                      P = 2^(S c - m) formed against m as it stands and
+//                      only re-formed after raising m when some weight
+//                      might exceed 448 (e4m3fn's largest value); fp32 row
+//                      sums of the unrounded weights.
+//   O^T += V_j^T P^T   P rounded to e4m3fn with v_cvt_pk_fp8_f32 straight
+//                      from the S^T accumulator into the B operand; V^T
+//                      read from the untransposed V tile with
+//                      ds_read_b64_tr_b8.
+//
+// Software pipeline: step j issues the PV MFMAs of tile j-1 and the QK
+// MFMAs of tile j+1 among the exponentials of tile j, so one wave keeps
+// its matrix core fed from its own instruction stream.
 //
 // O = O^T * v_descale / l in bf16, LSE fp32.  One workgroup of 4 waves owns
 // 128 queries (32 per wave, a query per lane); key tiles of 64 stream
@@ -91,44 +97,76 @@ __device__ __forceinline__ i32x2 lds_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
 }
 
-// One K/V tile.  The __restrict__ tile pointers keep the compiler from
-// waiting for the in-flight copy into another slot before reading these.
-template <int D, bool BAND>
-__device__ __forceinline__ void fwd8_tile(int j, int n_kt, const uint8_t* __restrict__ Kt,
-                                          const uint8_t* __restrict__ Vt, uint8_t* __restrict__ Kdst,
-                                          uint8_t* __restrict__ Vdst, __amdgpu_buffer_rsrc_t krs,
-                                          __amdgpu_buffer_rsrc_t vrs, uint32_t krow, uint32_t vrow,
-                                          const i32x8 (&qf)[D / 64], f32x16 (&acc)[D / 32], float& m, float& l,
-                                          int Nk, int wl, int wr, int qw0, float c, int lane, int wave) {
-  using TC = Tile8Copy<D>;
-  constexpr int KS = D / 64;
-  constexpr int DB = D / 32;
-  const int j0 = j * kBN8;
-  const int col = lane & 31, half = lane >> 5;
-  const int qi = qw0 + col;
-
-  if (j + 3 < n_kt) {
-    TC::issue(krs, krow, (uint32_t)(j + 3) * kBN8 * krow, Kdst, lane, wave);
-    TC::issue(vrs, vrow, (uint32_t)(j + 3) * kBN8 * vrow, Vdst, lane, wave);
+// Per-lane LDS byte offsets within one tile slot.  K operand: row col
+// (+32 per key block, which keeps the swizzle), bytes 64 ks + 32 half + 16 hl.
+// V^T operand (transposing reads): the lane's row for read u = 0 (+16 rows
+// per u, again swizzle-invariant), columns 32 db + 16 (g % 2) + 8 (lane % 2).
+template <int D>
+struct Tile8Addr {
+  int k[D / 64][2];
+  int v[D / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl) k[ks][hl] = off8<D>(col, 64 * ks + 32 * half + 16 * hl);
+    const int g = lane >> 4, pl = lane & 15, je = pl >> 1;
+    const int row = 8 * (je >> 2) + 4 * (g >> 1) + (je & 3);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) v[db] = off8<D>(row, 32 * db + 16 * (g & 1) + 8 * (pl & 1));
   }
+};
 
-  // ---- S^T = K Q^T for keys j0 + 32 mb + acc_row(half, r)
-  f32x16 s[2];
+// The A operands of S^T = K Q^T for one K tile: [key block][k step].
+template <int D>
+__device__ __forceinline__ void load_k8(const uint8_t* __restrict__ Kt, const Tile8Addr<D>& ta,
+                                        i32x8 (&ka)[2][D / 64]) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) {
+      const u32x4 lo = lds16(Kt, ta.k[ks][0] + 32 * mb * D);
+      const u32x4 hi = lds16(Kt, ta.k[ks][1] + 32 * mb * D);
+      ka[mb][ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                         (int)hi[3]};
+    }
+}
+
+// S^T (64 keys x 32 queries, two 32-key blocks) from loaded K operands.
+template <int D>
+__device__ __forceinline__ void scores8(const i32x8 (&ka)[2][D / 64], const i32x8 (&qf)[D / 64], f32x16 (&s)[2]) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     s[mb] = f32x16{};
-    const int row = 32 * mb + col;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 lo = lds16(Kt, off8<D>(row, 64 * ks + 32 * half));
-      const u32x4 hi = lds16(Kt, off8<D>(row, 64 * ks + 32 * half + 16));
-      const i32x8 a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
-                            (int)hi[3]};
-      s[mb] = mfma_fp8(a, qf[ks], s[mb]);
-    }
+    for (int ks = 0; ks < D / 64; ++ks) s[mb] = mfma_fp8(ka[mb][ks], qf[ks], s[mb]);
   }
+}
 
-  // ---- masks
+// The A operands of O^T += V^T P^T for one V tile, per 32-wide d block:
+// slot 8u + e of a lane holds key 32(u/2) + 16(u%2) + 8(e/4) + 4 half + e%4.
+template <int D>
+__device__ __forceinline__ void load_v8(const uint8_t* __restrict__ Vt, const Tile8Addr<D>& ta,
+                                        i32x8 (&va)[D / 32]) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const i32x2 t = lds_tr8(Vt + ta.v[db] + 16 * u * D);
+      va[db][2 * u] = t[0];
+      va[db][2 * u + 1] = t[1];
+    }
+}
+
+constexpr float kP8Max = 448.0f;  // largest finite e4m3fn
+
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+
+// -inf for the scores of tile j that query qi does not admit (only tiles
+// crossing the key tail or an edge of this wave's band).
+template <bool BAND>
+__device__ __forceinline__ void mask8(f32x16 (&s)[2], int j0, int Nk, int wl, int wr, int qw0, int qi, int half) {
   if ((j0 + kBN8 > Nk) ||
       (BAND && ((wr >= 0 && j0 + kBN8 - 1 > qw0 + wr) || (wl >= 0 && j0 < qw0 + kQW8 - 1 - wl)))) {
 #pragma unroll
@@ -140,67 +178,172 @@ __device__ __forceinline__ void fwd8_tile(int j, int n_kt, const uint8_t* __rest
           s[mb][r] = -__builtin_inff();
       }
   }
+}
 
-  // ---- online softmax
-  float mx = s[0][0];
+// One step of the software-pipelined loop, for tile j:
+//
+//   O^T += V_{j-1}^T P_{j-1}^T   (P and the V operands carried in registers
+//                                 from the previous step)
+//   P_j = 2^(S_j c - m)          (VALU)
+//   S_{j+1} = K_{j+1} Q^T        (into the registers of S_j once read)
+//
+// The eight MFMAs are spread through the ~100 VALU instructions of the
+// weights, so a wave keeps its matrix core busy while it issues its own
+// exponentials; the other wave on the SIMD fills the gaps.  Slot t mod 4
+// of the ring holds tile jt0 + t; the step fills the slot of tile j+3
+// (that of tile j-1, whose V operands are already in registers).
+//
+// The weights are formed against the running maximum m as it stands.  Only
+// if some lane's sum of its 16 weights of a row exceeds 448 (a weight
+// might not fit e4m3fn), or m is unset (m = -1e30 makes every admitted
+// weight +inf), does the wave take the slow path: S_j again from K_j
+// (still in its slot), row maximum, raise m, rescale O^T (which by then
+// holds V_{j-1} P_{j-1}) and l, weights again.  So m never lags the row
+// maximum by more than log2(448) and the fast path needs no maximum.
+template <int D, bool BAND, bool FIRST>
+__device__ __forceinline__ void fwd8_step(int j, int n_kt, f32x16 (&s)[2], i32x8& pf, i32x8 (&va)[D / 32],
+                                          const uint8_t* __restrict__ Kj, const uint8_t* __restrict__ Kn,
+                                          const uint8_t* __restrict__ Vj, uint8_t* __restrict__ Kdst,
+                                          uint8_t* __restrict__ Vdst, __amdgpu_buffer_rsrc_t krs,
+                                          __amdgpu_buffer_rsrc_t vrs, uint32_t krow, uint32_t vrow,
+                                          const i32x8 (&qf)[D / 64], f32x16 (&acc)[D / 32], float& m, float& l,
+                                          int Nk, int wl, int wr, int qw0, float c, int lane, int wave,
+                                          const Tile8Addr<D>& ta) {
+  using TC = Tile8Copy<D>;
+  constexpr int DB = D / 32;
+  const int j0 = j * kBN8;
+  const int half = lane >> 5;
+  const int qi = qw0 + (lane & 31);
+
+  if (j + 3 < n_kt) {
+    TC::issue(krs, krow, (uint32_t)(j + 3) * kBN8 * krow, Kdst, lane, wave);
+    TC::issue(vrs, vrow, (uint32_t)(j + 3) * kBN8 * vrow, Vdst, lane, wave);
+  }
+  mask8<BAND>(s, j0, Nk, wl, wr, qw0, qi, half);
+
+  // K(j+1) operands (reading K(j+1) when j+1 = n_kt reads a stale slot
+  // whose scores are never used; it keeps the MFMAs in one block with the
+  // exponentials)
+  i32x8 ka[2][D / 64];
+  load_k8<D>(Kn, ta, ka);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The eight MFMAs, each followed by a share of the weights' VALU work, in
+  // chunks the scheduler may not reorder:
+  //   PV(j-1) per d block (operands ready), with the V(j) reads that
+  //   replace its operands and the weights of key block 0;
+  //   S(j+1) block 0 (s[0] is consumed), with the exponent arguments of all
+  //   of key block 1 and half its exponentials;
+  //   S(j+1) block 1 (s[1] is consumed), with the rest.
+  constexpr int KS = D / 64;
+  float p[2][16];
+  float x1[16];
+  float ls0 = 0.f, ls1 = 0.f;
+  const float mneg = -m;
+  auto w0 = [&](int r) {
+    p[0][r] = exp2_fast(__builtin_fmaf(s[0][r], c, mneg));
+    ls0 += p[0][r];
+  };
+  if constexpr (FIRST) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int r = 0; r < 16; ++r) w0(r);
+  } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-  const float mxc = max_pair32(mx) * c;
-  if (__any(mxc > m + 8.0f)) {
-    const float mnew = fmaxf(m, mxc);
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = mfma_fp8(va[db], pf, acc[db]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const i32x2 t = lds_tr8(Vj + ta.v[db] + 16 * u * D);
+        va[db][2 * u] = t[0];
+        va[db][2 * u + 1] = t[1];
+      }
+#pragma unroll
+      for (int r = db * (16 / DB); r < (db + 1) * (16 / DB); ++r) w0(r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    s[0] = ks == 0 ? mfma_fp8(ka[0][0], qf[0], f32x16{}) : mfma_fp8(ka[0][ks], qf[ks], s[0]);
+#pragma unroll
+    for (int r = ks * (16 / KS); r < (ks + 1) * (16 / KS); ++r) x1[r] = __builtin_fmaf(s[1][r], c, mneg);
+#pragma unroll
+    for (int r = ks * (8 / KS); r < (ks + 1) * (8 / KS); ++r) {
+      p[1][r] = exp2_fast(x1[r]);
+      ls1 += p[1][r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    s[1] = ks == 0 ? mfma_fp8(ka[1][0], qf[0], f32x16{}) : mfma_fp8(ka[1][ks], qf[ks], s[1]);
+#pragma unroll
+    for (int r = 8 + ks * (8 / KS); r < 8 + (ks + 1) * (8 / KS); ++r) {
+      p[1][r] = exp2_fast(x1[r]);
+      ls1 += p[1][r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (FIRST) {  // the V(j) operands, for the epilogue or the next step
+    load_v8<D>(Vj, ta, va);
+  }
+  float ls = ls0 + ls1;
+  if (__any(!(ls <= kP8Max))) {  // rare (also catches +inf and NaN sums)
+    asm volatile("" ::: "memory");
+    f32x16 so[2];
+    {
+      i32x8 kj[2][D / 64];
+      load_k8<D>(Kj, ta, kj);
+      scores8<D>(kj, qf, so);
+    }
+    mask8<BAND>(so, j0, Nk, wl, wr, qw0, qi, half);
+    float mx = so[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, so[mb][r]);
+    const float mnew = fmaxf(m, max_pair32(mx) * c);
     const float alpha = exp2_fast(m - mnew);
     m = mnew;
     l *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    const float mneg2 = -m;
+    ls = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[mb][r] = exp2_fast(__builtin_fmaf(so[mb][r], c, mneg2));
+        ls += p[mb][r];
+      }
   }
-  // P <= 2^8 (inside e4m3's 448), rounded into the B operand: byte 16 mb + r
-  // of the lane holds the key of accumulator register r of block mb
-  i32x8 pf;
-  const float mneg = -m;
+  l += ls;
+
+  // P_j rounded into the B operand: byte 16 mb + r holds the key of
+  // accumulator register r of block mb, matching load_v8's slots (both
+  // halves of each word are written, so the old contents pass through
+  // unused instead of a zeroed register)
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; r += 4) {
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = exp2_fast(__builtin_fmaf(s[mb][r + e], c, mneg));
-        l += p[e];
-      }
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][r], p[mb][r + 1], pf[4 * mb + r / 4], false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(p[mb][r + 2], p[mb][r + 3], w, true);
       pf[4 * mb + r / 4] = w;
     }
+  // the V reads must have left LDS before the barrier, after which tile
+  // j+4 may land in the slot
+  wait_lds_reads();
 
-  // ---- O^T += V^T P^T: slot 8u + e of a lane holds key
-  // 32(u/2) + 16(u%2) + 8(e/4) + 4 half + e%4, the key P's byte 8u + e holds
-  const int g = lane >> 4, pl = lane & 15, je = pl >> 1;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    i32x8 a;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = 32 * (u >> 1) + 16 * (u & 1) + 8 * (je >> 2) + 4 * half + (je & 3);
-      const int cb = 32 * db + 16 * (g & 1) + 8 * (pl & 1);
-      const i32x2 t = lds_tr8(Vt + off8<D>(row, cb));
-      a[2 * u] = t[0];
-      a[2 * u + 1] = t[1];
-    }
-    acc[db] = mfma_fp8(a, pf, acc[db]);
-  }
-
-  // tile j+1 must have landed; the later ones fly on
+  // tile j+2 must have landed (its K is read next step); tile j+3 may fly on
   if (j + 3 < n_kt) {
-    wait_vmcnt<4 * TC::NI>();
-  } else if (j + 2 < n_kt) {
     wait_vmcnt<2 * TC::NI>();
   } else {
     wait_loads();
   }
   lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D, bool BAND>
@@ -261,8 +404,8 @@ __global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int t0 = 0; t0 < 3; ++t0) {
     const int jj = jt0 + t0;
     if (jj < n_kt) {
-      TC::issue(krs, krow, (uint32_t)jj * kBN8 * krow, sm.k[jj & 3], lane, wave);
-      TC::issue(vrs, vrow, (uint32_t)jj * kBN8 * vrow, sm.v[jj & 3], lane, wave);
+      TC::issue(krs, krow, (uint32_t)jj * kBN8 * krow, sm.k[t0], lane, wave);
+      TC::issue(vrs, vrow, (uint32_t)jj * kBN8 * vrow, sm.v[t0], lane, wave);
     }
   }
   f32x16 acc[DB];
@@ -270,10 +413,11 @@ __global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m = -1e30f, l = 0.f;
   const float c = p.c;
+  Tile8Addr<D> ta;
+  ta.init(lane);
 
+  // tiles jt0 and jt0+1 landed (S(jt0) now, V(jt0) and K(jt0+1) in the first step)
   if (n_kt - jt0 > 2) {
-    wait_vmcnt<4 * TC::NI>();
-  } else if (n_kt - jt0 > 1) {
     wait_vmcnt<2 * TC::NI>();
   } else {
     wait_loads();
@@ -282,10 +426,26 @@ __global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int ks = 0; ks < KS; ++ks) qf[ks] ^= (int)p.qflip;
   lds_barrier();
 
-  for (int j = jt0; j < n_kt; ++j) {
-    const int sl = j & 3;
-    fwd8_tile<D, BAND>(j, n_kt, sm.k[sl], sm.v[sl], sm.k[(sl + 3) & 3], sm.v[(sl + 3) & 3], krs, vrs, krow, vrow,
-                       qf, acc, m, l, p.Nk, p.wl, p.wr, qw0, c, lane, wave);
+  // Tile jt0 + t lives in slot t mod 4.
+  if (jt0 < n_kt) {
+    f32x16 sa[2];
+    i32x8 pf = i32x8{};
+    i32x8 va[DB];
+    {
+      i32x8 ka[2][KS];
+      load_k8<D>(sm.k[0], ta, ka);
+      scores8<D>(ka, qf, sa);
+    }
+    fwd8_step<D, BAND, true>(jt0, n_kt, sa, pf, va, sm.k[0], sm.k[1], sm.v[0], sm.k[3], sm.v[3], krs, vrs, krow,
+                             vrow, qf, acc, m, l, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta);
+    for (int j = jt0 + 1; j < n_kt; ++j) {
+      const int sl = (j - jt0) & 3;
+      fwd8_step<D, BAND, false>(j, n_kt, sa, pf, va, sm.k[sl], sm.k[(sl + 1) & 3], sm.v[sl], sm.k[(sl + 3) & 3],
+                                sm.v[(sl + 3) & 3], krs, vrs, krow, vrow, qf, acc, m, l, p.Nk, p.wl, p.wr, qw0, c,
+                                lane, wave, ta);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = mfma_fp8(va[db], pf, acc[db]);
   }
 
   // ---- epilogue: O = O^T * v_descale / l in bf16, LSE

@@ -133,10 +133,10 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
  *     the descaled inputs; lse: fp32 [B][H][Nq] natural log as fa_fwd_ex.
  *   H_kv, causal, window_left, window_right: as fa_fwd_ex; no dropout.
  * Arithmetic: Q K^T on the fp8 matrix cores with fp32 accumulation; the
- * softmax in fp32; the weights p_j = exp(s_j - m) (each <= 2^8, the running
- * maximum m lagging the row maximum by at most 8 in log2 units) rounded to
- * e4m3fn (nearest even) for the P V product, the normaliser l summed from
- * the unrounded weights in fp32.  Rounding the weights dominates the
+ * softmax in fp32; the weights p_j = exp(s_j - m) (each <= 448, the
+ * running maximum m lagging the row maximum by at most log2(448) in log2
+ * units) rounded to e4m3fn (nearest even) for the P V product, the
+ * normaliser l summed from the unrounded weights in fp32.  Rounding the weights dominates the
  * error: per element of O, |error| <= 2^-4 sum_j w_j |v_j| +
  * 2^-10 sum_j |v_j| / L, plus bf16 rounding, where w_j are the exact
  * softmax weights and L = sum_j exp(s_j - max s) >= 1 (each weight is off

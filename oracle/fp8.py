@@ -69,7 +69,7 @@ def fp8_rounding_model(q8, k8, v8, scale, causal, rows, window=(-1, -1), descale
     to e4m3fn adds to O, per element of the query rows ``rows`` [B, H, R].
 
     The fp8 forward forms p_j = 2^(c s_j - m) with a running maximum m
-    (m <= the row maximum and m >= it minus 8 in log2 units), rounds p_j to
+    (m <= the row maximum, and p_j <= 448), rounds p_j to
     e4m3fn (round to nearest even) for the P V product and divides by
     l = sum_j p_j of the unrounded weights.  Writing L = sum_j exp(s_j -
     s_max) >= 1 and w_j = exp(s_j - s_max) / L (the exact weights):

@@ -135,7 +135,7 @@ def emulate_fp8_weights(q8, k8, v8, scale, causal, lag, window=(-1, -1)):
     return out
 
 
-@pytest.mark.parametrize("lag", [0.0, 2.5, 7.9])
+@pytest.mark.parametrize("lag", [0.0, 2.5, 8.7])
 @pytest.mark.parametrize("causal", [False, True])
 def test_error_model_bounds_emulated_rounding(lag, causal):
     q8, k8, v8 = fp8_inputs(1, 2, 1, 64, 300, 64)
