@@ -13,21 +13,24 @@
 //                          then holds 16 keys x 1 query of every 32x32
 //                          block, so the row max and sum are in-lane plus
 //                          one exchange with lane i^32.
-//   online softmax         m' = max(m, max_j S*c) with c = |scale| log2 e;
-//                          P = 2^(S*c - m); l += sum P; O^T *= 2^(m - m').
-//                          The running max is only raised (and O^T, l
-//                          rescaled) when some row's tile max exceeds it by
-//                          more than 2^8; otherwise P <= 2^8 is computed
-//                          against the stale max, which changes no result
-//                          (O = O^T / l uses the same m in both).
+//   online softmax         P = 2^(S*c - m) with c = |scale| log2 e against
+//                          the running max m as it stands; l += sum P.
+//                          Only when some lane's sum of its 16 weights of a
+//                          row exceeds 2^15 (or m is unset) is m raised to
+//                          the row max and O^T, l rescaled by 2^(m - m');
+//                          a stale m changes no result (O = O^T / l uses
+//                          the same m in both) and needs no per-element
+//                          maximum.
 //   O^T += V_j^T P^T       A = V^T via ds_read_b64_tr_b16 from the
 //                          untransposed V tile; B = P^T repacked in place
 //                          from the S^T accumulator (no LDS round trip).
 //
-// The loop is software pipelined: the MFMAs for S of tile j+1 are issued
-// among the exponentials of tile j, so the matrix core and the VALU of a
-// SIMD work at the same time within one wave (the overlap FA3 gets from
-// asynchrony on Hopper, glossary article's FA-3 section).
+// Software pipeline: step j issues the PV MFMAs of tile j-1 and the S
+// MFMAs of tile j+1 among the exponentials of tile j, in chunks the
+// scheduler keeps in order, so one wave's matrix core and VALU work at the
+// same time (the overlap FA3 gets from asynchrony on Hopper, glossary
+// article's FA-3 section).  The V operands and P of tile j-1 stay in
+// registers across the step boundary.
 //
 // Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2 (O = 0, LSE = -inf for
 // a row that admits no key).  Masks: query i admits keys i - wl .. i + wr
@@ -60,8 +63,10 @@ struct FwdTile {
   static constexpr int QW = 32 * NQB;       // queries per wave
   static constexpr int BM = kWaves * QW;    // queries per workgroup
   static constexpr int WAVES_PER_SIMD = 2;
+  // S(j+1) in registers of its own (d = 128; at d = 64 the two query
+  // blocks leave no room, so S(j+1) overwrites S(j) after the weights)
+  static constexpr bool SEP_S = D == 128;
 };
-constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 template <int D>
 using TileCopy = TileCopyT<D, kBN, kWaves>;
@@ -84,36 +89,11 @@ struct RowState {
   float l[kNQB];  // this lane's partial row sum (lane i^32 holds the rest)
 };
 
-// One step of the software-pipelined loop: tile j's softmax and O += P V,
-// while the MFMAs form S for tile j+1 into `sn`.  A wave's issue stream
-// alternates those independent MFMAs with the exponentials of tile j, so
-// the matrix core and the VALU of one SIMD stay busy together even without
-// the other wave's help.  The LDS ring has four slots (tile t in slot
-// t mod 4): step j reads K(j+1) and V(j) and fills slot (j+3) mod 4.
-// The __restrict__ tile pointers tell the compiler the reads never alias
-// the in-flight copy, so it does not wait for that copy before reading;
-// the vmcnt wait and barrier at the end order the ring.
-template <int D, int DT, bool BAND, bool DROP, int kNQB = FwdTile<D>::NQB>
-__device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32x16 (&sn)[kNQB],
-                                         const uint16_t* __restrict__ Kn, const uint16_t* __restrict__ Vt,
-                                         uint16_t* __restrict__ Kdst, uint16_t* __restrict__ Vdst,
-                                         __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, uint32_t krow,
-                                         uint32_t vrow, uint32_t ktb, uint32_t vtb, const u32x4 (&qf)[kNQB][D / 16],
-                                         f32x16 (&acc)[D / 32][kNQB], RowState<kNQB>& st, int Nk, int wl, int wr, int qw0, float c,
-                                         int lane, int wave, const TileAddr<D>& ta, const DropoutParams& dp,
-                                         uint32_t bh) {
-  using TC = TileCopy<D>;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  const int j0 = j * kBN;
-  const int col = lane & 31, half = lane >> 5;
-
-  if (j + 3 < n_kt) {
-    TC::issue(krs, krow, (uint32_t)(j + 3) * ktb, Kdst, lane, wave);
-    TC::issue(vrs, vrow, (uint32_t)(j + 3) * vtb, Vdst, lane, wave);
-  }
-
-  // ---- masks (only tiles crossing the key tail or an edge of this wave's band)
+// -inf for the scores of tile j (keys j0 ..) that a query does not admit
+// (only tiles crossing the key tail or an edge of this wave's band).
+template <bool BAND, int kNQB>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[kNQB], int j0, int Nk, int wl, int wr, int qw0, int col,
+                                          int half) {
   constexpr int QW = 32 * kNQB;
   if ((j0 + kBN > Nk) ||
       (BAND && ((wr >= 0 && j0 + kBN - 1 > qw0 + wr) || (wl >= 0 && j0 < qw0 + QW - 1 - wl)))) {
@@ -128,95 +108,261 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
       }
     }
   }
-  // ---- row max; lazy rescale
-  float mxc[kNQB];
-  bool raise = false;
+}
+
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+
+// Weights of tile j: P = 2^(S c - m) against the running maximum as it
+// stands, the normaliser's partial sums (of the undropped weights),
+// dropout, and the packing into the MFMA B operand, one packed word (two
+// keys of one query block) at a time: word w = 4 kk + e of block nb holds
+// accumulator registers 8 kk + 2 e and +1.
+template <int DT, bool DROP>
+__device__ __forceinline__ uint32_t weight_word(const f32x16& s, int w, float c, float mneg, float (&ls)[2],
+                                                const u32x4& rnd, uint32_t thr) {
+  const int r = 2 * w;
+  float p0 = exp2_fast(__builtin_fmaf(s[r], c, mneg));
+  float p1 = exp2_fast(__builtin_fmaf(s[r + 1], c, mneg));
+  if constexpr (DT == DT_BF16 || DROP) {  // bf16 rounding (2^-9) is too coarse for the normaliser
+    ls[0] = r == 0 ? p0 : ls[0] + p0;
+    ls[1] = r == 0 ? p1 : ls[1] + p1;
+  }
+  if constexpr (DROP) {  // register r holds key 8*(r/4) + 4*half + r%4 of the tile
+    if (((rnd[r >> 2] >> (8 * (r & 3))) & 0xffu) < thr) p0 = 0.f;
+    if (((rnd[(r + 1) >> 2] >> (8 * ((r + 1) & 3))) & 0xffu) < thr) p1 = 0.f;
+  }
+  const uint32_t pw = pack2<DT>(p0, p1);
+  if constexpr (DT == DT_F16 && !DROP) {  // fp16-rounded P is accurate enough: sum pairs in one op
+    if (r == 0) ls[0] = ls[1] = 0.f;
+    ls[w & 1] = dot2_sum<DT>(pw, ls[w & 1]);
+  }
+  return pw;
+}
+
+template <int DT, bool DROP>
+__device__ __forceinline__ void weights(const f32x16& s, float c, float m, float (&ls)[2], u32x4 (&pfo)[2],
+                                        const u32x4& rnd, uint32_t thr) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) pfo[w >> 2][w & 3] = weight_word<DT, DROP>(s, w, c, -m, ls, rnd, thr);
+}
+
+constexpr float kLaneSumMax = 32768.0f;  // 2^15: each weight fits fp16 and bf16
+
+// One step of the software-pipelined loop, for tile j:
+//
+//   O^T += V_{j-1}^T P_{j-1}^T   (P and the V operands carried in registers
+//                                 from the previous step)
+//   P_j = 2^(S_j c - m)          (VALU)
+//   S_{j+1} = K_{j+1} Q^T        (into the registers of S_j once read)
+//
+// The MFMAs of both products are spread through the VALU work of the
+// weights in chunks the scheduler may not reorder, so one wave keeps its
+// matrix core fed from its own instruction stream (the overlap of
+// FA3's asynchrony, glossary article's FA-3 section, by scheduling).  The
+// LDS ring has four slots, tile jt0 + t in slot t mod 4; step j fills the
+// slot of tile j+3, that of tile j-1 whose V operands are already in
+// registers.  The __restrict__ tile pointers tell the compiler these reads
+// never alias the in-flight copy; the vmcnt wait and barrier at the end
+// order the ring.
+//
+// The weights are formed against the running maximum m as it stands.
+// Only if a lane's sum of its 16 weights of a row exceeds 2^15, or m is
+// unset (m = -1e30 makes every admitted weight +inf), does the wave take
+// the slow path: S_j again from K_j (still in its slot), row maximum,
+// raise m, rescale O^T (which by then holds V_{j-1} P_{j-1}) and l,
+// weights again.  The result is the same for any m (O = O^T / l uses one
+// m for both); m only keeps the weights in range.
+template <int D, int DT, bool BAND, bool DROP, bool FIRST, int kNQB = FwdTile<D>::NQB>
+__device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32x16 (&sn)[kNQB], u32x4 (&pf)[2][kNQB],
+                                         u32x4 (&va)[2][D / 32], const uint16_t* __restrict__ Kj,
+                                         const uint16_t* __restrict__ Kn, const uint16_t* __restrict__ Vj,
+                                         uint16_t* __restrict__ Kdst, uint16_t* __restrict__ Vdst,
+                                         __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, uint32_t krow,
+                                         uint32_t vrow, uint32_t ktb, uint32_t vtb, const u32x4 (&qf)[kNQB][D / 16],
+                                         f32x16 (&acc)[D / 32][kNQB], RowState<kNQB>& st, int Nk, int wl, int wr,
+                                         int qw0, float c, int lane, int wave, const TileAddr<D>& ta,
+                                         const DropoutParams& dp, uint32_t bh) {
+  using TC = TileCopy<D>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  const int j0 = j * kBN;
+  const int col = lane & 31, half = lane >> 5;
+
+  if constexpr (FwdTile<D>::SEP_S) {
+    // K(j) is no longer read (S(j) stays in registers), so K runs four
+    // tiles ahead: K(j+4) into K(j)'s slot, V(j+3) into V(j-1)'s
+    if (j + 4 < n_kt) TC::issue(krs, krow, (uint32_t)(j + 4) * ktb, Kdst, lane, wave);
+    if (j + 3 < n_kt) TC::issue(vrs, vrow, (uint32_t)(j + 3) * vtb, Vdst, lane, wave);
+  } else {
+    if (j + 3 < n_kt) {
+      TC::issue(krs, krow, (uint32_t)(j + 3) * ktb, Kdst, lane, wave);
+      TC::issue(vrs, vrow, (uint32_t)(j + 3) * vtb, Vdst, lane, wave);
+    }
+  }
+  mask_tile<BAND>(s, j0, Nk, wl, wr, qw0, col, half);
+
+  // K(j+1) operands (reading K(j+1) when j+1 = n_kt reads a stale slot
+  // whose scores are never used; it keeps the MFMAs in one block with the
+  // exponentials)
+  constexpr bool kSep = FwdTile<D>::SEP_S;
+  constexpr int kKLead = 2;  // with kSep, K(j+1) operands are read this many chunks ahead of use
+  u32x4 ka[KS];
+  if constexpr (!kSep || FIRST) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_b128(Kn, ta.rm[ks]);
+  }
+  u32x4 rnd[kNQB];
 #pragma unroll
   for (int nb = 0; nb < kNQB; ++nb) {
-    float mx = fmaxf(s[nb][0], s[nb][1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[nb][r]), s[nb][r + 1]);
-    mx = max_pair32(mx);
-    mxc[nb] = mx * c;
-    raise |= mxc[nb] > st.m[nb] + kRescaleSlack;
+    rnd[nb] = u32x4{0, 0, 0, 0};
+    if constexpr (DROP)  // this lane's 16 keys of tile j: one generator call
+      rnd[nb] = philox4x32_10(2u * (uint32_t)j + (uint32_t)half, (uint32_t)(qw0 + 32 * nb + col), bh, dp.offset,
+                              dp.seed_lo, dp.seed_hi);
   }
-  if (__any(raise)) {
+  __builtin_amdgcn_sched_barrier(0);
+
+  // PV(j-1) chunks, each with the V(j) reads that replace its operands and
+  // an equal share of the weights' packed words; then the S(j+1) MFMAs,
+  // which overwrite S(j) once every word has read it.
+  float ls[kNQB][2];
+  u32x4 pn[kNQB][2];
+  float mneg[kNQB];
+#pragma unroll
+  for (int nb = 0; nb < kNQB; ++nb) mneg[nb] = -st.m[nb];
+  constexpr int NW = 8 * kNQB;  // packed words per lane
+  // With room for it (d = 128: one wave per SIMD), S(j+1) goes to separate
+  // registers, so its MFMAs can share the weights' VALU work too: chunks of
+  // two MFMAs (PV first, then S) and one packed word each.
+  if constexpr (kSep && !FIRST) {
+    constexpr int NPVM = 2 * DB * kNQB, NSM = KS * kNQB, NCH = (NPVM + NSM) / 2;
+    constexpr int CPK = kNQB / 2 > 0 ? kNQB / 2 : 1;  // S chunks per k step (two MFMAs per chunk)
+    static_assert(NCH == NW, "one packed word per chunk");
+    static_assert(kNQB <= 2, "S chunk layout");
+#pragma unroll
+    for (int g = 0; g < NCH; ++g) {
+      {  // K(j+1) operand of k step ks, kKLead k steps ahead of its MFMAs
+        const int ks = (g - NPVM / 2) / CPK * (kNQB == 1 ? 2 : 1) + kKLead;
+        if ((g - NPVM / 2) % CPK == 0 && ks >= 0 && ks < KS) {
+          ka[ks] = lds_b128(Kn, ta.rm[ks]);
+          if (kNQB == 1 && ks + 1 < KS) ka[ks + 1] = lds_b128(Kn, ta.rm[ks + 1]);
+        }
+        if (g == NPVM / 2 - 1) {  // the first k steps
+#pragma unroll
+          for (int k0 = 0; k0 < kKLead && k0 < KS; ++k0) ka[k0] = lds_b128(Kn, ta.rm[k0]);
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int x = 2 * g + h2;
+        if (x < NPVM) {  // x = ((kk DB) + db) kNQB + nb
+          const int nb = x % kNQB, kd = x / kNQB, kk = kd / DB, db = kd % DB;
+          acc[db][nb] = mfma32<DT>(va[kk][db], pf[kk][nb], acc[db][nb]);
+          if (nb == kNQB - 1) va[kk][db] = lds_transposed_a<D>(Vj, ta, kk, db);
+        } else {  // y = ks kNQB + nb
+          const int y = x - NPVM, nb = y % kNQB, ks = y / kNQB;
+          sn[nb] = mfma32<DT>(ka[ks], qf[nb][ks], ks == 0 ? f32x16{} : sn[nb]);
+        }
+      }
+      const int nb = g / 8, w = g % 8;
+      pn[nb][w >> 2][w & 3] = weight_word<DT, DROP>(s[nb], w, c, mneg[nb], ls[nb], rnd[nb], dp.thr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if constexpr (!FIRST) {
+    constexpr int NPV = 2 * DB;
+    static_assert(NW % NPV == 0, "words per chunk");
+#pragma unroll
+    for (int g = 0; g < NPV; ++g) {
+      const int kk = g / DB, db = g % DB;
+#pragma unroll
+      for (int nb = 0; nb < kNQB; ++nb) acc[db][nb] = mfma32<DT>(va[kk][db], pf[kk][nb], acc[db][nb]);
+      va[kk][db] = lds_transposed_a<D>(Vj, ta, kk, db);
+#pragma unroll
+      for (int x = g * (NW / NPV); x < (g + 1) * (NW / NPV); ++x) {
+        const int nb = x / 8, w = x % 8;
+        pn[nb][w >> 2][w & 3] = weight_word<DT, DROP>(s[nb], w, c, mneg[nb], ls[nb], rnd[nb], dp.thr);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < kNQB; ++nb) weights<DT, DROP>(s[nb], c, st.m[nb], ls[nb], pn[nb], rnd[nb], dp.thr);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) va[kk][db] = lds_transposed_a<D>(Vj, ta, kk, db);
+  }
+  if constexpr (kSep && FIRST) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < kNQB; ++nb) sn[nb] = mfma32<DT>(ka[ks], qf[nb][ks], ks == 0 ? f32x16{} : sn[nb]);
+  } else if constexpr (!kSep) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int nb = 0; nb < kNQB; ++nb) s[nb] = mfma32<DT>(ka[ks], qf[nb][ks], ks == 0 ? f32x16{} : s[nb]);
+    }
+  }
+  bool raise = false;
+#pragma unroll
+  for (int nb = 0; nb < kNQB; ++nb) raise |= !(ls[nb][0] + ls[nb][1] <= kLaneSumMax);
+  if (__any(raise)) {  // rare (also catches +inf and NaN sums)
+    asm volatile("" ::: "memory");
+    f32x16 so[kNQB];
+    if constexpr (kSep) {  // S(j) is still in s
+#pragma unroll
+      for (int nb = 0; nb < kNQB; ++nb) so[nb] = s[nb];
+    } else {  // S(j) was overwritten: again from K(j), still in its slot
+#pragma unroll
+      for (int nb = 0; nb < kNQB; ++nb) so[nb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 a = lds_b128(Kj, ta.rm[ks]);
+#pragma unroll
+        for (int nb = 0; nb < kNQB; ++nb) so[nb] = mfma32<DT>(a, qf[nb][ks], so[nb]);
+      }
+      mask_tile<BAND>(so, j0, Nk, wl, wr, qw0, col, half);
+    }
 #pragma unroll
     for (int nb = 0; nb < kNQB; ++nb) {
-      const float mnew = fmaxf(st.m[nb], mxc[nb]);
+      float mx = so[nb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, so[nb][r]);
+      const float mnew = fmaxf(st.m[nb], max_pair32(mx) * c);
       const float alpha = exp2_fast(st.m[nb] - mnew);
       st.m[nb] = mnew;
       st.l[nb] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db][nb] *= alpha;
+      weights<DT, DROP>(so[nb], c, st.m[nb], ls[nb], pn[nb], rnd[nb], dp.thr);
     }
   }
-
-  // ---- S(j+1) = K(j+1) Q^T, issued first so the MFMAs run under the exponentials
-#pragma unroll
-  for (int nb = 0; nb < kNQB; ++nb) sn[nb] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const u32x4 a = lds_b128(Kn, ta.rm[ks]);
-#pragma unroll
-    for (int nb = 0; nb < kNQB; ++nb) sn[nb] = mfma32<DT>(a, qf[nb][ks], sn[nb]);
-  }
-
-  // ---- P = 2^(S c - m) packed into the MFMA B operand (after dropout:
-  // the normaliser sums the undropped weights, the kept ones are rescaled
-  // once in the epilogue)
-  u32x4 pf[2][kNQB];
-  float ls[kNQB][2];
 #pragma unroll
   for (int nb = 0; nb < kNQB; ++nb) {
-    const float mneg = -st.m[nb];
-    ls[nb][0] = ls[nb][1] = 0.f;
-    u32x4 rnd = u32x4{0, 0, 0, 0};
-    if constexpr (DROP)  // this lane's 16 keys of tile j: one generator call
-      rnd = philox4x32_10(2u * (uint32_t)j + (uint32_t)half, (uint32_t)(qw0 + 32 * nb + col), bh, dp.offset,
-                          dp.seed_lo, dp.seed_hi);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 8 * kk + 2 * e;
-        float p0 = exp2_fast(__builtin_fmaf(s[nb][r], c, mneg));
-        float p1 = exp2_fast(__builtin_fmaf(s[nb][r + 1], c, mneg));
-        if constexpr (DT == DT_BF16 || DROP) {  // bf16 rounding (2^-9) is too coarse for the normaliser
-          ls[nb][0] = (r == 0) ? p0 : ls[nb][0] + p0;
-          ls[nb][1] = (r == 0) ? p1 : ls[nb][1] + p1;
-        }
-        if constexpr (DROP) {  // register r holds key 8*(r/4) + 4*half + r%4 of the tile
-          if (((rnd[r >> 2] >> (8 * (r & 3))) & 0xffu) < dp.thr) p0 = 0.f;
-          if (((rnd[(r + 1) >> 2] >> (8 * ((r + 1) & 3))) & 0xffu) < dp.thr) p1 = 0.f;
-        }
-        w[e] = pack2<DT>(p0, p1);
-      }
-      if constexpr (DT == DT_F16 && !DROP) {  // fp16-rounded P is accurate enough: sum pairs in one op
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ls[nb][e & 1] = dot2_sum<DT>(w[e], ls[nb][e & 1]);
-      }
-      pf[kk][nb] = u32x4{w[0], w[1], w[2], w[3]};
-    }
+    st.l[nb] += ls[nb][0] + ls[nb][1];
+    pf[0][nb] = pn[nb][0];
+    pf[1][nb] = pn[nb][1];
   }
-  // ---- O^T += V^T P^T
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const u32x4 a = lds_transposed_a<D>(Vt, ta, kk, db);
-#pragma unroll
-      for (int nb = 0; nb < kNQB; ++nb) acc[db][nb] = mfma32<DT>(a, pf[kk][nb], acc[db][nb]);
-    }
-#pragma unroll
-  for (int nb = 0; nb < kNQB; ++nb) st.l[nb] += ls[nb][0] + ls[nb][1];
 
-  // tile j+2 must have landed (K read next step, V the step after); j+3 may fly on
-  if (j + 3 < n_kt) {
-    wait_vmcnt<2 * TC::NI>();
+  // the V reads must have left LDS before the barrier, after which tile
+  // j+4 may land in the slot
+  wait_lds_reads();
+
+  if constexpr (FwdTile<D>::SEP_S) {
+    // K(j+2) and V(j+1) (read next step) must have landed; the copies
+    // issued after them (K(j+3), V(j+2), K(j+4), V(j+3)) may fly on
+    if (j + 4 < n_kt) {
+      wait_vmcnt<4 * TC::NI>();
+    } else {
+      wait_loads();
+    }
   } else {
-    wait_loads();
+    // tile j+2 must have landed (its K is read next step); tile j+3 may fly on
+    if (j + 3 < n_kt) {
+      wait_vmcnt<2 * TC::NI>();
+    } else {
+      wait_loads();
+    }
   }
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -295,15 +441,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
       qf[nb][ks] = x;
     }
   }
-  // prologue: tiles jt0 .. jt0+2 in flight (tile j lives in slot j mod 4)
+  // prologue: tiles jt0 .. jt0+2 in flight (tile jt0 + t lives in slot
+  // t mod 4), and K of tile jt0+3 where K runs four tiles ahead
+  constexpr bool kSep = FwdTile<D>::SEP_S;
 #pragma unroll
   for (int t0 = 0; t0 < 3; ++t0) {
     const int jj = jt0 + t0;
     if (jj < n_kt) {
-      TC::issue(krs, krow, (uint32_t)jj * ktb, Ks[jj & 3], lane, wave);
-      TC::issue(vrs, vrow, (uint32_t)jj * vtb, Vs[jj & 3], lane, wave);
+      TC::issue(krs, krow, (uint32_t)jj * ktb, Ks[t0], lane, wave);
+      TC::issue(vrs, vrow, (uint32_t)jj * vtb, Vs[t0], lane, wave);
     }
   }
+  if (kSep && jt0 + 3 < n_kt) TC::issue(krs, krow, (uint32_t)(jt0 + 3) * ktb, Ks[3], lane, wave);
 
   f32x16 acc[DB][kNQB];
 #pragma unroll
@@ -321,7 +470,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   TileAddr<D> ta;
   ta.init(lane);
 
-  if (n_kt - jt0 > 2) {
+  // tiles jt0 and jt0+1 landed (K(jt0) for S(jt0) now, V(jt0) and
+  // K(jt0+1) in the first step); with K four ahead, V(jt0+1), K(jt0+2),
+  // V(jt0+2) and K(jt0+3) may fly on
+  if (kSep && n_kt - jt0 > 3) {
+    wait_vmcnt<4 * TC::NI>();
+  } else if (!kSep && n_kt - jt0 > 2) {
     wait_vmcnt<2 * TC::NI>();
   } else {
     wait_loads();
@@ -332,26 +486,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
     for (int ks = 0; ks < KS; ++ks) qf[nb][ks] ^= p.qflip;
   lds_barrier();
 
-  // S(0)
-  f32x16 sa[kNQB], sb[kNQB];
+  // Tile jt0 + t lives in slot t mod 4.
+  if (jt0 < n_kt) {
+    f32x16 sa[kNQB];
 #pragma unroll
-  for (int nb = 0; nb < kNQB; ++nb) sa[nb] = f32x16{};
+    for (int nb = 0; nb < kNQB; ++nb) sa[nb] = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const u32x4 a = lds_b128(Ks[jt0 & 3], ta.rm[ks]);
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 a = lds_b128(Ks[0], ta.rm[ks]);
 #pragma unroll
-    for (int nb = 0; nb < kNQB; ++nb) sa[nb] = mfma32<DT>(a, qf[nb][ks], sa[nb]);
-  }
-
-  // (Unrolling by two so that S alternates between the two register sets
-  // without the copy costs ~60 more registers and spills at d = 64.)
-  for (int j = jt0; j < n_kt; ++j) {
-    const int sl = j & 3;
-    fwd_step<D, DT, BAND, DROP>(j, n_kt, sa, sb, Ks[(sl + 1) & 3], Vs[sl], Ks[(sl + 3) & 3], Vs[(sl + 3) & 3], krs,
-                                vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta,
-                                p.drop, (uint32_t)bh);
+      for (int nb = 0; nb < kNQB; ++nb) sa[nb] = mfma32<DT>(a, qf[nb][ks], sa[nb]);
+    }
+    if constexpr (kSep) {  // the first step copies K(jt0+4) into K(jt0)'s slot
+      wait_lds_reads();
+      lds_barrier();
+    }
+    u32x4 pf[2][kNQB];
+    u32x4 va[2][DB];
+    // with S(j+1) in registers of its own it is copied back to sa after
+    // each step (unrolling by two to alternate instead spills at d = 128)
+    f32x16 sb[kNQB];
+    fwd_step<D, DT, BAND, DROP, true>(jt0, n_kt, sa, sb, pf, va, Ks[0], Ks[1], Vs[0], Ks[kSep ? 0 : 3], Vs[3], krs, vrs, krow,
+                                      vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta, p.drop,
+                                      (uint32_t)bh);
+    if constexpr (kSep) {
 #pragma unroll
-    for (int nb = 0; nb < kNQB; ++nb) sa[nb] = sb[nb];
+      for (int nb = 0; nb < kNQB; ++nb) sa[nb] = sb[nb];
+    }
+    for (int j = jt0 + 1; j < n_kt; ++j) {
+      const int sl = (j - jt0) & 3;
+      fwd_step<D, DT, BAND, DROP, false>(j, n_kt, sa, sb, pf, va, Ks[sl], Ks[(sl + 1) & 3], Vs[sl],
+                                         Ks[kSep ? sl : (sl + 3) & 3], Vs[(sl + 3) & 3], krs, vrs, krow, vrow, ktb, vtb, qf, acc,
+                                         st, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta, p.drop, (uint32_t)bh);
+      if constexpr (kSep) {
+#pragma unroll
+        for (int nb = 0; nb < kNQB; ++nb) sa[nb] = sb[nb];
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int nb = 0; nb < kNQB; ++nb) acc[db][nb] = mfma32<DT>(va[kk][db], pf[kk][nb], acc[db][nb]);
   }
 
   // ---- epilogue: O = O^T / l, LSE
