@@ -51,7 +51,7 @@ def log(*a):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("fa_device.h", "fa_kernels.h", "fa_fwd.hip", "fa_bwd.hip"):
+    for f in ("fa_device.h", "fa_kernels.h", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip"):
         with open(os.path.join(ROOT, "exact_io_aware_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -197,7 +197,8 @@ def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
     ff = 4.0 * B * H * d * pairs_causal
     res["fp8_fwd"] = {"workload": "B1 H16 N16384 d128 float8_e4m3fn causal (the bf16 inputs cast), bf16 out",
                       "fwd_ms": tf, "fwd_tflops": ff / tf / 1e9, "peak": PEAK_TFLOPS["fp8"],
-                      "fwd_frac_of_peak": ff / tf / 1e9 / PEAK_TFLOPS["fp8"]}
+                      "fwd_frac_of_peak": ff / tf / 1e9 / PEAK_TFLOPS["fp8"],
+                      "traffic": measured_traffic("fp8_fwd")}
     log("fp8_fwd: fwd %.3f ms (%.1f TFLOP/s, %.1f%% of the fp8 peak)" % (
         tf, ff / tf / 1e9, 100 * ff / tf / 1e9 / PEAK_TFLOPS["fp8"]))
     return res
