@@ -24,9 +24,11 @@
 //                untransposed LDS tiles with ds_read_b64_tr_b16.
 //   dq_kernel    a workgroup owns 128 queries (32 per wave) with Q and dO
 //                in registers; 32-key tiles of K and V stream through a
-//                3-slot ring.  S^T and dP^T have a query
+//                4-slot ring.  S^T and dP^T have a query
 //                per lane (its lse and D are lane-local); dQ^T += K^T dS^T
-//                reads K^T transposed from the K tile.
+//                reads K^T transposed from the K tile.  Each step forms
+//                dS of tile j on the VALU, then issues dQ(j) and the S and
+//                dP MFMAs of tile j+1 as one interleaved run.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -39,7 +41,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kT = 32;        // rows per streamed tile (queries in dkdv, keys in dq)
-constexpr int kNBuf = 3;      // ring slots: tile t+2 loads while tile t is computed
 constexpr int kStatPad = 64;  // per-(b,h) stride of the workspace statistics, rounded up to this
 
 template <int DT>
@@ -470,17 +471,30 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 }
 
 // ------------------------------------------------------------ dQ
+// dQ: a workgroup owns 128 queries (32 per wave) with Q and dO in
+// registers; 32-key tiles of K and V stream through a 4-slot ring (tile
+// t + 3 requested while tile t is used).  Software pipeline, step j:
+//
+//   VALU   P(j) = 2^(S(j) c - lse), masks, dS(j) = P (dP(j) - D), packed;
+//   MFMA   dQ^T += K(j)^T dS(j)^T, S(j+1)^T = K(j+1) Q^T and
+//          dP(j+1)^T = V(j+1) dO^T - D, interleaved and written over the
+//          S(j), dP(j) registers just consumed, with their LDS operands
+//          read a few MFMAs ahead.
+//
+// Each wave alternates a VALU phase and an MFMA phase; the two waves on a
+// SIMD (two workgroups) fill each other's phases.
 template <int D, int DT, bool BAND, bool DROP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(BwdParams p) {
   constexpr int QW = 32;
   constexpr int BM = kWaves * QW;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int NB = 4;  // ring slots
   using TC = TileCopyT<D, kT, kWaves>;
 
   struct Smem {  // one LDS object, as in dkdv_kernel
-    uint16_t k[kNBuf][kT * D];
-    uint16_t v[kNBuf][kT * D];
+    uint16_t k[NB][kT * D];
+    uint16_t v[NB][kT * D];
   };
   __shared__ __attribute__((aligned(1024))) Smem sm;
   auto& Ks = sm.k;
@@ -515,12 +529,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   const int n_kt = (kend + kT - 1) / kT;
 
+  // tile jt0 + t lives in slot t mod 4
   auto issue = [&](int j, int slot) {
     TC::issue(krs, krow, (uint32_t)j * kT * krow, Ks[slot], lane, wave);
     TC::issue(vrs, vrow, (uint32_t)j * kT * vrow, Vs[slot], lane, wave);
   };
-  if (jt0 < n_kt) issue(jt0, 0);
-  if (jt0 + 1 < n_kt) issue(jt0 + 1, 1);
+#pragma unroll
+  for (int t0 = 0; t0 < 3; ++t0)
+    if (jt0 + t0 < n_kt) issue(jt0 + t0, t0);
 
   // Q^T and dO^T of this wave's queries as B operands (zeros past Nq).
   u32x4 qf[KS], of[KS];
@@ -553,55 +569,75 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   TileAddr<D> ta;
   ta.init(lane);
 
-  wait_loads();
+  // tiles jt0 and jt0+1 landed (S(jt0) now, tile jt0+1 in the first step)
+  if (n_kt - jt0 > 2) {
+    wait_vmcnt<2 * TC::NI>();
+  } else {
+    wait_loads();
+  }
   lds_barrier();
 
-  int slot = 0;
+  // S(jt0)^T and dP(jt0)^T - D: rows are keys j0 + acc_row(half, r), column this lane's query
+  f32x16 s, dp;
+  if (jt0 < n_kt) {
+    s = rows_times_regs<D, DT>(Ks[0], qf, ta);
+    dp = rows_times_regs<D, DT>(Vs[0], of, ta, dinit);
+  }
   for (int j = jt0; j < n_kt; ++j) {
     const int j0 = j * kT;
-    int nslot = slot + 2;
-    nslot = nslot >= kNBuf ? nslot - kNBuf : nslot;
-    if (j + 2 < n_kt) issue(j + 2, nslot);
+    const int sl = (j - jt0) & 3;
+    if (j + 3 < n_kt) issue(j + 3, (sl + 3) & 3);
 
-    // skip tiles outside this wave's band
-    const bool active = qw0 < p.Nq && !(BAND && ((p.wr >= 0 && j0 > qw0 + QW - 1 + p.wr) ||
-                                                 (p.wl >= 0 && j0 + kT - 1 < qw0 - p.wl)));
-    auto body = [&](const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ Vt) {  // as in dkdv_kernel
-      // S^T = K Q^T and dP^T = V dO^T: rows are keys j0 + acc_row(half, r); column = this lane's query
-      f32x16 s = rows_times_regs<D, DT>(Kt, qf, ta);
-      f32x16 dp = rows_times_regs<D, DT>(Vt, of, ta, dinit);  // dP^T - D (dP^T with dropout)
-      u32x4 rnd = u32x4{0, 0, 0, 0};
-      if constexpr (DROP)  // the forward's draw for this query and the lane's 16 keys of tile j
-        rnd = philox4x32_10(2u * (uint32_t)j + (uint32_t)half, (uint32_t)qi, (uint32_t)bh, p.drop.offset,
-                            p.drop.seed_lo, p.drop.seed_hi);
-      const bool need_mask = (j0 + kT > p.Nk) || (BAND && ((p.wr >= 0 && j0 + kT - 1 > qw0 + p.wr) ||
-                                                            (p.wl >= 0 && j0 < qw0 + QW - 1 - p.wl)));
+    // ---- VALU phase: dS(j)
+    u32x4 rnd = u32x4{0, 0, 0, 0};
+    if constexpr (DROP)  // the forward's draw for this query and the lane's 16 keys of tile j
+      rnd = philox4x32_10(2u * (uint32_t)j + (uint32_t)half, (uint32_t)qi, (uint32_t)bh, p.drop.offset,
+                          p.drop.seed_lo, p.drop.seed_hi);
+    const bool need_mask = (j0 + kT > p.Nk) || (BAND && ((p.wr >= 0 && j0 + kT - 1 > qw0 + p.wr) ||
+                                                          (p.wl >= 0 && j0 < qw0 + QW - 1 - p.wl)));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = exp2_fast(__builtin_fmaf(s[r], c, -lse2));
-        if (need_mask) {
-          const int kk = j0 + acc_row(half, r);
-          if (kk >= p.Nk || (BAND && ((p.wr >= 0 && kk > qi + p.wr) || (p.wl >= 0 && kk < qi - p.wl)))) pv = 0.f;
-        }
-        if constexpr (DROP) {  // dS = P (keep * scale * dP - D)
-          const float m = ((rnd[r >> 2] >> (8 * (r & 3))) & 0xffu) >= p.drop.thr ? p.drop.scale : 0.f;
-          dp[r] = pv * __builtin_fmaf(m, dp[r], ndsv);
-        } else {
-          dp[r] = pv * dp[r];
-        }
+    for (int r = 0; r < 16; ++r) {
+      float pv = exp2_fast(__builtin_fmaf(s[r], c, -lse2));
+      if (need_mask) {
+        const int kk = j0 + acc_row(half, r);
+        if (kk >= p.Nk || (BAND && ((p.wr >= 0 && kk > qi + p.wr) || (p.wl >= 0 && kk < qi - p.wl)))) pv = 0.f;
       }
-      const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
-      tile_t_times<D, DT>(adq, Kt, bd, ta);  // dQ^T += K^T dS^T
-    };
-    if (active) body(Ks[slot], Vs[slot]);
+      if constexpr (DROP) {  // dS = P (keep * scale * dP - D)
+        const float m = ((rnd[r >> 2] >> (8 * (r & 3))) & 0xffu) >= p.drop.thr ? p.drop.scale : 0.f;
+        dp[r] = pv * __builtin_fmaf(m, dp[r], ndsv);
+      } else {
+        dp[r] = pv * dp[r];
+      }
+    }
+    const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
+    __builtin_amdgcn_sched_barrier(0);
 
-    if (j + 2 < n_kt) {
+    // ---- MFMA phase: dQ(j), S(j+1), dP(j+1) (reading tile j+1's stale
+    // slot when j+1 = n_kt; those scores are never used)
+    {
+      const uint16_t* __restrict__ Kt = Ks[sl];
+      const uint16_t* __restrict__ Kn = Ks[(sl + 1) & 3];
+      const uint16_t* __restrict__ Vn = Vs[(sl + 1) & 3];
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        if (i < 2 * DB) {
+          const int kk = i / DB, db = i % DB;
+          adq[db] = mfma32<DT>(lds_transposed_a<D>(Kt, ta, kk, db), bd[kk], adq[db]);
+        }
+        s = mfma32<DT>(lds_b128(Kn, ta.rm[i]), qf[i], i == 0 ? f32x16{} : s);
+        dp = mfma32<DT>(lds_b128(Vn, ta.rm[i]), of[i], i == 0 ? dinit : dp);
+      }
+      sched_reads_ahead<2 * DB + 2 * KS, 4 * DB + 2 * KS>();
+    }
+
+    // tile j+2 (read next step) must have landed; tile j+3 may fly on
+    if (j + 3 < n_kt) {
       wait_vmcnt<2 * TC::NI>();
     } else {
       wait_loads();
     }
     lds_barrier();
-    slot = slot + 1 >= kNBuf ? 0 : slot + 1;
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   if (qi < p.Nq) store_rows<DT, DB>(p.dq + b * p.sdq.b + h * p.sdq.h + qi * p.sdq.s, adq, p.scale, half);
