@@ -147,7 +147,9 @@ def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(c["k"]), torch.empty_like(c["v"])
-        ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_BF16), dtype=torch.uint8, device=q.device)
+        # with fewer K/V heads, the workspace that lets the dK/dV stage split
+        ws = torch.empty(fa.fa_bwd_ex_workspace_bytes(B, H, c["k"].shape[1], N, N, d, fa.FA_BF16), dtype=torch.uint8,
+                         device=q.device)
 
         def fwd():
             fa.fa_fwd_ex(q, c["k"], c["v"], o, lse, s, True, c["window"], "bhsd", stream, c["dropout"])

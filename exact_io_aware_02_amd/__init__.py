@@ -23,7 +23,7 @@ __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_DEVICE", "FA_ERR_LAUNCH",
     "FA_FP16", "FA_BF16", "FaError", "lib_path", "load_library",
     "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_fwd_fp8", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
-    "fa_bwd_ex", "fa_bwd_workspace_bytes",
+    "fa_bwd_ex", "fa_bwd_workspace_bytes", "fa_bwd_ex_workspace_bytes",
     "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
     "fa_status_string", "fa_last_error_message", "fa_abi_version",
     "attention_fwd", "attention_bwd", "attention_fwd_fp8", "EXPORTED_SYMBOLS",
@@ -35,7 +35,8 @@ FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED_SYMBOLS = (
     "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
-    "fa_bwd_ex", "fa_fwd_fp8", "fa_status_string", "fa_last_error_message", "fa_abi_version",
+    "fa_bwd_ex", "fa_fwd_fp8", "fa_bwd_ex_workspace_bytes", "fa_status_string", "fa_last_error_message",
+    "fa_abi_version",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +75,8 @@ def load_library():
     lib.fa_fwd_strided.restype = _i
     lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
     lib.fa_bwd_workspace_bytes.restype = _sz
+    lib.fa_bwd_ex_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+    lib.fa_bwd_ex_workspace_bytes.restype = _sz
     lib.fa_bwd.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp, _sz, _vp]
     lib.fa_bwd.restype = _i
     lib.fa_bwd_strided.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i] + [_I64x3] * 8 + [_vp, _sz, _vp]
@@ -194,6 +197,12 @@ def fa_fwd_strided(q, k, v, o, lse, scale, causal, layout="bshd", stream=None):
 
 def fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype):
     return int(load_library().fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype))
+
+
+def fa_bwd_ex_workspace_bytes(B, H, H_kv, Nq, Nk, d, dtype):
+    """C ``fa_bwd_ex_workspace_bytes``: the workspace that lets ``fa_bwd_ex``
+    split the dK/dV stage when there are fewer K/V heads."""
+    return int(load_library().fa_bwd_ex_workspace_bytes(B, H, H_kv, Nq, Nk, d, dtype))
 
 
 def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, stream=None):
@@ -361,7 +370,8 @@ def attention_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bhsd", 
     Hkv, Nk = _dims(k, layout)[1:3]
     s = _default_scale(d, scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    nbytes = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, _dtype_code(q))
+    nbytes = (fa_bwd_ex_workspace_bytes(B, H, Hkv, Nq, Nk, d, _dtype_code(q)) if Hkv != H
+              else fa_bwd_workspace_bytes(B, H, Nq, Nk, d, _dtype_code(q)))
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     contiguous = all(t.is_contiguous() for t in (q, k, v, o, do))
     if Hkv != H or window is not None or dropout is not None:

@@ -160,7 +160,7 @@ void contiguous_strides(int H, int N, int d, int64_t st[3]) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 3; }
+int fa_abi_version(void) { return 4; }
 
 const char* fa_status_string(int status) {
   switch (status) {
@@ -299,6 +299,12 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   return FA_OK;
 }
 
+size_t fa_bwd_ex_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d, int dtype) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || (d != 64 && d != 128) || (dtype != FA_FP16 && dtype != FA_BF16)) return 0;
+  if (H > 0 && (H_kv < 1 || H % H_kv != 0)) return 0;
+  return fa::bwd_split_workspace_bytes(B, H, H > 0 ? H_kv : 1, Nq, Nk, d);
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || (d != 64 && d != 128) || (dtype != FA_FP16 && dtype != FA_BF16)) return 0;
   return fa::bwd_workspace_bytes(B, H, Nq);
@@ -338,10 +344,16 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(FA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   if (workspace_bytes < need)
     return fail(FA_ERR_INVALID_ARG, "workspace_bytes = %zu < required %zu", workspace_bytes, need);
+  // fewer K/V heads: split each K/V head's query heads over more dK/dV
+  // workgroups when the workspace holds their partial sums
+  const int splits = fa::bwd_kv_splits(B, H, H_kv, Nk);
+  const size_t need_split = fa::bwd_split_workspace_bytes(B, H, H_kv, Nq, Nk, d);
+  const bool split = splits > 1 && (stages & FA_BWD_DKDV) && workspace_bytes >= need_split;
+  const size_t used = split ? need_split : need;
   const void* ins[6] = {q, k, v, o, dout, lse};
   const Extent eins[6] = {eq, ek, ev, eo, edo, Extent{0, (int64_t)B * H * Nq * 4}};
   void* outs[4] = {dq, dk, dv, workspace};
-  const Extent eouts[4] = {edq, edk, edv, Extent{0, (int64_t)need}};
+  const Extent eouts[4] = {edq, edk, edv, Extent{0, (int64_t)used}};
   const char* onames[4] = {"dq", "dk", "dv", "workspace"};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
@@ -383,6 +395,8 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   p.drop = drop;
   p.scale = scale;
   p.c = scale * 1.4426950408889634f;
+  p.S = split ? splits : 1;
+  p.part = split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need) : nullptr;
   hipError_t e = fa::launch_bwd(p, d, dtype, band.present(), stages, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;

@@ -225,10 +225,14 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
   const int pair = wave & (NPAIR - 1);
   const bool role_a = wave < NPAIR;
   const int Hkv = p.H / p.G;
-  const int BH = p.B * Hkv;  // workgroups per key tile: one per (batch, K/V head)
+  const int BH = p.B * Hkv;
+  // workgroups per key tile: one per (batch, K/V head, group of G / S query heads)
   const int t = blockIdx.x;
-  const int kt = t / BH;  // ascending key tiles: the causal-heaviest first
-  const int bhk = t - kt * BH;
+  const int kt = t / (BH * p.S);  // ascending key tiles: the causal-heaviest first
+  const int rem = t - kt * BH * p.S;
+  const int bhk = rem / p.S;
+  const int sp = rem - bhk * p.S;
+  const int GS = p.G / p.S;  // query heads of this workgroup: hk * G + sp * GS + [0, GS)
   const int b = bhk / Hkv, hk = bhk - b * Hkv;
   const int k0 = kt * BNK;
   const int kw0 = k0 + pair * KW;
@@ -248,10 +252,11 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     if (p.wl >= 0) qhi = min(n_qt, (k0 + BNK - 1 + p.wl) / kT + 1);
   }
   const int nq = max(0, qhi - qlo);
-  const int U = p.G * nq;
+  const int U = GS * nq;
+  const int h0 = hk * p.G + sp * GS;
 
   // requests go out in step order; (iss_h, iss_it) is the next one's tile
-  int iss_h = hk * p.G, iss_it = qlo;
+  int iss_h = h0, iss_it = qlo;
   auto issue = [&](int slot) {
     // role A streams Q and lse2, role B dO and -D
     const uint16_t* tp = role_a ? p.q + b * p.sq.b + iss_h * p.sq.h : p.dout + b * p.sdo.b + iss_h * p.sdo.h;
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     // One step.  (Unrolling by the ring depth would turn the slot bases
     // into immediates, but makes this compiler spill role A's registers.)
     int it = qlo;            // query tile of the current step
-    int hcur = hk * p.G;     // its query head
+    int hcur = h0;           // its query head
     auto step = [&](int u) {
       const int SL = u & (NB - 1);
       const int XB = SL & 1;
@@ -456,7 +461,15 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     }
 
     if (key < p.Nk) {
-      if constexpr (A) {
+      if (p.S > 1) {  // fp32 partial row of dK (B) or dV (A), scaled by the reduction
+        float* rowp = p.part + ((((size_t)(A ? 1 : 0) * p.S + sp) * BH + bhk) * (size_t)p.Nk + key) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *(f32x4*)(rowp + db * 32 + 8 * g4 + 4 * half) =
+                f32x4{acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]};
+      } else if constexpr (A) {
         store_rows<DT, DB>(p.dv + b * p.sdv.b + hk * p.sdv.h + key * p.sdv.s, acc, DROP ? p.drop.scale : 1.0f, half);
       } else {
         store_rows<DT, DB>(p.dk + b * p.sdk.b + hk * p.sdk.h + key * p.sdk.s, acc, p.scale, half);
@@ -468,6 +481,36 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
   } else {
     run(std::false_type{});
   }
+}
+
+// dK, dV = the scaled sums of the S partials, 8 values of one row per
+// thread, in a fixed order (deterministic).
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdParams p, int rows) {
+  constexpr int CH = D / 8;  // 8-value chunks per row
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= 2 * (int64_t)rows * CH) return;
+  const int which = (int)(i / ((int64_t)rows * CH));  // 0: dK, 1: dV
+  const int64_t rc = i - (int64_t)which * rows * CH;
+  const int row = (int)(rc / CH), ch = (int)(rc - (int64_t)row * CH);
+  const int bhk = row / p.Nk, key = row - bhk * p.Nk;
+  const int Hkv = p.H / p.G;
+  const int b = bhk / Hkv, hk = bhk - b * Hkv;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.S; ++s) {
+    const float* src = p.part + (((size_t)which * p.S + s) * rows + row) * (size_t)D + 8 * ch;
+    const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] += x0[e];
+      a[4 + e] += x1[e];
+    }
+  }
+  const float mul = which == 0 ? p.scale : (p.drop.thr > 0 ? p.drop.scale : 1.0f);
+  uint16_t* dst = which == 0 ? p.dk + b * p.sdk.b + hk * p.sdk.h + key * p.sdk.s
+                             : p.dv + b * p.sdv.b + hk * p.sdv.h + key * p.sdv.s;
+  *(u32x4*)(dst + 8 * ch) = u32x4{pack2<DT>(a[0] * mul, a[1] * mul), pack2<DT>(a[2] * mul, a[3] * mul),
+                                  pack2<DT>(a[4] * mul, a[5] * mul), pack2<DT>(a[6] * mul, a[7] * mul)};
 }
 
 // ------------------------------------------------------------ dQ
@@ -650,9 +693,12 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
   constexpr int RPB = kThreads / (D / 8);
   const int64_t prep_bpb = (stat_stride(p.Nq) + RPB - 1) / RPB;
   const int64_t g0 = prep_bpb * BH;
-  const int64_t g1 = (int64_t)((p.Nk + 127) / 128) * BHkv;
+  const int64_t g1 = (int64_t)((p.Nk + 127) / 128) * BHkv * p.S;
+  const int64_t rrows = BHkv * (int64_t)p.Nk;  // rows of dK (and of dV)
+  const int64_t gr = (2 * rrows * (D / 8) + kThreads - 1) / kThreads;
   const int64_t g2 = (int64_t)((p.Nq + 127) / 128) * BH;
-  if (g0 > 0x7fffffff || g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (g0 > 0x7fffffff || g1 > 0x7fffffff || g2 > 0x7fffffff || rrows > 0x7fffffff || gr > 0x7fffffff)
+    return hipErrorInvalidConfiguration;
   hipError_t e = hipSuccess;
   if ((stages & 1) && g0 > 0) {  // Nq may be 0 (then dK = dV = 0 and there is no dQ)
     hipLaunchKernelGGL((prep_kernel<D, DT>), dim3((unsigned)g0), dim3(kThreads), 0, stream, p, (int)prep_bpb);
@@ -661,6 +707,10 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
   if ((stages & 2) && g1 > 0) {
     hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP>), dim3((unsigned)g1), dim3(2 * kThreads), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.S > 1) {
+      hipLaunchKernelGGL((dkdv_reduce_kernel<D, DT>), dim3((unsigned)gr), dim3(kThreads), 0, stream, p, (int)rrows);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   if ((stages & 4) && g2 > 0) {
     hipLaunchKernelGGL((dq_kernel<D, DT, BAND, DROP>), dim3((unsigned)g2), dim3(kThreads), 0, stream, p);
@@ -686,6 +736,26 @@ size_t bwd_workspace_bytes(int B, int H, int Nq) {
 
 float* bwd_lse2_region(void* workspace, int B, int H, int Nq) {
   return static_cast<float*>(workspace) + (size_t)B * (size_t)H * (size_t)stat_stride(Nq);
+}
+
+// Enough dK/dV workgroups to balance a causal band over the chip: at least
+// 1024 (four per CU), splitting each K/V head's G query heads into S groups,
+// S the smallest divisor of G that gets there (else G).
+int bwd_kv_splits(int B, int H, int H_kv, int Nk) {
+  if (H_kv <= 0 || H % H_kv != 0) return 1;
+  const int G = H / H_kv;
+  if (G == 1) return 1;
+  const int64_t base = (int64_t)((Nk + 127) / 128) * B * H_kv;
+  for (int S = 1; S < G; ++S)
+    if (G % S == 0 && base * S >= 1024) return S;
+  return G;
+}
+
+size_t bwd_split_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d) {
+  const size_t stats = bwd_workspace_bytes(B, H, Nq);
+  const int S = bwd_kv_splits(B, H, H_kv, Nk);
+  if (S <= 1) return stats;
+  return stats + 2 * (size_t)S * (size_t)B * (size_t)H_kv * (size_t)Nk * (size_t)d * sizeof(float);
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int stages, hipStream_t stream) {

@@ -50,6 +50,12 @@ struct BwdParams {
   DropoutParams drop;
   float scale;  // the softmax scale as given
   float c;      // scale * log2(e) (signed)
+  // dK/dV of a K/V head split over S groups of its G query heads (S
+  // divides G): each workgroup writes fp32 partial sums to `part`
+  // ([2][S][B*H_kv][Nk][d]: dK^T then dV^T, unscaled) and a reduction kernel
+  // sums them; S = 1 accumulates all G heads in registers (part unused).
+  int S;
+  float* part;
 };
 
 // fp8 (OCP e4m3fn) forward: q, k, v are bytes, o is bf16.
@@ -77,6 +83,10 @@ hipError_t launch_fwd(const FwdParams& p, int d, int dtype, bool banded, hipStre
 // each B*H rows of Nq rounded up to 64 fp32 values (H = query heads).
 size_t bwd_workspace_bytes(int B, int H, int Nq);
 float* bwd_lse2_region(void* workspace, int B, int H, int Nq);
+// Split of each K/V head's query heads for the dK/dV stage (1 = none) and
+// the workspace bytes that split needs in total (statistics included).
+int bwd_kv_splits(int B, int H, int H_kv, int Nk);
+size_t bwd_split_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d);
 // stages: OR of 1 (row statistics), 2 (dK, dV), 4 (dQ), run in that order.
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int stages, hipStream_t stream);
 

@@ -208,7 +208,12 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
  * lse.  dk, dv are [B][H_kv][Nk][d] through their strides; a K/V
  * head's gradients sum the contributions of all query heads that use it.
  * The workspace is sized by fa_bwd_workspace_bytes(B, H, Nq, ...) with H
- * the number of query heads.  lse must be what fa_fwd_ex wrote (-inf for a
+ * the number of query heads, or, with fewer K/V heads, preferably by
+ * fa_bwd_ex_workspace_bytes: a workspace that large lets the dK/dV stage
+ * split each K/V head's query heads over more workgroups (their fp32
+ * partial sums are added in a fixed order by a second kernel, so results
+ * stay deterministic; they can differ from the unsplit order in the last
+ * bits of fp32 rounding).  lse must be what fa_fwd_ex wrote (-inf for a
  * row that admits no key; such a row gets dq = 0). */
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
               const void* dout, void* dq, void* dk, void* dv,
@@ -220,13 +225,22 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               const int64_t dk_strides[3], const int64_t dv_strides[3],
               void* workspace, size_t workspace_bytes, int stages, void* stream);
 
+/* Workspace bytes for fa_bwd_ex with H_kv K/V heads that enables the split
+ * dK/dV stage (at least fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype); 0 if
+ * the sizes are invalid).  The extra part holds 2 * S * B * H_kv * Nk * d
+ * fp32 partial sums, S the number of groups each K/V head's H / H_kv query
+ * heads are split into (1, i.e. no extra part, when H_kv = H or the
+ * problem already fills the chip). */
+size_t fa_bwd_ex_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d, int dtype);
+
 /* Static name of a status code ("FA_OK", ...); "FA_UNKNOWN_STATUS" otherwise. */
 const char* fa_status_string(int status);
 
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* fa_last_error_message(void);
 
-/* Library ABI version, currently 3 (3 added fa_fwd_fp8). */
+/* Library ABI version, currently 4 (3 added fa_fwd_fp8, 4
+ * fa_bwd_ex_workspace_bytes). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

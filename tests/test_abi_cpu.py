@@ -46,7 +46,7 @@ def test_exported_dynamic_symbols_are_c_names():
 
 
 def test_status_strings_and_version():
-    assert fa.fa_abi_version() == 3
+    assert fa.fa_abi_version() == 4
     assert fa.fa_status_string(0) == "FA_OK"
     assert fa.fa_status_string(1) == "FA_ERR_INVALID_ARG"
     assert fa.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
@@ -293,3 +293,33 @@ def test_python_fp8_binding_checks_dtypes():
     with pytest.raises(fa.FaError) as e:
         fa.attention_fwd_fp8(q, q, q)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
+
+
+def test_ex_workspace_bytes():
+    base = fa.fa_bwd_workspace_bytes(1, 16, 16384, 16384, 128, fa.FA_BF16)
+    # equal heads: nothing extra
+    assert fa.fa_bwd_ex_workspace_bytes(1, 16, 16, 16384, 16384, 128, fa.FA_BF16) == base
+    # 16 query heads on 2 K/V heads at 16K: 128 key blocks x 2 = 256 dK/dV workgroups, split 4 ways
+    big = fa.fa_bwd_ex_workspace_bytes(1, 16, 2, 16384, 16384, 128, fa.FA_BF16)
+    assert big == base + 2 * 4 * 1 * 2 * 16384 * 128 * 4
+    # a problem that already fills the chip is not split
+    assert fa.fa_bwd_ex_workspace_bytes(8, 64, 8, 16384, 16384, 128, fa.FA_BF16) == \
+        fa.fa_bwd_workspace_bytes(8, 64, 16384, 16384, 128, fa.FA_BF16)
+    # invalid sizes give 0
+    assert fa.fa_bwd_ex_workspace_bytes(1, 16, 3, 128, 128, 128, fa.FA_BF16) == 0
+    assert fa.fa_bwd_ex_workspace_bytes(1, 16, 2, 128, 128, 96, fa.FA_BF16) == 0
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful where no HIP device exists")
+def test_ex_accepts_either_workspace_size():
+    """The split workspace is optional: the statistics-only size stays valid."""
+    lib = fa.load_library()
+    I3 = ctypes.c_int64 * 3
+    H, Hkv, N = 8, 2, 64
+    sq = I3(H * N * 64, N * 64, 64)
+    sk = I3(Hkv * N * 64, N * 64, 64)
+    st = [sq, sk, sk, sq, sq, sq, sk, sk]
+    for nbytes in (fa.fa_bwd_workspace_bytes(1, H, N, N, 64, 0), fa.fa_bwd_ex_workspace_bytes(1, H, Hkv, N, N, 64, 0)):
+        assert lib.fa_bwd_ex(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), P(6 * A), P(7 * A), P(8 * A), P(9 * A),
+                             1, H, Hkv, N, N, 64, 0.125, 1, -1, -1, 0.0, 0, 0, 0, *st, P(10 * A), nbytes,
+                             fa.FA_BWD_ALL, None) == fa.FA_ERR_DEVICE

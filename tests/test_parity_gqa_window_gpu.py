@@ -115,3 +115,76 @@ def test_gqa_equals_repeated_heads():
         err = (g1.float() - ref).abs().max().item() / ref.abs().max().item()
         say("  grouped K/V gradient vs summed repeated heads: %.3e" % err)
         assert err < 1e-2
+
+
+def _bwd_ex(q, k, v, o, lse, do, causal, nbytes, window=None, dropout=None):
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    fa.fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, 1.0 / np.sqrt(q.shape[-1]), causal, ws, window,
+                 dropout=dropout)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("H,Hkv,N,d,dt,causal,window,dropout", [
+    (8, 2, 300, 128, "bf16", True, None, None),
+    (4, 1, 257, 64, "fp16", False, None, None),
+    (6, 3, 400, 64, "bf16", True, (100, -1), None),
+    (8, 2, 256, 128, "bf16", True, None, (0.1, 7, 3)),
+])
+def test_split_kv_gradients_match_unsplit(H, Hkv, N, d, dt, causal, window, dropout):
+    """The split dK/dV stage (partials reduced by a second kernel) against
+    the single-pass one: dQ bit-identical, dK/dV equal up to fp32 summation
+    order, and both within the oracle's tolerance."""
+    say("case split_kv H%d Hkv%d N%d d%d %s causal=%d window=%r dropout=%r" % (H, Hkv, N, d, dt, causal, window,
+                                                                                 dropout))
+    inp = make_qkv(1, H, N, N, d, dt, seed=31, with_do=True, Hkv=Hkv)
+    q, k, v, do = (inp[x].to(DEV) for x in ("q", "k", "v", "do"))
+    s = 1.0 / np.sqrt(d)
+    o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=s, window=window, dropout=dropout)
+    small = fa.fa_bwd_workspace_bytes(1, H, N, N, d, fa.FA_BF16 if dt == "bf16" else fa.FA_FP16)
+    big = fa.fa_bwd_ex_workspace_bytes(1, H, Hkv, N, N, d, fa.FA_BF16 if dt == "bf16" else fa.FA_FP16)
+    assert big > small
+    g0 = _bwd_ex(q, k, v, o, lse, do, causal, small, window, dropout)
+    g1 = _bwd_ex(q, k, v, o, lse, do, causal, big, window, dropout)
+    torch.cuda.synchronize()
+    assert torch.equal(g0[0], g1[0])
+    for nm, a, b in zip(("dk", "dv"), g0[1:], g1[1:]):
+        err = (a.float() - b.float()).abs().max().item() / max(b.float().abs().max().item(), 1e-30)
+        say("  %s split vs unsplit: max rel %.2e" % (nm, err))
+        assert err < 1e-2
+    w = window if window is not None else (-1, -1)
+    args = [to_bhsd64(inp[x]) for x in ("q", "k", "v")]
+    g_ref = attention_bwd64(*args, to_bhsd64(inp["do"]), s, causal, window=w, dropout=dropout)
+    for nm, g, r in zip(("dq", "dk", "dv"), g1, g_ref):
+        rel = np.linalg.norm(to_bhsd64(g.cpu()) - r) / np.linalg.norm(r)
+        say("  %s rel-F err (split) %.3e" % (nm, rel))
+        assert rel <= TOL_GRAD, nm
+
+
+def test_split_kv_16k_gqa_identities():
+    """The benchmark's fewer-K/V-heads backward (16 query heads on 2 K/V
+    heads, 16K causal d=128 bf16, split dK/dV): per K/V head the key sums
+    sum_j dK_j = 0 and sum_j dV_j = sum over its query heads and rows of dO
+    hold, and the split result matches the single-pass one."""
+    say("case split_kv_16k")
+    B, H, Hkv, N, d = 1, 16, 2, 16384, 128
+    inp = make_qkv(B, H, N, N, d, "bf16", seed=3, in_scale=0.5, with_do=True, Hkv=Hkv)
+    q, k, v, do = (inp[x].to(DEV) for x in ("q", "k", "v", "do"))
+    o, lse = fa.attention_fwd(q, k, v, causal=True)
+    small = fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_BF16)
+    big = fa.fa_bwd_ex_workspace_bytes(B, H, Hkv, N, N, d, fa.FA_BF16)
+    g0 = _bwd_ex(q, k, v, o, lse, do, True, small)
+    g1 = _bwd_ex(q, k, v, o, lse, do, True, big)
+    torch.cuda.synchronize()
+    assert torch.equal(g0[0], g1[0])
+    for nm, a, b in zip(("dk", "dv"), g0[1:], g1[1:]):
+        err = (a.float() - b.float()).abs().max().item() / b.float().abs().max().item()
+        say("  %s split vs unsplit: max rel %.2e" % (nm, err))
+        assert err < 1e-2
+    dk, dv = g1[1].double(), g1[2].double()
+    G = H // Hkv
+    sum_do = do.double().view(B, Hkv, G, N, d).sum(dim=(2, 3))
+    err_v = ((dv.sum(dim=2) - sum_do).abs().max() / sum_do.abs().max()).item()
+    err_k = (dk.sum(dim=2).abs().max() / dk.abs().sum(dim=2).max()).item()
+    say("  sum_j dV_j vs sum dO: %.2e; |sum_j dK_j| / sum_j |dK_j|: %.2e" % (err_v, err_k))
+    assert err_v < 2e-2 and err_k < 2e-2
