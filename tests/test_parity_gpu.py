@@ -348,3 +348,53 @@ def test_pages_accuracy_recipe():
     err = np.abs(to_bhsd64(o) - ro).max()
     say("  pages' recipe max diff %.3e" % err)
     assert err < 1e-3
+
+
+def test_batch_offsets_beyond_32_bits():
+    """Batch strides past 2^31 elements (64-bit offsets): q, k, v are views
+    into one 8.6 GB buffer with batch stride 2^31 + 64; the result equals the
+    contiguous copies' bit for bit, forward and backward."""
+    say("case batch_offsets_beyond_32_bits")
+    B, H, N, d = 2, 1, 256, 64
+    S = (1 << 31) + 64
+    buf = torch.empty(B * S, dtype=torch.float16, device=DEV)
+    inp = make_qkv(B, H, N, N, d, "fp16", seed=41, with_do=True)
+    views = []
+    for i, name in enumerate(("q", "k", "v")):
+        vw = torch.as_strided(buf, (B, H, N, d), (S, N * d, d, 1), storage_offset=i * N * d)
+        vw.copy_(inp[name].to(DEV))
+        views.append(vw)
+    q, k, v = views
+    do = inp["do"].to(DEV)
+    o1, l1 = fa.attention_fwd(q, k, v, causal=True)
+    g1 = fa.attention_bwd(q, k, v, o1, l1, do, causal=True)
+    qc, kc, vc = (x.contiguous() for x in views)
+    o2, l2 = fa.attention_fwd(qc, kc, vc, causal=True)
+    g2 = fa.attention_bwd(qc, kc, vc, o2, l2, do, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    del buf, views, q, k, v
+    torch.cuda.empty_cache()
+
+
+def test_large_grid_sampled_rows():
+    """32 x 32 (batch, head) pairs of 1024 causal fp16 tokens (8192 forward
+    workgroups): sampled rows of two (b, h) pairs against the oracle."""
+    say("case large_grid_sampled_rows")
+    B, H, N, d = 32, 32, 1024, 64
+    inp = make_qkv(B, H, N, N, d, "fp16", seed=43)
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    o, lse = fa.attention_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(1, 1, N, 64, seed=44)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        q64, k64, v64 = (to_bhsd64(inp[x][b:b + 1, h:h + 1]) for x in ("q", "k", "v"))
+        ro, rl = attention_rows_fwd64(q64, k64, v64, 1 / 8.0, True, rows)
+        go = o[b, h].cpu().double().numpy()[rows[0, 0]]
+        gl = lse[b, h].cpu().double().numpy()[rows[0, 0]]
+        eo = np.abs(go - ro[0, 0]).max()
+        el = np.abs(gl - rl[0, 0]).max()
+        say("  (b, h) = (%d, %d): O max-abs %.2e, LSE %.2e" % (b, h, eo, el))
+        assert eo <= TOL_O["fp16"] and el <= TOL_LSE
