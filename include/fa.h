@@ -31,8 +31,9 @@
  *    caller's next synchronisation, as usual in HIP.
  *  - Element type of Q, K, V, O, dO, dQ, dK, dV is `dtype` (FA_FP16 or
  *    FA_BF16; fp32 is not supported, as the skill guide's "精度が落ちる"
- *    issue and the glossary article's FP32 anti-pattern state).  LSE and the
- *    backward workspace are fp32.
+ *    issue and the glossary article's FP32 anti-pattern state), except in
+ *    fa_fwd_fp8 (e4m3fn Q, K, V; bf16 O).  LSE and the backward workspace
+ *    are fp32.
  *  - Head dimension d must be 64 or 128.
  *  - Default layout ("BHSD", the SDPA layout of the skill guide's quick
  *    start): Q/O are [B][H][Nq][d], K/V are [B][H][Nk][d], contiguous.
@@ -45,8 +46,9 @@
  *  - B, H or Nq equal to 0: nothing to do, FA_OK.  Nk must be >= 1 when
  *    Nq >= 1 (a softmax over no keys is undefined).
  *  - Each base pointer must be 16-byte aligned and each stride a multiple of
- *    8 elements; element offsets within one (b, h) slice must fit in 31
- *    bits.  O must not alias Q, K or V; dQ/dK/dV must not alias any input.
+ *    8 elements (16 for fa_fwd_fp8's byte tensors); element offsets within
+ *    one (b, h) slice must fit in 31 bits (offsets across batches and heads
+ *    are 64-bit).  O must not alias Q, K or V; dQ/dK/dV must not alias any input.
  *  - Return value: FA_OK (0) or an fa_status code.  Arguments are checked
  *    before any HIP call; on error nothing is enqueued.  A thread-local
  *    human-readable detail is available from fa_last_error_message().
