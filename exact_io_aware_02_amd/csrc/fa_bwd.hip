@@ -117,9 +117,9 @@ __device__ __forceinline__ void store_rows(uint16_t* rowp, const f32x16 (&acc)[D
 // held in registers, contracting over d.
 template <int D, int DT>
 __device__ __forceinline__ f32x16 rows_times_regs(const uint16_t* tile, const u32x4 (&bf)[D / 16],
-                                                  const TileAddr<D>& ta, f32x16 s = f32x16{}) {
+                                                  const TileLayout<D>& ta, f32x16 s = f32x16{}) {
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) s = mfma32<DT>(lds_b128(tile, ta.rm[ks]), bf[ks], s);
+  for (int ks = 0; ks < D / 16; ++ks) s = mfma32<DT>(lds_rowmajor<D>(tile, ta, ks), bf[ks], s);
   return s;
 }
 
@@ -127,7 +127,7 @@ __device__ __forceinline__ f32x16 rows_times_regs(const uint16_t* tile, const u3
 // 32, packed from a 32x32 accumulator in its register k order).
 template <int D, int DT>
 __device__ __forceinline__ void tile_t_times(f32x16 (&acc)[D / 32], const uint16_t* tile, const u32x4 (&bp)[2],
-                                             const TileAddr<D>& ta) {
+                                             const TileLayout<D>& ta) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -202,15 +202,16 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
   constexpr int DB = D / 32;
   constexpr int NB = 4;             // ring slots (a power of two)
   constexpr int PD = NB - 1;        // prefetch distance: tile t+PD is requested in step t
-  using TC = TileCopyT<D, kT, NPAIR>;  // a Q or dO tile over the four waves of one role
-  constexpr int NLOADS = TC::NI + 1;  // per wave per tile: its share of Q (A) or dO (B), 8 statistics
+  static_assert(kT == 32, "Q/dO tiles are the 32-row tiles of fa_device.h");
+  // a Q or dO tile is copied by the four waves of one role
+  constexpr int NLOADS = TileLayout<D>::template copy_insts<NPAIR>() + 1;  // per wave per tile: its share of Q (A) or dO (B), 8 statistics
 
   // One LDS object (separate __shared__ variables get separate alias
   // scopes, and the compiler then waits for every in-flight copy into a
   // variable before reading any part of it).
   struct Smem {
-    uint16_t q[NB][kT * D];
-    uint16_t o[NB][kT * D];  // dO
+    uint16_t q[NB][kTileElems<D>];
+    uint16_t o[NB][kTileElems<D>];  // dO
     float l[NB][kT];         // lse * log2(e)
     float d[NB][kT];         // -D
     f32x4 x[2][NPAIR][4][64];  // fp32 P hand-over, double buffered: [step & 1][pair][register group][lane]
@@ -263,7 +264,8 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     const __amdgpu_buffer_rsrc_t trs = head_rsrc(tp, p.Nq, tstride, D);
     const __amdgpu_buffer_rsrc_t srs =
         f32_rsrc((role_a ? p.lse2 : p.dsum) + ((int64_t)b * p.H + iss_h) * sst, sst);
-    TC::issue(trs, trow, (uint32_t)iss_it * kT * trow, role_a ? sm.q[slot] : sm.o[slot], lane, pair);
+    TileLayout<D>::template issue<NPAIR>(trs, trow, (uint32_t)iss_it * kT * trow, role_a ? sm.q[slot] : sm.o[slot], lane,
+                                         pair);
     vec_to_lds<8>(srs, (uint32_t)(iss_it * kT + 8 * pair) * 4, (role_a ? sm.l[slot] : sm.d[slot]) + 8 * pair, lane);
     if (++iss_it == qhi) {
       iss_it = qlo;
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     if constexpr (!A) {
       u32x4* z = (u32x4*)sm.q[NB - 1];
 #pragma unroll
-      for (int i = 0; i < kT * D / 8 / 256; ++i) z[(tid - 256) + 256 * i] = u32x4{0, 0, 0, 0};
+      for (int i = tid - 256; i < TileLayout<D>::BYTES / 16; i += 256) z[i] = u32x4{0, 0, 0, 0};
     }
 
     f32x16 acc[DB];  // dV^T (A) or dK^T (B)
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     u32x4 pk[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};  // A: P; B: dS of the previous tile
     const float c = p.c;
 
-    TileAddr<D> ta;
+    TileLayout<D> ta;
     ta.init(lane);
 
     // Tile pointers are __restrict__ parameters of inlined lambdas so that
@@ -533,11 +535,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NB = 4;  // ring slots
-  using TC = TileCopyT<D, kT, kWaves>;
+  static_assert(kT == 32, "K/V tiles are the 32-row tiles of fa_device.h");
+  constexpr int NI = TileLayout<D>::template copy_insts<kWaves>();  // copy instructions per wave per tile
 
   struct Smem {  // one LDS object, as in dkdv_kernel
-    uint16_t k[NB][kT * D];
-    uint16_t v[NB][kT * D];
+    uint16_t k[NB][kTileElems<D>];
+    uint16_t v[NB][kTileElems<D>];
   };
   __shared__ __attribute__((aligned(1024))) Smem sm;
   auto& Ks = sm.k;
@@ -574,8 +577,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // tile jt0 + t lives in slot t mod 4
   auto issue = [&](int j, int slot) {
-    TC::issue(krs, krow, (uint32_t)j * kT * krow, Ks[slot], lane, wave);
-    TC::issue(vrs, vrow, (uint32_t)j * kT * vrow, Vs[slot], lane, wave);
+    TileLayout<D>::template issue<kWaves>(krs, krow, (uint32_t)j * kT * krow, Ks[slot], lane, wave);
+    TileLayout<D>::template issue<kWaves>(vrs, vrow, (uint32_t)j * kT * vrow, Vs[slot], lane, wave);
   };
 #pragma unroll
   for (int t0 = 0; t0 < 3; ++t0)
@@ -609,12 +612,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int db = 0; db < DB; ++db) adq[db] = f32x16{};
   const float c = p.c;
 
-  TileAddr<D> ta;
+  TileLayout<D> ta;
   ta.init(lane);
 
   // tiles jt0 and jt0+1 landed (S(jt0) now, tile jt0+1 in the first step)
   if (n_kt - jt0 > 2) {
-    wait_vmcnt<2 * TC::NI>();
+    wait_vmcnt<2 * NI>();
   } else {
     wait_loads();
   }
@@ -667,15 +670,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           const int kk = i / DB, db = i % DB;
           adq[db] = mfma32<DT>(lds_transposed_a<D>(Kt, ta, kk, db), bd[kk], adq[db]);
         }
-        s = mfma32<DT>(lds_b128(Kn, ta.rm[i]), qf[i], i == 0 ? f32x16{} : s);
-        dp = mfma32<DT>(lds_b128(Vn, ta.rm[i]), of[i], i == 0 ? dinit : dp);
+        s = mfma32<DT>(lds_rowmajor<D>(Kn, ta, i), qf[i], i == 0 ? f32x16{} : s);
+        dp = mfma32<DT>(lds_rowmajor<D>(Vn, ta, i), of[i], i == 0 ? dinit : dp);
       }
       sched_reads_ahead<2 * DB + 2 * KS, 4 * DB + 2 * KS>();
     }
 
     // tile j+2 (read next step) must have landed; tile j+3 may fly on
     if (j + 3 < n_kt) {
-      wait_vmcnt<2 * TC::NI>();
+      wait_vmcnt<2 * NI>();
     } else {
       wait_loads();
     }

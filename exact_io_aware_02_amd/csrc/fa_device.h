@@ -1,6 +1,6 @@
 // Device helpers shared by the gfx950 attention kernels: operand types, the
-// 32x32x16 MFMA wrappers, fp32 -> fp16/bf16 packing, the LDS tile swizzle
-// and the transposing LDS read.
+// 32x32x16 MFMA wrappers, fp32 -> fp16/bf16 packing, the LDS tile layouts
+// with their HBM -> LDS copies and operand reads.
 //
 // Register layouts of v_mfma_f32_32x32x16_{f16,bf16} (one wave, lane i):
 //   A (32 x 16, M x K): lane i holds A[i % 32][8*(i/32) + 0..7]
@@ -64,25 +64,6 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 // Row of the 32x32 accumulator held by lane-half `half` in register r.
 __device__ __forceinline__ int acc_row(int half, int r) { return ((r >> 2) << 3) + (half << 2) + (r & 3); }
 
-// LDS tiles are [rows][D] 16-bit elements, rows of D/8 16-byte chunks; chunk
-// c of row r lives at physical chunk c ^ swz(r).  The XOR keeps every 8-byte
-// group contiguous and makes both read patterns the kernels use free of bank
-// conflicts: 16 consecutive rows at one chunk (128-bit operand reads) and
-// 4 consecutive rows x 4 consecutive chunks (transposing 64-bit reads).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) {
-    return ((r & 3) << 2) | ((r >> 2) & 3);
-  } else {
-    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  }
-}
-// Element offset of (row r, column col) in a swizzled [rows][D] tile.
-template <int D>
-__device__ __forceinline__ int tile_off(int r, int col) {
-  return r * D + ((((col >> 3) ^ swz<D>(r)) << 3) | (col & 7));
-}
-
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane l receives element
 // j (j = 0..3) from the 8-byte word addressed by lane 4*j + (l%16)/4 of the
 // group, at 16-bit offset l%4.  With lane p of a group pointing at
@@ -93,66 +74,148 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_ptr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// A-operand of an MFMA whose k index runs over tile rows (keys or queries)
-// and whose m index runs over the d columns: lane i gets column
-// 32*db + i%32 and rows {kb + 4*(i/32) + 0..3, kb + 8 + 4*(i/32) + 0..3},
-// matching the k order of a 32x32 accumulator's registers 8*kk..8*kk+7
-// (see acc_row).  `kb` is the first of the 16 rows.
-template <int D>
-__device__ __forceinline__ u32x4 load_transposed_a(const uint16_t* tile, int lane, int kb, int db) {
-  const int g = lane >> 4, p = lane & 15;
-  const int row0 = kb + 4 * (g >> 1) + (p >> 2);
-  const int col = db * 32 + 16 * (g & 1) + 4 * (p & 3);
-  u32x2 lo = lds_read_tr16(tile + tile_off<D>(row0, col));
-  u32x2 hi = lds_read_tr16(tile + tile_off<D>(row0 + 8, col));
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
+// ---------------------------------------------------------------- LDS tiles
+//
+// A tile holds 32 rows (keys or queries) of D 16-bit elements.  It is filled
+// by HBM -> LDS copies of 1 KiB per wave instruction (lane i writes bytes
+// 16 i .. 16 i + 15 of the instruction's block; buffer_load ... lds, no
+// staging registers) and read as MFMA operands in two patterns:
+//
+//   row-major operand, k over the d columns: lane i reads the 8 columns
+//     16 ks + 8 (i/32) .. +7 of row i % 32 (one ds_read_b128 per k step ks);
+//   transposed operand, k over the rows, m over the d columns: lane i gets
+//     column 32 db + i%32 of rows {16 kk + 4 (i/32) + 0..3, +8 + 0..3},
+//     matching the k order of a 32x32 accumulator's registers 8 kk .. 8 kk+7
+//     (see acc_row), from two ds_read_b64_tr_b16 whose 16-lane groups each
+//     cover 4 rows x 16 columns.
+//
+// Each layout makes both read patterns free of LDS bank conflicts and lets
+// every group of four lanes of a copy instruction fetch 64 contiguous bytes
+// of one row.  TileLayout<D> holds a lane's read offsets; rm_off(ks) and
+// tr_off(kk, db, hi) are byte offsets from the tile's base (hi: rows +8).
 
-// A- or B-operand whose k index runs over the d columns: 8 consecutive
-// columns 16*ks + 8*(lane/32) .. +7 of tile row `r`.
 template <int D>
-__device__ __forceinline__ u32x4 load_rowmajor_op(const uint16_t* tile, int r, int ks, int half) {
-  const int c = 2 * ks + half;
-  return *(const u32x4*)(tile + r * D + ((c ^ swz<D>(r)) << 3));
-}
+struct TileLayout;
 
-// Per-lane LDS byte offsets of every operand read of a 32-row swizzled
-// [32][D] tile, computed once: the swizzle of the rows a lane touches
-// depends only on the lane (and the 8-row half), never on the k-step, so
-// the reads of any tile slot are `slot base + these offsets + immediates`.
-template <int D>
-struct TileAddr {
-  uint32_t rm[D / 16];     // row-major operand (row = lane % 32), k-step ks
-  uint32_t tr[D / 32][2];  // transposed operand, column block db, rows +0 / +8 (k-block 0)
+// d = 64: rows of 128 bytes (8 chunks of 16 bytes); chunk c of row r lives
+// at physical chunk c ^ swz(r).  The XOR spreads 16 consecutive rows of one
+// chunk and 4 rows x 4 chunks over distinct banks; the k-step offsets of a
+// lane are not affine, so they are kept per lane (6 registers).
+template <>
+struct TileLayout<64> {
+  static constexpr int D = 64;
+  static constexpr int BYTES = 32 * D * 2;
+  static __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+  static __device__ __forceinline__ int elem_off(int r, int col) {
+    return r * D + ((((col >> 3) ^ swz(r)) << 3) | (col & 7));
+  }
+  uint32_t rm[D / 16];
+  uint32_t tr[D / 32][2];
 
   __device__ __forceinline__ void init(int lane) {
     const int col = lane & 31, half = lane >> 5;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) rm[ks] = 2u * (uint32_t)(col * D + (((2 * ks + half) ^ swz<D>(col)) << 3));
+    for (int ks = 0; ks < D / 16; ++ks) rm[ks] = 2u * (uint32_t)(col * D + (((2 * ks + half) ^ swz(col)) << 3));
     const int g = lane >> 4, p = lane & 15;
     const int row0 = 4 * (g >> 1) + (p >> 2);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int c = db * 32 + 16 * (g & 1) + 4 * (p & 3);
-      tr[db][0] = 2u * (uint32_t)tile_off<D>(row0, c);
-      tr[db][1] = 2u * (uint32_t)tile_off<D>(row0 + 8, c);
+      tr[db][0] = 2u * (uint32_t)elem_off(row0, c);
+      tr[db][1] = 2u * (uint32_t)elem_off(row0 + 8, c);
     }
   }
+  __device__ __forceinline__ uint32_t rm_off(int ks) const { return rm[ks]; }
+  // the swizzle repeats every 16 rows, so the k block is a plain row offset
+  __device__ __forceinline__ uint32_t tr_off(int kk, int db, int hi) const { return tr[db][hi] + kk * 16u * D * 2u; }
+
+  // Copy rows [0, 32) of one head's [N][64] tensor (row stride row_bytes,
+  // first row at byte tile_byte_off) into the tile at `lds`, spread over
+  // WAVES waves: lane i of an instruction fetches the global chunk whose
+  // swizzled home is byte 16 i of the instruction's block of 8 rows.
+  template <int WAVES>
+  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t tile_byte_off,
+                                               uint16_t* lds, int lane, int wave) {
+    constexpr int NI = 4 / WAVES;
+    static_assert(NI >= 1 && NI * WAVES == 4, "tile must split evenly over the waves");
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (wave * NI + i) * 8 + lane / 8;
+      const int c = (lane % 8) ^ swz(r);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(lds + (wave * NI + i) * 8 * D), 16,
+          (uint32_t)r * row_bytes + (uint32_t)(c * 16), tile_byte_off, 0, 0);
+    }
+  }
+  template <int WAVES>
+  static constexpr int copy_insts() { return 4 / WAVES; }
 };
 
-// Byte distance between the two 16-row k-blocks of a transposed operand
-// read: the swizzle repeats every 16 rows, so it is a plain row offset.
+// d = 128: 8 blocks of 4 rows, each block 1 KiB of data plus 16 bytes of
+// padding (stride 1040).  Inside a block, chunk c (16 bytes) of row t sits
+// at position 16 (c / 4) + 4 t + c % 4.  So a copy instruction fills one
+// block from 4 consecutive rows, each group of four lanes fetching 64
+// contiguous bytes, and the address of (row r, chunk c) splits into a row
+// part and a chunk part: every read of a tile is one per-lane base plus
+// immediate offsets (no per-k-step address registers or adds).  The
+// 16-byte shift per block plus the 4 t term put 16 consecutive rows of one
+// chunk, and 4 rows x 4 consecutive chunks, on distinct banks.
+template <>
+struct TileLayout<128> {
+  static constexpr int BLK = 1040;
+  static constexpr int BYTES = 8 * BLK;
+  uint32_t rb, tb;  // lane bases of the row-major and transposed reads
+
+  __device__ __forceinline__ void init(int lane) {
+    const int r = lane & 31, h = lane >> 5;
+    rb = (uint32_t)((r >> 2) * BLK + (4 * (r & 3) + h) * 16);
+    const int g = lane >> 4, p = lane & 15;
+    tb = (uint32_t)((g >> 1) * BLK + (4 * (p >> 2) + 2 * (g & 1) + ((p >> 1) & 1)) * 16 + (p & 1) * 8);
+  }
+  __device__ __forceinline__ uint32_t rm_off(int ks) const { return rb + 256u * (ks >> 1) + 32u * (ks & 1); }
+  __device__ __forceinline__ uint32_t tr_off(int kk, int db, int hi) const {
+    return tb + (uint32_t)(kk * 4 * BLK + db * 256 + hi * 2 * BLK);
+  }
+
+  // Copy rows [0, 32) of one head's [N][128] tensor (row stride row_bytes,
+  // first row at byte tile_byte_off) into the tile at `lds`, one block per
+  // instruction, spread over WAVES waves.
+  template <int WAVES>
+  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t tile_byte_off,
+                                               uint16_t* lds, int lane, int wave) {
+    constexpr int NI = 8 / WAVES;
+    static_assert(NI >= 1 && NI * WAVES == 8, "tile must split evenly over the waves");
+    const int t = (lane >> 2) & 3, c = 4 * (lane >> 4) + (lane & 3);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int b = wave * NI + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)((char*)lds + b * BLK), 16,
+          (uint32_t)(4 * b + t) * row_bytes + (uint32_t)(c * 16), tile_byte_off, 0, 0);
+    }
+  }
+  template <int WAVES>
+  static constexpr int copy_insts() { return 8 / WAVES; }
+};
+
+// Elements of one 32-row tile slot (16-bit units), for sizing LDS rings.
 template <int D>
-constexpr uint32_t kTrKBlockBytes = 16u * D * 2u;
+constexpr int kTileElems = TileLayout<D>::BYTES / 2;
 
 __device__ __forceinline__ u32x4 lds_b128(const uint16_t* base, uint32_t byte_off) {
   return *(const u32x4*)((const char*)base + byte_off);
 }
+// Row-major operand of k step ks.
 template <int D>
-__device__ __forceinline__ u32x4 lds_transposed_a(const uint16_t* base, const TileAddr<D>& ta, int kk, int db) {
-  const char* b = (const char*)base + kk * kTrKBlockBytes<D>;
-  u32x2 lo = lds_read_tr16((const uint16_t*)(b + ta.tr[db][0]));
-  u32x2 hi = lds_read_tr16((const uint16_t*)(b + ta.tr[db][1]));
+__device__ __forceinline__ u32x4 lds_rowmajor(const uint16_t* base, const TileLayout<D>& ta, int ks) {
+  return lds_b128(base, ta.rm_off(ks));
+}
+// Transposed operand of k block kk (rows 16 kk ..) and d block db.
+template <int D>
+__device__ __forceinline__ u32x4 lds_transposed_a(const uint16_t* base, const TileLayout<D>& ta, int kk, int db) {
+  const char* b = (const char*)base;
+  u32x2 lo = lds_read_tr16((const uint16_t*)(b + ta.tr_off(kk, db, 0)));
+  u32x2 hi = lds_read_tr16((const uint16_t*)(b + ta.tr_off(kk, db, 1)));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -206,34 +269,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t f32_rsrc(const float* base, int n) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n * 4, 0x00020000);
 }
-
-// Asynchronous copies of ROWS consecutive rows of one head's [N][D] tensor
-// into a swizzled [ROWS][D] LDS tile, spread over WAVES waves.  Each wave
-// instruction moves 1 KiB: lane i fills LDS bytes 16*i .. 16*i+15 of its
-// block, so it fetches the global 16-byte chunk whose swizzled home is that
-// slot (buffer_load ... lds; no registers are staged).
-template <int D, int ROWS, int WAVES>
-struct TileCopyT {
-  static constexpr int CH = D / 8;               // 16-byte chunks per row
-  static constexpr int RPI = 64 / CH;            // rows per wave instruction
-  static constexpr int NI = ROWS / RPI / WAVES;  // instructions per wave per tile
-  static_assert(NI >= 1 && NI * RPI * WAVES == ROWS, "tile must split evenly over the waves");
-
-  // row_bytes: the tensor's row stride in bytes; tile_byte_off: byte offset
-  // of the tile's first row (both wave-uniform).
-  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t tile_byte_off,
-                                               uint16_t* lds, int lane, int wave) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = (wave * NI + i) * RPI + lane / CH;
-      const int c = (lane % CH) ^ swz<D>(r);
-      const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)(c * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(lds + (wave * NI + i) * RPI * D), 16, voff, tile_byte_off, 0,
-          0);
-    }
-  }
-};
 
 // Asynchronous copy of N fp32 values (N a multiple of 4, at most 256) into
 // LDS by one wave; lanes past N/4 are idle.

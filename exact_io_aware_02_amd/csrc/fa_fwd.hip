@@ -68,8 +68,15 @@ struct FwdTile {
   static constexpr bool SEP_S = D == 128;
 };
 
+static_assert(kBN == 32, "K/V tiles are the 32-row tiles of fa_device.h");
 template <int D>
-using TileCopy = TileCopyT<D, kBN, kWaves>;
+struct TileCopy {
+  static constexpr int NI = TileLayout<D>::template copy_insts<kWaves>();  // instructions per wave per tile
+  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t tile_byte_off,
+                                               uint16_t* lds, int lane, int wave) {
+    TileLayout<D>::template issue<kWaves>(rs, row_bytes, tile_byte_off, lds, lane, wave);
+  }
+};
 
 template <int DT>
 __device__ __forceinline__ float dot2_sum(uint32_t packed, float acc);
@@ -180,7 +187,7 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
                                          __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, uint32_t krow,
                                          uint32_t vrow, uint32_t ktb, uint32_t vtb, const u32x4 (&qf)[kNQB][D / 16],
                                          f32x16 (&acc)[D / 32][kNQB], RowState<kNQB>& st, int Nk, int wl, int wr,
-                                         int qw0, float c, int lane, int wave, const TileAddr<D>& ta,
+                                         int qw0, float c, int lane, int wave, const TileLayout<D>& ta,
                                          const DropoutParams& dp, uint32_t bh) {
   using TC = TileCopy<D>;
   constexpr int KS = D / 16;
@@ -209,7 +216,7 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
   u32x4 ka[KS];
   if constexpr (!kSep || FIRST) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_b128(Kn, ta.rm[ks]);
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_rowmajor<D>(Kn, ta, ks);
   }
   u32x4 rnd[kNQB];
 #pragma unroll
@@ -243,12 +250,12 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
       {  // K(j+1) operand of k step ks, kKLead k steps ahead of its MFMAs
         const int ks = (g - NPVM / 2) / CPK * (kNQB == 1 ? 2 : 1) + kKLead;
         if ((g - NPVM / 2) % CPK == 0 && ks >= 0 && ks < KS) {
-          ka[ks] = lds_b128(Kn, ta.rm[ks]);
-          if (kNQB == 1 && ks + 1 < KS) ka[ks + 1] = lds_b128(Kn, ta.rm[ks + 1]);
+          ka[ks] = lds_rowmajor<D>(Kn, ta, ks);
+          if (kNQB == 1 && ks + 1 < KS) ka[ks + 1] = lds_rowmajor<D>(Kn, ta, ks + 1);
         }
         if (g == NPVM / 2 - 1) {  // the first k steps
 #pragma unroll
-          for (int k0 = 0; k0 < kKLead && k0 < KS; ++k0) ka[k0] = lds_b128(Kn, ta.rm[k0]);
+          for (int k0 = 0; k0 < kKLead && k0 < KS; ++k0) ka[k0] = lds_rowmajor<D>(Kn, ta, k0);
         }
       }
 #pragma unroll
@@ -317,7 +324,7 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
       for (int nb = 0; nb < kNQB; ++nb) so[nb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 a = lds_b128(Kj, ta.rm[ks]);
+        const u32x4 a = lds_rowmajor<D>(Kj, ta, ks);
 #pragma unroll
         for (int nb = 0; nb < kNQB; ++nb) so[nb] = mfma32<DT>(a, qf[nb][ks], so[nb]);
       }
@@ -377,7 +384,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NBUF = 4;  // K/V ring (see fwd_step)
-  constexpr int TILE = kBN * D;
+  constexpr int TILE = kTileElems<D>;
 
   // One LDS object for the whole ring: the compiler gives every separate
   // __shared__ variable its own alias scope, and then makes each LDS read
@@ -467,7 +474,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   }
   const float c = p.c;
 
-  TileAddr<D> ta;
+  TileLayout<D> ta;
   ta.init(lane);
 
   // tiles jt0 and jt0+1 landed (K(jt0) for S(jt0) now, V(jt0) and
@@ -493,7 +500,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
     for (int nb = 0; nb < kNQB; ++nb) sa[nb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 a = lds_b128(Ks[0], ta.rm[ks]);
+      const u32x4 a = lds_rowmajor<D>(Ks[0], ta, ks);
 #pragma unroll
       for (int nb = 0; nb < kNQB; ++nb) sa[nb] = mfma32<DT>(a, qf[nb][ks], sa[nb]);
     }
@@ -503,8 +510,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
     }
     u32x4 pf[2][kNQB];
     u32x4 va[2][DB];
-    // with S(j+1) in registers of its own it is copied back to sa after
-    // each step (unrolling by two to alternate instead spills at d = 128)
+    // with S(j+1) in registers of its own, sa and sb alternate
     f32x16 sb[kNQB];
     fwd_step<D, DT, BAND, DROP, true>(jt0, n_kt, sa, sb, pf, va, Ks[0], Ks[1], Vs[0], Ks[kSep ? 0 : 3], Vs[3], krs, vrs, krow,
                                       vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta, p.drop,
@@ -513,7 +519,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
 #pragma unroll
       for (int nb = 0; nb < kNQB; ++nb) sa[nb] = sb[nb];
     }
-    for (int j = jt0 + 1; j < n_kt; ++j) {
+    int j = jt0 + 1;
+    if constexpr (kSep) {
+      // two steps per iteration with the roles of sa and sb swapped, so
+      // S(j+1) is not copied back every step
+      for (; j + 1 < n_kt; j += 2) {
+        const int sl = (j - jt0) & 3, sl2 = (sl + 1) & 3;
+        fwd_step<D, DT, BAND, DROP, false>(j, n_kt, sa, sb, pf, va, Ks[sl], Ks[sl2], Vs[sl], Ks[sl], Vs[(sl + 3) & 3], krs,
+                                           vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta,
+                                           p.drop, (uint32_t)bh);
+        fwd_step<D, DT, BAND, DROP, false>(j + 1, n_kt, sb, sa, pf, va, Ks[sl2], Ks[(sl2 + 1) & 3], Vs[sl2], Ks[sl2],
+                                           Vs[sl], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c,
+                                           lane, wave, ta, p.drop, (uint32_t)bh);
+      }
+    }
+    for (; j < n_kt; ++j) {
       const int sl = (j - jt0) & 3;
       fwd_step<D, DT, BAND, DROP, false>(j, n_kt, sa, sb, pf, va, Ks[sl], Ks[(sl + 1) & 3], Vs[sl],
                                          Ks[kSep ? sl : (sl + 3) & 3], Vs[(sl + 3) & 3], krs, vrs, krow, vrow, ktb, vtb, qf, acc,
