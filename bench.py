@@ -26,13 +26,21 @@ dropout_p); plus the fp8 forward alone on the inputs cast to float8_e4m3fn
 
 cpu_baseline: the fp64 numpy oracle (test infrastructure) on four heads of the
 same workload, forward + backward, timed on the host cores.
+
+power_context: under load the chip runs at its power cap and lowers its
+clock; the forward is run back to back for a few seconds while amd-smi reads
+the GFX clock and socket power, and so is a bf16 GEMM of 8192^3 (torch.matmul
+on random operands) as the dense-MFMA rate a tuned library reaches under
+the same cap.
 """
 import argparse
 import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +63,82 @@ def kernel_source_hash():
         with open(os.path.join(ROOT, "exact_io_aware_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def smi_sample():
+    """(mean GFX clock in MHz over the XCDs, socket power in W) read with
+    amd-smi in a child process, or None where it is unavailable."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--power", "--clock", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        txt = r.stdout
+        d, _ = json.JSONDecoder().raw_decode(txt[txt.index("["):])
+        g = d[0]
+        clks = [v["clk"]["value"] for kk, v in g["clock"].items()
+                if kk.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        return float(sum(clks)) / len(clks), float(g["power"]["socket_power"]["value"])
+    except Exception:
+        return None
+
+
+def sustained(torch, fn, seconds, stream):
+    """Run fn back to back for about `seconds` while a second thread samples
+    the clock and power twice; returns (ms per call, MHz, W)."""
+    samples = []
+
+    def sampler():
+        time.sleep(min(1.5, seconds / 3))
+        for _ in range(2):
+            x = smi_sample()
+            if x is not None:
+                samples.append(x)
+            time.sleep(0.3)
+
+    th = threading.Thread(target=sampler)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    e0.record(stream)
+    while n == 0 or th.is_alive() or time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    th.join()
+    ms = e0.elapsed_time(e1) / n
+    if not samples:
+        return ms, None, None
+    return ms, sum(x[0] for x in samples) / len(samples), sum(x[1] for x in samples) / len(samples)
+
+
+def power_context(torch, fa, q, k, v, o, lse, s, causal, stream, fwd_flop, peak):
+    """The chip's power cap sets its clock under load: the forward back to
+    back with amd-smi's clock and power readings, beside a large bf16 GEMM
+    (torch.matmul, hipBLASLt) on random N(0,1) operands as the dense-MFMA
+    rate a tuned library reaches under the same cap."""
+    out = {}
+    ms, mhz, w = sustained(torch, lambda: fa.fa_fwd(q, k, v, o, lse, s, causal, stream), 4.0, stream)
+    tf = fwd_flop / ms / 1e9
+    out["fwd"] = {"ms": ms, "tflops": tf, "sclk_mhz": mhz, "socket_power_w": w}
+    n = 8192
+    g = torch.Generator(device="cpu").manual_seed(11)
+    a = torch.randn(n, n, generator=g).to(torch.bfloat16).to(q.device)
+    b = torch.randn(n, n, generator=g).to(torch.bfloat16).to(q.device)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=q.device)
+    ms_g, mhz_g, w_g = sustained(torch, lambda: torch.matmul(a, b, out=c), 4.0, stream)
+    tf_g = 2.0 * n ** 3 / ms_g / 1e9
+    out["gemm_bf16"] = {"m_n_k": [n, n, n], "ms": ms_g, "tflops": tf_g, "frac_of_peak": tf_g / peak,
+                        "sclk_mhz": mhz_g, "socket_power_w": w_g}
+    out["fwd_frac_of_gemm"] = tf / tf_g
+    if mhz:
+        out["fwd_frac_of_peak_at_sclk"] = tf / (peak * mhz / 2400.0)
+    del a, b, c
+    return out
 
 
 def measured_traffic(kernel):
@@ -221,6 +305,8 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 times), so a counter "
                          "profile of this command can calibrate FETCH_SIZE/WRITE_SIZE against known bytes")
+    ap.add_argument("--no-power-context", action="store_true",
+                    help="skip the clock/power readings and the GEMM comparison")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -349,6 +435,12 @@ def main():
         "roofline": roof(dominant),
         "roofline_fwd": roof("fwd"),
     }
+    if not args.no_power_context:
+        out["power_context"] = power_context(torch, fa, q, k, v, o, lse, s, causal, stream, fwd_flop, peak)
+        pc = out["power_context"]
+        log("power context: fwd %.1f TFLOP/s at %s MHz / %s W; bf16 GEMM 8192^3 %.1f TFLOP/s at %s MHz / %s W" % (
+            pc["fwd"]["tflops"], pc["fwd"]["sclk_mhz"], pc["fwd"]["socket_power_w"], pc["gemm_bf16"]["tflops"],
+            pc["gemm_bf16"]["sclk_mhz"], pc["gemm_bf16"]["socket_power_w"]))
     if not args.no_rows_f:
         out["rows_f"] = next_rows(fa, torch, q, k, v, do, s, stream, peak, min(K, 10))
     if not args.no_cpu_baseline:
