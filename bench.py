@@ -27,6 +27,9 @@ dropout_p); plus the fp8 forward alone on the inputs cast to float8_e4m3fn
 cpu_baseline: the fp64 numpy oracle (test infrastructure) on four heads of the
 same workload, forward + backward, timed on the host cores.
 
+small_configs: the four smaller workloads (forward; forward and backward
+for the training-step one), per-launch median and back-to-back loop times.
+
 power_context: under load the chip runs at its power cap and lowers its
 clock; the forward is run back to back for a few seconds while amd-smi reads
 the GFX clock and socket power, and so is a bf16 GEMM of 8192^3 (torch.matmul
@@ -138,6 +141,65 @@ def power_context(torch, fa, q, k, v, o, lse, s, causal, stream, fwd_flop, peak)
     if mhz:
         out["fwd_frac_of_peak_at_sclk"] = tf / (peak * mhz / 2400.0)
     del a, b, c
+    return out
+
+
+def small_configs(fa, torch, stream, peak_of):
+    """The four smaller workloads (the 16K one is the step above), timed the
+    way the pages time attention: 10 warm-up launches, then 100 launches,
+    each bracketed by HIP events (median per launch) and the whole loop
+    (back-to-back average, which hides launch gaps).  These run in
+    microseconds on at most 256 workgroups, so they are launch- and
+    occupancy-bound; their fraction of peak is context, not a target."""
+    from attn_inputs import WORKLOADS, make_qkv
+
+    def timed(fn):
+        for _ in range(10):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+        l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        med = sorted(a.elapsed_time(b) for a, b in ev)[50]
+        l0.record(stream)
+        for _ in range(100):
+            fn()
+        l1.record(stream)
+        torch.cuda.synchronize()
+        return med, l0.elapsed_time(l1) / 100
+
+    out = {}
+    for name, w in WORKLOADS.items():
+        if w.N >= 16384:
+            continue
+        inp = make_qkv(w.B, w.H, w.N, w.N, w.d, w.dtype, w.layout, seed=w.seed, in_scale=w.in_scale,
+                       with_do=w.backward)
+        q, k, v = (inp[x].to(stream.device) for x in ("q", "k", "v"))
+        s = 1.0 / math.sqrt(w.d)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+        peak = peak_of(w.dtype)
+        for causal in w.causal:
+            flop = 4.0 * w.B * w.H * w.N * w.N * w.d / (2 if causal else 1)
+            med, loop = timed(lambda: fa.fa_fwd_ex(q, k, v, o, lse, s, causal, (-1, -1), w.layout, stream))
+            key = "%s%s fwd" % (name, "" if len(w.causal) == 1 else (" causal" if causal else " noncausal"))
+            out[key] = {"median_ms": med, "loop_ms": loop, "tflops_loop": flop / loop / 1e9,
+                        "frac_of_peak_loop": flop / loop / 1e9 / peak}
+            if w.backward:
+                do = inp["do"].to(q.device)
+                dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+                ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.N, w.d, fa.FA_FP16 if w.dtype == "fp16"
+                                                           else fa.FA_BF16), dtype=torch.uint8, device=q.device)
+                med, loop = timed(lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, stream))
+                out[name + " bwd"] = {"median_ms": med, "loop_ms": loop, "tflops_loop": 2.5 * flop / loop / 1e9,
+                                      "frac_of_peak_loop": 2.5 * flop / loop / 1e9 / peak}
+    for kk, r in out.items():
+        log("  %-52s median %.4f ms, loop %.4f ms, %.1f TFLOP/s (%.1f%% of peak)" % (
+            kk, r["median_ms"], r["loop_ms"], r["tflops_loop"], 100 * r["frac_of_peak_loop"]))
     return out
 
 
@@ -307,6 +369,8 @@ def main():
                          "profile of this command can calibrate FETCH_SIZE/WRITE_SIZE against known bytes")
     ap.add_argument("--no-power-context", action="store_true",
                     help="skip the clock/power readings and the GEMM comparison")
+    ap.add_argument("--no-small-configs", action="store_true",
+                    help="skip timing the four smaller workloads")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -441,6 +505,9 @@ def main():
         log("power context: fwd %.1f TFLOP/s at %s MHz / %s W; bf16 GEMM 8192^3 %.1f TFLOP/s at %s MHz / %s W" % (
             pc["fwd"]["tflops"], pc["fwd"]["sclk_mhz"], pc["fwd"]["socket_power_w"], pc["gemm_bf16"]["tflops"],
             pc["gemm_bf16"]["sclk_mhz"], pc["gemm_bf16"]["socket_power_w"]))
+    if not args.no_small_configs:
+        log("smaller workloads:")
+        out["small_configs"] = small_configs(fa, torch, stream, lambda dt: PEAK_TFLOPS[dt])
     if not args.no_rows_f:
         out["rows_f"] = next_rows(fa, torch, q, k, v, do, s, stream, peak, min(K, 10))
     if not args.no_cpu_baseline:

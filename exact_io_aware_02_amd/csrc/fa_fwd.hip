@@ -2,9 +2,10 @@
 //
 // One workgroup of 4 waves owns BM query rows of one (batch, head); each
 // wave owns 32 of them at d = 128 (64, as two 32-query MFMA column blocks,
-// at d = 64) and their softmax state, so the row max and row sum never
-// leave the wave (FlashAttention-2's point of less communication between
-// warps, refbase Q&A on FA2's improvements).  K/V tiles of BN = 32 keys
+// at d = 64, or 32 when that grid would leave CUs idle) and their softmax
+// state, so the row max and row sum never leave the wave (FlashAttention-2's
+// point of less communication between warps, refbase Q&A on FA2's
+// improvements).  K/V tiles of BN = 32 keys
 // stream from HBM straight into LDS (buffer_load ... lds, no staging
 // registers) through a 4-slot ring.  Per tile and wave:
 //
@@ -56,10 +57,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 32;            // keys per pipeline tile
 // Queries per wave are 32 * NQB (NQB = 32-query MFMA column blocks): 64
-// halves the LDS bytes per MFMA but needs ~260 registers at d = 128.
-template <int D>
+// halves the LDS bytes per MFMA but needs ~260 registers at d = 128.  At
+// d = 64, grids too small to give every CU two workgroups use NQB = 1
+// (twice the workgroups, half the work per step of a wave).
+template <int D, int NQB_ = (D == 64 ? 2 : 1)>
 struct FwdTile {
-  static constexpr int NQB = D == 64 ? 2 : 1;
+  static constexpr int NQB = NQB_;
   static constexpr int QW = 32 * NQB;       // queries per wave
   static constexpr int BM = kWaves * QW;    // queries per workgroup
   static constexpr int WAVES_PER_SIMD = 2;
@@ -375,12 +378,12 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int DT, bool BAND, bool DROP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTile<D>::WAVES_PER_SIMD,
-                                                                          FwdTile<D>::WAVES_PER_SIMD))) void fwd_kernel(FwdParams p) {
-  constexpr int kNQB = FwdTile<D>::NQB;
-  constexpr int kQW = FwdTile<D>::QW;
-  constexpr int kBM = FwdTile<D>::BM;
+template <int D, int DT, bool BAND, bool DROP, int NQB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTile<D, NQB>::WAVES_PER_SIMD,
+                                                                          FwdTile<D, NQB>::WAVES_PER_SIMD))) void fwd_kernel(FwdParams p) {
+  constexpr int kNQB = NQB;
+  constexpr int kQW = FwdTile<D, NQB>::QW;
+  constexpr int kBM = FwdTile<D, NQB>::BM;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NBUF = 4;  // K/V ring (see fwd_step)
@@ -575,20 +578,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   }
 }
 
-template <int D, int DT, bool BAND, bool DROP>
+template <int D, int DT, bool BAND, bool DROP, int NQB>
 hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
-  constexpr int kBM = FwdTile<D>::BM;
+  constexpr int kBM = FwdTile<D, NQB>::BM;
   const int n_qt = (p.Nq + kBM - 1) / kBM;
   const int64_t blocks = (int64_t)n_qt * p.B * p.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND, DROP>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND, DROP, NQB>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
+template <int D, int DT, int NQB>
+hipError_t launch_dcn(const FwdParams& p, bool banded, hipStream_t stream) {
+  if (p.drop.thr > 0)
+    return banded ? launch_t<D, DT, true, true, NQB>(p, stream) : launch_t<D, DT, false, true, NQB>(p, stream);
+  return banded ? launch_t<D, DT, true, false, NQB>(p, stream) : launch_t<D, DT, false, false, NQB>(p, stream);
+}
+
+// Workgroups that fill every CU twice (two waves per SIMD).
+constexpr int64_t kFullGrid = 512;
+
 template <int D, int DT>
 hipError_t launch_dc(const FwdParams& p, bool banded, hipStream_t stream) {
-  if (p.drop.thr > 0) return banded ? launch_t<D, DT, true, true>(p, stream) : launch_t<D, DT, false, true>(p, stream);
-  return banded ? launch_t<D, DT, true, false>(p, stream) : launch_t<D, DT, false, false>(p, stream);
+  if constexpr (D == 64) {
+    constexpr int BM2 = FwdTile<64, 2>::BM;
+    const int64_t blocks2 = (int64_t)((p.Nq + BM2 - 1) / BM2) * p.B * p.H;
+    if (blocks2 < kFullGrid) return launch_dcn<D, DT, 1>(p, banded, stream);
+    return launch_dcn<D, DT, 2>(p, banded, stream);
+  } else {
+    return launch_dcn<D, DT, FwdTile<D>::NQB>(p, banded, stream);
+  }
 }
 
 }  // namespace
