@@ -28,7 +28,8 @@ cpu_baseline: the fp64 numpy oracle (test infrastructure) on four heads of the
 same workload, forward + backward, timed on the host cores.
 
 small_configs: the four smaller workloads (forward; forward and backward
-for the training-step one), per-launch median and back-to-back loop times.
+for the training-step one), timed per launch from a replayed HIP graph and
+from a Python loop.
 
 power_context: under load the chip runs at its power cap and lowers its
 clock; the forward is run back to back for a few seconds while amd-smi reads
@@ -145,32 +146,49 @@ def power_context(torch, fa, q, k, v, o, lse, s, causal, stream, fwd_flop, peak)
 
 
 def small_configs(fa, torch, stream, peak_of):
-    """The four smaller workloads (the 16K one is the step above), timed the
-    way the pages time attention: 10 warm-up launches, then 100 launches,
-    each bracketed by HIP events (median per launch) and the whole loop
-    (back-to-back average, which hides launch gaps).  These run in
-    microseconds on at most 256 workgroups, so they are launch- and
-    occupancy-bound; their fraction of peak is context, not a target."""
+    """The four smaller workloads (the 16K one is the step above).  They
+    run in microseconds, less than the Python binding takes to launch them,
+    so each is timed two ways: 20 launches captured in a HIP graph and
+    replayed 10 times (GPU time per launch, no host gaps), and 100 launches
+    from Python back to back (what an eager caller sees).  With at most 512
+    workgroups they are occupancy- and latency-bound; their fraction of
+    peak is context, not a target."""
     from attn_inputs import WORKLOADS, make_qkv
 
-    def timed(fn):
+    def graph_ms(fn):
+        side = torch.cuda.Stream(device=stream.device)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            for _ in range(20):
+                fn(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         for _ in range(10):
-            fn()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
-        l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g.replay()
+        e1.record(stream)
         torch.cuda.synchronize()
-        for a, b in ev:
-            a.record(stream)
-            fn()
-            b.record(stream)
+        return e0.elapsed_time(e1) / 200
+
+    def eager_ms(fn):
+        for _ in range(10):
+            fn(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        med = sorted(a.elapsed_time(b) for a, b in ev)[50]
-        l0.record(stream)
+        e0.record(stream)
         for _ in range(100):
-            fn()
-        l1.record(stream)
+            fn(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        return med, l0.elapsed_time(l1) / 100
+        return e0.elapsed_time(e1) / 100
 
     out = {}
     for name, w in WORKLOADS.items():
@@ -185,21 +203,23 @@ def small_configs(fa, torch, stream, peak_of):
         peak = peak_of(w.dtype)
         for causal in w.causal:
             flop = 4.0 * w.B * w.H * w.N * w.N * w.d / (2 if causal else 1)
-            med, loop = timed(lambda: fa.fa_fwd_ex(q, k, v, o, lse, s, causal, (-1, -1), w.layout, stream))
+            fwd = lambda st: fa.fa_fwd_ex(q, k, v, o, lse, s, causal, (-1, -1), w.layout, st)
+            gm, em = graph_ms(fwd), eager_ms(fwd)
             key = "%s%s fwd" % (name, "" if len(w.causal) == 1 else (" causal" if causal else " noncausal"))
-            out[key] = {"median_ms": med, "loop_ms": loop, "tflops_loop": flop / loop / 1e9,
-                        "frac_of_peak_loop": flop / loop / 1e9 / peak}
+            out[key] = {"graph_ms": gm, "eager_loop_ms": em, "tflops": flop / gm / 1e9,
+                        "frac_of_peak": flop / gm / 1e9 / peak}
             if w.backward:
                 do = inp["do"].to(q.device)
                 dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
                 ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.N, w.d, fa.FA_FP16 if w.dtype == "fp16"
                                                            else fa.FA_BF16), dtype=torch.uint8, device=q.device)
-                med, loop = timed(lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, stream))
-                out[name + " bwd"] = {"median_ms": med, "loop_ms": loop, "tflops_loop": 2.5 * flop / loop / 1e9,
-                                      "frac_of_peak_loop": 2.5 * flop / loop / 1e9 / peak}
+                bwd = lambda st: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, st)
+                gm, em = graph_ms(bwd), eager_ms(bwd)
+                out[name + " bwd"] = {"graph_ms": gm, "eager_loop_ms": em, "tflops": 2.5 * flop / gm / 1e9,
+                                      "frac_of_peak": 2.5 * flop / gm / 1e9 / peak}
     for kk, r in out.items():
-        log("  %-52s median %.4f ms, loop %.4f ms, %.1f TFLOP/s (%.1f%% of peak)" % (
-            kk, r["median_ms"], r["loop_ms"], r["tflops_loop"], 100 * r["frac_of_peak_loop"]))
+        log("  %-52s graph %.4f ms, eager loop %.4f ms, %.1f TFLOP/s (%.1f%% of peak)" % (
+            kk, r["graph_ms"], r["eager_loop_ms"], r["tflops"], 100 * r["frac_of_peak"]))
     return out
 
 
