@@ -177,6 +177,14 @@ __device__ __forceinline__ void wait_ring(int later) {
   }
 }
 
+// At d = 64 a dK/dV wave needs at most 128 registers, so two workgroups
+// share a CU (four waves per SIMD: measured 20% faster than two; at d = 128,
+// one), and a dQ wave at most 168 (three per SIMD: 10% faster than two).
+template <int D>
+constexpr int kDkvWavesPerSimd = D == 64 ? 4 : 2;
+template <int D>
+constexpr int kDqWavesPerSimd = D == 64 ? 3 : 2;
+
 // ------------------------------------------------------------ dK, dV
 // Eight waves in four pairs.  The two waves of a pair own the same 32 keys
 // and, with waves placed on SIMDs round-robin, the same SIMD; they split
@@ -194,7 +202,7 @@ __device__ __forceinline__ void wait_ring(int later) {
 // Query tiles (Q, dO and the two row statistics) stream HBM -> LDS through
 // a 4-slot ring; tile t+3 is requested in phase 2 of step t.
 template <int D, int DT, bool BAND, bool DROP>
-__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(kDkvWavesPerSimd<D>, kDkvWavesPerSimd<D>))) void dkdv_kernel(BwdParams p) {
   constexpr int KW = 32;            // keys per pair
   constexpr int NPAIR = kWaves;     // pairs per workgroup
   constexpr int BNK = NPAIR * KW;   // keys per workgroup
@@ -529,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdParams p, int 
 // Each wave alternates a VALU phase and an MFMA phase; the two waves on a
 // SIMD (two workgroups) fill each other's phases.
 template <int D, int DT, bool BAND, bool DROP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWavesPerSimd<D>, kDqWavesPerSimd<D>))) void dq_kernel(BwdParams p) {
   constexpr int QW = 32;
   constexpr int BM = kWaves * QW;
   constexpr int KS = D / 16;

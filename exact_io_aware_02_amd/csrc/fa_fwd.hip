@@ -1,12 +1,10 @@
 // Forward attention kernel for gfx950.
 //
-// One workgroup of 4 waves owns BM query rows of one (batch, head); each
-// wave owns 32 of them at d = 128 (64, as two 32-query MFMA column blocks,
-// at d = 64, or 32 when that grid would leave CUs idle) and their softmax
-// state, so the row max and row sum never leave the wave (FlashAttention-2's
-// point of less communication between warps, refbase Q&A on FA2's
-// improvements).  K/V tiles of BN = 32 keys
-// stream from HBM straight into LDS (buffer_load ... lds, no staging
+// One workgroup of 4 waves owns BM = 128 query rows of one (batch, head);
+// each wave owns 32 of them and their softmax state, so the row max and row
+// sum never leave the wave (FlashAttention-2's point of less communication
+// between warps, refbase Q&A on FA2's improvements).  K/V tiles of BN = 32
+// keys stream from HBM straight into LDS (buffer_load ... lds, no staging
 // registers) through a 4-slot ring.  Per tile and wave:
 //
 //   S^T = K_j Q^T          32x32x16 MFMAs; A = K rows from LDS, B = Q held
@@ -56,18 +54,19 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 32;            // keys per pipeline tile
-// Queries per wave are 32 * NQB (NQB = 32-query MFMA column blocks): 64
-// halves the LDS bytes per MFMA but needs ~260 registers at d = 128.  At
-// d = 64, grids too small to give every CU two workgroups use NQB = 1
-// (twice the workgroups, half the work per step of a wave).
-template <int D, int NQB_ = (D == 64 ? 2 : 1)>
+// Queries per wave are 32 * NQB (NQB = 32-query MFMA column blocks).  64
+// halves the LDS bytes per MFMA but needs ~260 registers at d = 128 and
+// ~220 at d = 64 (two waves per SIMD); 32 at d = 64 needs ~140, which lets
+// three waves share a SIMD and doubles the workgroups of small grids
+// (measured faster at every size tried).
+template <int D, int NQB_ = 1>
 struct FwdTile {
   static constexpr int NQB = NQB_;
   static constexpr int QW = 32 * NQB;       // queries per wave
   static constexpr int BM = kWaves * QW;    // queries per workgroup
-  static constexpr int WAVES_PER_SIMD = 2;
-  // S(j+1) in registers of its own (d = 128; at d = 64 the two query
-  // blocks leave no room, so S(j+1) overwrites S(j) after the weights)
+  static constexpr int WAVES_PER_SIMD = (D == 64 && NQB == 1) ? 3 : 2;
+  // S(j+1) in registers of its own at d = 128; at d = 64 it overwrites S(j)
+  // after the weights (fewer registers, so three waves fit a SIMD)
   static constexpr bool SEP_S = D == 128;
 };
 
@@ -595,19 +594,9 @@ hipError_t launch_dcn(const FwdParams& p, bool banded, hipStream_t stream) {
   return banded ? launch_t<D, DT, true, false, NQB>(p, stream) : launch_t<D, DT, false, false, NQB>(p, stream);
 }
 
-// Workgroups that fill every CU twice (two waves per SIMD).
-constexpr int64_t kFullGrid = 512;
-
 template <int D, int DT>
 hipError_t launch_dc(const FwdParams& p, bool banded, hipStream_t stream) {
-  if constexpr (D == 64) {
-    constexpr int BM2 = FwdTile<64, 2>::BM;
-    const int64_t blocks2 = (int64_t)((p.Nq + BM2 - 1) / BM2) * p.B * p.H;
-    if (blocks2 < kFullGrid) return launch_dcn<D, DT, 1>(p, banded, stream);
-    return launch_dcn<D, DT, 2>(p, banded, stream);
-  } else {
-    return launch_dcn<D, DT, FwdTile<D>::NQB>(p, banded, stream);
-  }
+  return launch_dcn<D, DT, FwdTile<D>::NQB>(p, banded, stream);
 }
 
 }  // namespace

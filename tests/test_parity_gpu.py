@@ -401,13 +401,11 @@ def test_large_grid_sampled_rows():
 
 
 @pytest.mark.parametrize("dtype,causal", [("bf16", False), ("fp16", True)])
-def test_d64_grid_at_two_query_blocks_per_wave(dtype, causal):
-    """At d = 64 the forward gives each wave 64 queries once the grid fills
-    every CU twice (B*H*ceil(N/256) >= 512 workgroups), and 32 below that;
-    the other d = 64 cases are small grids.  4 x 32 heads of 1024 tokens sit
-    exactly at the switch: every head against the oracle."""
+def test_d64_full_chip_every_head(dtype, causal):
+    """A d = 64 grid that fills the chip (4 x 32 heads of 1024 tokens: 1024
+    forward workgroups, three per CU): every head against the oracle."""
     B, H, N, d = 4, 32, 1024, 64
-    say("case d64_full_grid %s causal=%s" % (dtype, causal))
+    say("case d64_full_chip %s causal=%s" % (dtype, causal))
     inp = make_qkv(B, H, N, N, d, dtype, seed=47)
     o, lse = fwd_gpu(inp, causal, 1 / 8.0, "bhsd")
     q, k, v = (to_bhsd64(inp[x]) for x in ("q", "k", "v"))
