@@ -346,8 +346,14 @@ __device__ __forceinline__ void fwd8_step(int j, int n_kt, f32x16 (&s)[2], i32x8
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Waves per SIMD: at d = 64 a wave needs ~156 registers, so three fit (the
+// kernel is VALU-bound, and a third wave measured 8-10% faster); at d = 128
+// (~234), two.
+template <int D>
+constexpr int kFp8WavesPerSimd = D == 64 ? 3 : 2;
+
 template <int D, bool BAND>
-__global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_fp8_kernel(Fp8Params p) {
+__global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(kFp8WavesPerSimd<D>, kFp8WavesPerSimd<D>))) void fwd_fp8_kernel(Fp8Params p) {
   constexpr int KS = D / 64;
   constexpr int DB = D / 32;
   constexpr int TILE = kBN8 * D;
