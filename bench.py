@@ -393,7 +393,7 @@ def main():
                     help="skip timing the four smaller workloads")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(attention heads shard with no communication; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
