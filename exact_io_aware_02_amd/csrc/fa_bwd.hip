@@ -649,18 +649,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
                           p.drop.seed_lo, p.drop.seed_hi);
     const bool need_mask = (j0 + kT > p.Nk) || (BAND && ((p.wr >= 0 && j0 + kT - 1 > qw0 + p.wr) ||
                                                           (p.wl >= 0 && j0 < qw0 + QW - 1 - p.wl)));
+    float pv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pv[r] = exp2_fast(__builtin_fmaf(s[r], c, -lse2));
+    if (need_mask) {
+      // one branch per tile (the empty asm keeps it a branch: per element,
+      // the compiler would branch sixteen times on every tile)
+      asm volatile("");
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = j0 + acc_row(half, r);
+        if (kk >= p.Nk || (BAND && ((p.wr >= 0 && kk > qi + p.wr) || (p.wl >= 0 && kk < qi - p.wl)))) pv[r] = 0.f;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float pv = exp2_fast(__builtin_fmaf(s[r], c, -lse2));
-      if (need_mask) {
-        const int kk = j0 + acc_row(half, r);
-        if (kk >= p.Nk || (BAND && ((p.wr >= 0 && kk > qi + p.wr) || (p.wl >= 0 && kk < qi - p.wl)))) pv = 0.f;
-      }
       if constexpr (DROP) {  // dS = P (keep * scale * dP - D)
         const float m = ((rnd[r >> 2] >> (8 * (r & 3))) & 0xffu) >= p.drop.thr ? p.drop.scale : 0.f;
-        dp[r] = pv * __builtin_fmaf(m, dp[r], ndsv);
+        dp[r] = pv[r] * __builtin_fmaf(m, dp[r], ndsv);
       } else {
-        dp[r] = pv * dp[r];
+        dp[r] = pv[r] * dp[r];
       }
     }
     const u32x4 bd[2] = {pack_acc8<DT>(dp, 0), pack_acc8<DT>(dp, 1)};
