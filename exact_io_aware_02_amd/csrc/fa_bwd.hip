@@ -134,26 +134,6 @@ __device__ __forceinline__ void tile_t_times(f32x16 (&acc)[D / 32], const uint16
     for (int db = 0; db < D / 32; ++db) acc[db] = mfma32<DT>(lds_transposed_a<D>(tile, ta, kk, db), bp[kk], acc[db]);
 }
 
-// Pin the issue order of a straight-line run of NM MFMAs fed by NR LDS
-// reads: the reads of the first kLA MFMAs go first, then each MFMA is
-// followed by an even share of the remaining reads, so an operand is read
-// about kLA MFMAs (kLA x 32 cycles) before its use and the LDS latency
-// hides under the matrix core.  Without this the scheduler issues each
-// read right before its MFMA.
-constexpr int kLA = 4;
-template <int NM, int NR>
-__device__ __forceinline__ void sched_reads_ahead() {
-  constexpr int first = NR * kLA / NM;
-  constexpr int rest = NR - first;
-  constexpr int per = (rest + NM - kLA - 1) / (NM - kLA);
-  __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < NM - kLA) __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
-  }
-}
-
 // Wait until the ring tile just after the one being consumed has landed:
 // `later` tiles were requested after it (at most MAXT, each L loads per
 // wave), and vmcnt counts in request order, so leaving min(later, MAXT) * L
@@ -410,7 +390,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(kD
             }
           }
           sd = rows_times_regs<D, DT>(Ot, kv, ta, dinit);
-          // issue order: operand reads kLA MFMAs ahead of their use
+          // issue order: operand reads kReadLead MFMAs ahead of their use
           sched_reads_ahead<2 * DB + KS, (4 * DB + 4 + KS)>();
         };
         // on the first step dS = 0 and the previous slot holds zeros

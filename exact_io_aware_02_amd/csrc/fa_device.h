@@ -219,6 +219,26 @@ __device__ __forceinline__ u32x4 lds_transposed_a(const uint16_t* base, const Ti
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Pin the issue order of a straight-line run of NM MFMAs fed by NR LDS
+// reads: the reads of the first kReadLead MFMAs go first, then each MFMA
+// is followed by an even share of the remaining reads, so an operand is
+// read about kReadLead MFMAs (kReadLead x 32 cycles) before its use and the
+// LDS latency hides under the matrix core.  Without this the scheduler
+// issues each read right before its MFMA.
+constexpr int kReadLead = 4;
+template <int NM, int NR>
+__device__ __forceinline__ void sched_reads_ahead() {
+  constexpr int first = NR * kReadLead / NM;
+  constexpr int rest = NR - first;
+  constexpr int per = (rest + NM - kReadLead - 1) / (NM - kReadLead);
+  __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < NM - kReadLead) __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+  }
+}
+
 // Pack registers 8*kk .. 8*kk+7 of an fp32 accumulator into an MFMA operand.
 template <int DT>
 __device__ __forceinline__ u32x4 pack_acc8(const f32x16& s, int kk) {

@@ -24,12 +24,15 @@
 //                          untransposed V tile; B = P^T repacked in place
 //                          from the S^T accumulator (no LDS round trip).
 //
-// Software pipeline: step j issues the PV MFMAs of tile j-1 and the S
-// MFMAs of tile j+1 among the exponentials of tile j, in chunks the
-// scheduler keeps in order, so one wave's matrix core and VALU work at the
-// same time (the overlap FA3 gets from asynchrony on Hopper, glossary
-// article's FA-3 section).  The V operands and P of tile j-1 stay in
-// registers across the step boundary.
+// Two schedules of the key loop (FwdCfg).  Interleaved, for small grids:
+// step j issues the PV MFMAs of tile j-1 and the S MFMAs of tile j+1 among
+// the exponentials of tile j, in chunks the scheduler keeps in order, so
+// one wave's matrix core and VALU work at the same time (the overlap FA3
+// gets from asynchrony on Hopper, glossary article's FA-3 section); the V
+// operands and P of tile j-1 stay in registers across the step boundary.
+// Phased, for grids that fill the chip: the exponentials of tile j, then
+// PV(j) and S(j+1); with fewer registers three waves (d = 128) or four
+// (d = 64) share a SIMD and fill each other's phases.
 //
 // Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2 (O = 0, LSE = -inf for
 // a row that admits no key).  Masks: query i admits keys i - wl .. i + wr
@@ -54,21 +57,35 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 32;            // keys per pipeline tile
-// Queries per wave are 32 * NQB (NQB = 32-query MFMA column blocks).  64
+// Each wave owns 32 queries (one 32-query MFMA column block): 64 per wave
 // halves the LDS bytes per MFMA but needs ~260 registers at d = 128 and
-// ~220 at d = 64 (two waves per SIMD); 32 at d = 64 needs ~140, which lets
-// three waves share a SIMD and doubles the workgroups of small grids
-// (measured faster at every size tried).
-template <int D, int NQB_ = 1>
-struct FwdTile {
-  static constexpr int NQB = NQB_;
-  static constexpr int QW = 32 * NQB;       // queries per wave
-  static constexpr int BM = kWaves * QW;    // queries per workgroup
-  static constexpr int WAVES_PER_SIMD = (D == 64 && NQB == 1) ? 3 : 2;
-  // S(j+1) in registers of its own at d = 128; at d = 64 it overwrites S(j)
-  // after the weights (fewer registers, so three waves fit a SIMD)
-  static constexpr bool SEP_S = D == 128;
+// ~220 at d = 64, and measured slower at both.
+constexpr int kQW = 32;                // queries per wave
+constexpr int kBM = kWaves * kQW;      // queries per workgroup
+
+// Two schedules of the key loop (see fwd_step and fwd_step_phased):
+//  * interleaved: a wave spreads the PV and S MFMAs of neighbouring tiles
+//    through the exponentials of the current one, so it keeps its matrix
+//    core fed by itself.  This needs the V operands, P and (at d = 128)
+//    S(j+1) carried in registers (~210 at d = 128, two waves per SIMD;
+//    ~140 at d = 64, three) and is used for grids too small to give every
+//    CU two workgroups;
+//  * phased: the exponentials, then the MFMAs, with the waves sharing a
+//    SIMD filling each other's phases.  It needs ~160 registers at d = 128
+//    (three waves per SIMD, with a 3-slot ring so three workgroups fit the
+//    LDS) and ~105 at d = 64 (four).  On full grids it measured 7-12%
+//    faster at d = 128 and 2-8% at d = 64; on small grids, where a SIMD
+//    has one wave, 8% slower.
+template <int D, bool PHASED>
+struct FwdCfg {
+  static constexpr int WAVES_PER_SIMD = PHASED ? (D == 64 ? 4 : 3) : (D == 64 ? 3 : 2);
+  static constexpr int NBUF = PHASED && D == 128 ? 3 : 4;  // K/V ring slots
+  // interleaved, d = 128: S(j+1) in registers of its own; otherwise it
+  // overwrites S(j) after the weights
+  static constexpr bool SEP_S = !PHASED && D == 128;
 };
+// Workgroups from which the phased schedule is used (two per CU).
+constexpr int64_t kPhasedMinBlocks = 512;
 
 static_assert(kBN == 32, "K/V tiles are the 32-row tiles of fa_device.h");
 template <int D>
@@ -181,7 +198,7 @@ constexpr float kLaneSumMax = 32768.0f;  // 2^15: each weight fits fp16 and bf16
 // raise m, rescale O^T (which by then holds V_{j-1} P_{j-1}) and l,
 // weights again.  The result is the same for any m (O = O^T / l uses one
 // m for both); m only keeps the weights in range.
-template <int D, int DT, bool BAND, bool DROP, bool FIRST, int kNQB = FwdTile<D>::NQB>
+template <int D, int DT, bool BAND, bool DROP, bool FIRST, int kNQB = 1>
 __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32x16 (&sn)[kNQB], u32x4 (&pf)[2][kNQB],
                                          u32x4 (&va)[2][D / 32], const uint16_t* __restrict__ Kj,
                                          const uint16_t* __restrict__ Kn, const uint16_t* __restrict__ Vj,
@@ -197,7 +214,7 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
   const int j0 = j * kBN;
   const int col = lane & 31, half = lane >> 5;
 
-  if constexpr (FwdTile<D>::SEP_S) {
+  if constexpr (FwdCfg<D, false>::SEP_S) {
     // K(j) is no longer read (S(j) stays in registers), so K runs four
     // tiles ahead: K(j+4) into K(j)'s slot, V(j+3) into V(j-1)'s
     if (j + 4 < n_kt) TC::issue(krs, krow, (uint32_t)(j + 4) * ktb, Kdst, lane, wave);
@@ -213,7 +230,7 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
   // K(j+1) operands (reading K(j+1) when j+1 = n_kt reads a stale slot
   // whose scores are never used; it keeps the MFMAs in one block with the
   // exponentials)
-  constexpr bool kSep = FwdTile<D>::SEP_S;
+  constexpr bool kSep = FwdCfg<D, false>::SEP_S;
   constexpr int kKLead = 2;  // with kSep, K(j+1) operands are read this many chunks ahead of use
   u32x4 ka[KS];
   if constexpr (!kSep || FIRST) {
@@ -357,7 +374,7 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
   // j+4 may land in the slot
   wait_lds_reads();
 
-  if constexpr (FwdTile<D>::SEP_S) {
+  if constexpr (FwdCfg<D, false>::SEP_S) {
     // K(j+2) and V(j+1) (read next step) must have landed; the copies
     // issued after them (K(j+3), V(j+2), K(j+4), V(j+3)) may fly on
     if (j + 4 < n_kt) {
@@ -377,15 +394,98 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int DT, bool BAND, bool DROP, int NQB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTile<D, NQB>::WAVES_PER_SIMD,
-                                                                          FwdTile<D, NQB>::WAVES_PER_SIMD))) void fwd_kernel(FwdParams p) {
-  constexpr int kNQB = NQB;
-  constexpr int kQW = FwdTile<D, NQB>::QW;
-  constexpr int kBM = FwdTile<D, NQB>::BM;
+// One step of the phased schedule, for tile j: the weights of tile j
+// against the running maximum (VALU; the rare rescale finds S(j) still in
+// registers), then PV(j) and S(j+1) (MFMA, their LDS operands read a few
+// MFMAs ahead), which overwrite S(j).  The waves sharing a SIMD fill each
+// other's phases.  The ring holds NBUF tiles; step j requests tile
+// j + NBUF - 1 into the slot of tile j-1, read in full by the last step.
+template <int D, int DT, bool BAND, bool DROP, int kNQB>
+__device__ __forceinline__ void fwd_step_phased(int j, int n_kt, f32x16 (&s)[kNQB], const uint16_t* __restrict__ Vj,
+                                            const uint16_t* __restrict__ Kn, uint16_t* __restrict__ Kdst,
+                                            uint16_t* __restrict__ Vdst, __amdgpu_buffer_rsrc_t krs,
+                                            __amdgpu_buffer_rsrc_t vrs, uint32_t krow, uint32_t vrow, uint32_t ktb,
+                                            uint32_t vtb, const u32x4 (&qf)[kNQB][D / 16], f32x16 (&acc)[D / 32][kNQB],
+                                            RowState<kNQB>& st, int Nk, int wl, int wr, int qw0, float c, int lane,
+                                            int wave, const TileLayout<D>& ta, const DropoutParams& dp, uint32_t bh) {
+  using TC = TileCopy<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NBUF = 4;  // K/V ring (see fwd_step)
+  const int j0 = j * kBN;
+  const int col = lane & 31, half = lane >> 5;
+  constexpr int PD = FwdCfg<D, true>::NBUF - 1;  // tile j+PD goes to the slot of tile j-1
+  if (j + PD < n_kt) {
+    TC::issue(krs, krow, (uint32_t)(j + PD) * ktb, Kdst, lane, wave);
+    TC::issue(vrs, vrow, (uint32_t)(j + PD) * vtb, Vdst, lane, wave);
+  }
+  mask_tile<BAND>(s, j0, Nk, wl, wr, qw0, col, half);
+  u32x4 rnd[kNQB];
+#pragma unroll
+  for (int nb = 0; nb < kNQB; ++nb) {
+    rnd[nb] = u32x4{0, 0, 0, 0};
+    if constexpr (DROP)
+      rnd[nb] = philox4x32_10(2u * (uint32_t)j + (uint32_t)half, (uint32_t)(qw0 + 32 * nb + col), bh, dp.offset,
+                              dp.seed_lo, dp.seed_hi);
+  }
+  float ls[kNQB][2];
+  u32x4 pn[kNQB][2];
+#pragma unroll
+  for (int nb = 0; nb < kNQB; ++nb) weights<DT, DROP>(s[nb], c, st.m[nb], ls[nb], pn[nb], rnd[nb], dp.thr);
+  bool raise = false;
+#pragma unroll
+  for (int nb = 0; nb < kNQB; ++nb) raise |= !(ls[nb][0] + ls[nb][1] <= kLaneSumMax);
+  if (__any(raise)) {  // rare: S(j) is still in s
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int nb = 0; nb < kNQB; ++nb) {
+      float mx = s[nb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
+      const float mnew = fmaxf(st.m[nb], max_pair32(mx) * c);
+      const float alpha = exp2_fast(st.m[nb] - mnew);
+      st.m[nb] = mnew;
+      st.l[nb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db][nb] *= alpha;
+      weights<DT, DROP>(s[nb], c, st.m[nb], ls[nb], pn[nb], rnd[nb], dp.thr);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < kNQB; ++nb) st.l[nb] += ls[nb][0] + ls[nb][1];
+  __builtin_amdgcn_sched_barrier(0);
+  // PV(j), then S(j+1) (after the last tile: a stale slot, never used)
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const u32x4 a = lds_transposed_a<D>(Vj, ta, kk, db);
+#pragma unroll
+      for (int nb = 0; nb < kNQB; ++nb) acc[db][nb] = mfma32<DT>(a, pn[nb][kk], acc[db][nb]);
+    }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 a = lds_rowmajor<D>(Kn, ta, ks);
+#pragma unroll
+    for (int nb = 0; nb < kNQB; ++nb) s[nb] = mfma32<DT>(a, qf[nb][ks], ks == 0 ? f32x16{} : s[nb]);
+  }
+  sched_reads_ahead<(2 * DB + KS) * kNQB, 4 * DB + KS>();
+  // tile j+2 (read next step) must have landed; later ones may fly on
+  if (j + PD < n_kt) {
+    wait_vmcnt<(PD - 2) * 2 * TC::NI>();
+  } else {
+    wait_loads();
+  }
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, int DT, bool BAND, bool DROP, bool PHASED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdCfg<D, PHASED>::WAVES_PER_SIMD,
+                                                                          FwdCfg<D, PHASED>::WAVES_PER_SIMD))) void fwd_kernel(FwdParams p) {
+  constexpr int kNQB = 1;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int NBUF = FwdCfg<D, PHASED>::NBUF;  // K/V ring (see fwd_step, fwd_step_phased)
   constexpr int TILE = kTileElems<D>;
 
   // One LDS object for the whole ring: the compiler gives every separate
@@ -450,18 +550,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
       qf[nb][ks] = x;
     }
   }
-  // prologue: tiles jt0 .. jt0+2 in flight (tile jt0 + t lives in slot
-  // t mod 4), and K of tile jt0+3 where K runs four tiles ahead
-  constexpr bool kSep = FwdTile<D>::SEP_S;
+  // prologue: tiles jt0 .. jt0+NBUF-2 in flight (tile jt0 + t lives in
+  // slot t mod NBUF), and K of tile jt0+3 where K runs four tiles ahead
+  constexpr bool kSep = FwdCfg<D, PHASED>::SEP_S;
 #pragma unroll
-  for (int t0 = 0; t0 < 3; ++t0) {
+  for (int t0 = 0; t0 < NBUF - 1; ++t0) {
     const int jj = jt0 + t0;
     if (jj < n_kt) {
       TC::issue(krs, krow, (uint32_t)jj * ktb, Ks[t0], lane, wave);
       TC::issue(vrs, vrow, (uint32_t)jj * vtb, Vs[t0], lane, wave);
     }
   }
-  if (kSep && jt0 + 3 < n_kt) TC::issue(krs, krow, (uint32_t)(jt0 + 3) * ktb, Ks[3], lane, wave);
+  if constexpr (kSep) {
+    if (jt0 + 3 < n_kt) TC::issue(krs, krow, (uint32_t)(jt0 + 3) * ktb, Ks[3], lane, wave);
+  }
 
   f32x16 acc[DB][kNQB];
 #pragma unroll
@@ -480,12 +582,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   ta.init(lane);
 
   // tiles jt0 and jt0+1 landed (K(jt0) for S(jt0) now, V(jt0) and
-  // K(jt0+1) in the first step); with K four ahead, V(jt0+1), K(jt0+2),
-  // V(jt0+2) and K(jt0+3) may fly on
+  // K(jt0+1) in the first step); the later ones may fly on (with K four
+  // ahead: V(jt0+1), K(jt0+2), V(jt0+2) and K(jt0+3))
   if (kSep && n_kt - jt0 > 3) {
     wait_vmcnt<4 * TC::NI>();
-  } else if (!kSep && n_kt - jt0 > 2) {
-    wait_vmcnt<2 * TC::NI>();
+  } else if (!kSep && n_kt - jt0 >= NBUF - 1) {
+    wait_vmcnt<(NBUF - 3) * 2 * TC::NI>();
   } else {
     wait_loads();
   }
@@ -495,8 +597,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
     for (int ks = 0; ks < KS; ++ks) qf[nb][ks] ^= p.qflip;
   lds_barrier();
 
-  // Tile jt0 + t lives in slot t mod 4.
-  if (jt0 < n_kt) {
+  if constexpr (PHASED) {
+    if (jt0 < n_kt) {
+      f32x16 sa[kNQB];
+#pragma unroll
+      for (int nb = 0; nb < kNQB; ++nb) sa[nb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 a = lds_rowmajor<D>(Ks[0], ta, ks);
+#pragma unroll
+        for (int nb = 0; nb < kNQB; ++nb) sa[nb] = mfma32<DT>(a, qf[nb][ks], sa[nb]);
+      }
+      auto wrap = [](int x) { return x >= NBUF ? x - NBUF : x; };
+      int sl = 0;  // slot of tile j
+      for (int j = jt0; j < n_kt; ++j) {
+        const int sp = wrap(sl + NBUF - 1);  // slot of tile j-1
+        fwd_step_phased<D, DT, BAND, DROP, kNQB>(j, n_kt, sa, Vs[sl], Ks[wrap(sl + 1)], Ks[sp], Vs[sp], krs, vrs, krow,
+                                                 vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta,
+                                                 p.drop, (uint32_t)bh);
+        sl = wrap(sl + 1);
+      }
+    }
+  } else if (jt0 < n_kt) {
+    // Tile jt0 + t lives in slot t mod 4.
     f32x16 sa[kNQB];
 #pragma unroll
     for (int nb = 0; nb < kNQB; ++nb) sa[nb] = f32x16{};
@@ -577,26 +700,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdTil
   }
 }
 
-template <int D, int DT, bool BAND, bool DROP, int NQB>
-hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
-  constexpr int kBM = FwdTile<D, NQB>::BM;
-  const int n_qt = (p.Nq + kBM - 1) / kBM;
-  const int64_t blocks = (int64_t)n_qt * p.B * p.H;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND, DROP, NQB>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+template <int D, int DT, bool BAND, bool DROP, bool PHASED>
+hipError_t launch_t(const FwdParams& p, int64_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND, DROP, PHASED>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int DT, int NQB>
-hipError_t launch_dcn(const FwdParams& p, bool banded, hipStream_t stream) {
+template <int D, int DT, bool PHASED>
+hipError_t launch_ds(const FwdParams& p, bool banded, int64_t blocks, hipStream_t stream) {
   if (p.drop.thr > 0)
-    return banded ? launch_t<D, DT, true, true, NQB>(p, stream) : launch_t<D, DT, false, true, NQB>(p, stream);
-  return banded ? launch_t<D, DT, true, false, NQB>(p, stream) : launch_t<D, DT, false, false, NQB>(p, stream);
+    return banded ? launch_t<D, DT, true, true, PHASED>(p, blocks, stream)
+                  : launch_t<D, DT, false, true, PHASED>(p, blocks, stream);
+  return banded ? launch_t<D, DT, true, false, PHASED>(p, blocks, stream)
+                : launch_t<D, DT, false, false, PHASED>(p, blocks, stream);
 }
 
 template <int D, int DT>
 hipError_t launch_dc(const FwdParams& p, bool banded, hipStream_t stream) {
-  return launch_dcn<D, DT, FwdTile<D>::NQB>(p, banded, stream);
+  const int64_t blocks = (int64_t)((p.Nq + kBM - 1) / kBM) * p.B * p.H;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (blocks >= kPhasedMinBlocks) return launch_ds<D, DT, true>(p, banded, blocks, stream);
+  return launch_ds<D, DT, false>(p, banded, blocks, stream);
 }
 
 }  // namespace
