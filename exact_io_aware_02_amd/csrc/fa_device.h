@@ -228,14 +228,19 @@ __device__ __forceinline__ u32x4 lds_transposed_a(const uint16_t* base, const Ti
 constexpr int kReadLead = 4;
 template <int NM, int NR>
 __device__ __forceinline__ void sched_reads_ahead() {
-  constexpr int first = NR * kReadLead / NM;
-  constexpr int rest = NR - first;
-  constexpr int per = (rest + NM - kReadLead - 1) / (NM - kReadLead);
-  __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
+  if constexpr (NM <= kReadLead) {  // a short run: every read first
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+  } else {
+    constexpr int first = NR * kReadLead / NM;
+    constexpr int rest = NR - first;
+    constexpr int per = (rest + NM - kReadLead - 1) / (NM - kReadLead);
+    __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
 #pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < NM - kReadLead) __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < NM - kReadLead) __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+    }
   }
 }
 

@@ -17,13 +17,16 @@
 //                      read from the untransposed V tile with
 //                      ds_read_b64_tr_b8.
 //
-// Software pipeline: step j issues the PV MFMAs of tile j-1 and the QK
-// MFMAs of tile j+1 among the exponentials of tile j, so one wave keeps
-// its matrix core fed from its own instruction stream.
+// Two schedules of the key loop (Fp8Cfg), as in the 16-bit forward.
+// Interleaved, for small grids: step j issues the PV MFMAs of tile j-1 and
+// the QK MFMAs of tile j+1 among the exponentials of tile j, so one wave
+// keeps its matrix core fed from its own instruction stream.  Phased, for
+// grids that fill the chip: the weights of tile j, then PV(j) and S(j+1),
+// with more waves per SIMD filling each other's phases.
 //
 // O = O^T * v_descale / l in bf16, LSE fp32.  One workgroup of 4 waves owns
 // 128 queries (32 per wave, a query per lane); key tiles of 64 stream
-// HBM -> LDS through a 4-slot ring.  Causal masks, sliding windows and
+// HBM -> LDS through a ring of 3 or 4 slots.  Causal masks, sliding windows and
 // fewer K/V heads work as in the 16-bit forward.
 //
 // Operand layouts (measured on gfx950): the A and B operands of the fp8 MFMA
@@ -346,22 +349,120 @@ __device__ __forceinline__ void fwd8_step(int j, int n_kt, f32x16 (&s)[2], i32x8
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Waves per SIMD: at d = 64 a wave needs ~156 registers, so three fit (the
-// kernel is VALU-bound, and a third wave measured 8-10% faster); at d = 128
-// (~234), two.
-template <int D>
-constexpr int kFp8WavesPerSimd = D == 64 ? 3 : 2;
+// Two schedules of the key loop, as in the 16-bit forward: interleaved
+// (fwd8_step; two waves per SIMD at d = 128, where a wave needs ~234
+// registers, three at d = 64) for grids too small to give every CU two
+// workgroups, and phased (fwd8_step_phased: the weights of tile j, then
+// PV(j) and S(j+1); ~150 registers at d = 128, so three waves share a SIMD
+// with a 3-slot ring, four at d = 64) for the others.
+template <int D, bool PHASED>
+struct Fp8Cfg {
+  static constexpr int WAVES_PER_SIMD = PHASED ? (D == 64 ? 4 : 3) : (D == 64 ? 3 : 2);
+  static constexpr int NBUF = PHASED && D == 128 ? 3 : 4;
+};
+constexpr int64_t kPhasedMinBlocks8 = 512;
 
+// One step of the phased schedule for tile j: the weights of S(j) (the
+// rare rescale finds S(j) still in registers), P(j) rounded into the B
+// operand, then PV(j) and S(j+1) with their LDS operands read a few MFMAs
+// ahead.  Step j requests tile j + NBUF - 1 into the slot of tile j-1.
 template <int D, bool BAND>
-__global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(kFp8WavesPerSimd<D>, kFp8WavesPerSimd<D>))) void fwd_fp8_kernel(Fp8Params p) {
+__device__ __forceinline__ void fwd8_step_phased(int j, int n_kt, f32x16 (&s)[2], const uint8_t* __restrict__ Vj,
+                                                 const uint8_t* __restrict__ Kn, uint8_t* __restrict__ Kdst,
+                                                 uint8_t* __restrict__ Vdst, __amdgpu_buffer_rsrc_t krs,
+                                                 __amdgpu_buffer_rsrc_t vrs, uint32_t krow, uint32_t vrow,
+                                                 const i32x8 (&qf)[D / 64], f32x16 (&acc)[D / 32], float& m, float& l,
+                                                 int Nk, int wl, int wr, int qw0, float c, int lane, int wave,
+                                                 const Tile8Addr<D>& ta) {
+  using TC = Tile8Copy<D>;
+  constexpr int DB = D / 32;
+  constexpr int KS = D / 64;
+  constexpr int PD = Fp8Cfg<D, true>::NBUF - 1;
+  const int j0 = j * kBN8;
+  const int half = lane >> 5;
+  const int qi = qw0 + (lane & 31);
+  if (j + PD < n_kt) {
+    TC::issue(krs, krow, (uint32_t)(j + PD) * kBN8 * krow, Kdst, lane, wave);
+    TC::issue(vrs, vrow, (uint32_t)(j + PD) * kBN8 * vrow, Vdst, lane, wave);
+  }
+  mask8<BAND>(s, j0, Nk, wl, wr, qw0, qi, half);
+  // P(j) rounded into the B operand as it is formed: byte 16 mb + r holds
+  // the key of accumulator register r of block mb, matching load_v8's slots
+  i32x8 pf;
+  float ls = 0.f;
+  auto weights8 = [&](float mneg) {
+    ls = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        float w4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w4[e] = exp2_fast(__builtin_fmaf(s[mb][r + e], c, mneg));
+          ls += w4[e];
+        }
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(w4[0], w4[1], 0, false);
+        pf[4 * mb + r / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(w4[2], w4[3], w, true);
+      }
+  };
+  weights8(-m);
+  if (__any(!(ls <= kP8Max))) {  // rare (also catches +inf and NaN sums)
+    asm volatile("" ::: "memory");
+    float mx = s[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    const float mnew = fmaxf(m, max_pair32(mx) * c);
+    const float alpha = exp2_fast(m - mnew);
+    m = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    weights8(-m);
+  }
+  l += ls;
+  __builtin_amdgcn_sched_barrier(0);
+  // PV(j), then S(j+1) (after the last tile: a stale slot, never used)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    i32x8 va;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const i32x2 t = lds_tr8(Vj + ta.v[db] + 16 * u * D);
+      va[2 * u] = t[0];
+      va[2 * u + 1] = t[1];
+    }
+    acc[db] = mfma_fp8(va, pf, acc[db]);
+  }
+  {
+    i32x8 ka[2][KS];
+    load_k8<D>(Kn, ta, ka);
+    scores8<D>(ka, qf, s);
+  }
+  sched_reads_ahead<DB + 2 * KS, 4 * DB + 4 * KS>();
+  // tile j+2 (read next step) must have landed; later ones may fly on
+  if (j + PD < n_kt) {
+    wait_vmcnt<(PD - 2) * 2 * TC::NI>();
+  } else {
+    wait_loads();
+  }
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, bool BAND, bool PHASED>
+__global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(Fp8Cfg<D, PHASED>::WAVES_PER_SIMD, Fp8Cfg<D, PHASED>::WAVES_PER_SIMD))) void fwd_fp8_kernel(Fp8Params p) {
   constexpr int KS = D / 64;
   constexpr int DB = D / 32;
   constexpr int TILE = kBN8 * D;
+  constexpr int NBUF = Fp8Cfg<D, PHASED>::NBUF;
   using TC = Tile8Copy<D>;
 
   struct Smem {  // one LDS object (see the 16-bit forward)
-    uint8_t k[4][TILE];
-    uint8_t v[4][TILE];
+    uint8_t k[NBUF][TILE];
+    uint8_t v[NBUF][TILE];
   };
   __shared__ __attribute__((aligned(1024))) Smem sm;
 
@@ -407,7 +508,7 @@ __global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(kFp8WavesPe
     qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
 #pragma unroll
-  for (int t0 = 0; t0 < 3; ++t0) {
+  for (int t0 = 0; t0 < NBUF - 1; ++t0) {
     const int jj = jt0 + t0;
     if (jj < n_kt) {
       TC::issue(krs, krow, (uint32_t)jj * kBN8 * krow, sm.k[t0], lane, wave);
@@ -423,8 +524,8 @@ __global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(kFp8WavesPe
   ta.init(lane);
 
   // tiles jt0 and jt0+1 landed (S(jt0) now, V(jt0) and K(jt0+1) in the first step)
-  if (n_kt - jt0 > 2) {
-    wait_vmcnt<2 * TC::NI>();
+  if (n_kt - jt0 >= NBUF - 1) {
+    wait_vmcnt<(NBUF - 3) * 2 * TC::NI>();
   } else {
     wait_loads();
   }
@@ -432,8 +533,25 @@ __global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(kFp8WavesPe
   for (int ks = 0; ks < KS; ++ks) qf[ks] ^= (int)p.qflip;
   lds_barrier();
 
-  // Tile jt0 + t lives in slot t mod 4.
-  if (jt0 < n_kt) {
+  if constexpr (PHASED) {
+    if (jt0 < n_kt) {
+      f32x16 sa[2];
+      {
+        i32x8 ka[2][KS];
+        load_k8<D>(sm.k[0], ta, ka);
+        scores8<D>(ka, qf, sa);
+      }
+      auto wrap = [](int x) { return x >= NBUF ? x - NBUF : x; };
+      int sl = 0;  // slot of tile j
+      for (int j = jt0; j < n_kt; ++j) {
+        const int sp = wrap(sl + NBUF - 1);  // slot of tile j-1
+        fwd8_step_phased<D, BAND>(j, n_kt, sa, sm.v[sl], sm.k[wrap(sl + 1)], sm.k[sp], sm.v[sp], krs, vrs, krow, vrow,
+                                  qf, acc, m, l, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta);
+        sl = wrap(sl + 1);
+      }
+    }
+  } else if (jt0 < n_kt) {
+    // Tile jt0 + t lives in slot t mod 4.
     f32x16 sa[2];
     i32x8 pf = i32x8{};
     i32x8 va[DB];
@@ -477,7 +595,11 @@ hipError_t launch8(const Fp8Params& p, hipStream_t stream) {
   const int n_qt = (p.Nq + kBM8 - 1) / kBM8;
   const int64_t blocks = (int64_t)n_qt * p.B * p.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, BAND>), dim3((unsigned)blocks), dim3(kT8), 0, stream, p);
+  if (blocks >= kPhasedMinBlocks8) {
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, BAND, true>), dim3((unsigned)blocks), dim3(kT8), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, BAND, false>), dim3((unsigned)blocks), dim3(kT8), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -161,3 +161,37 @@ def test_fp8_fwd_gqa_equals_repeated_heads():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
+
+
+PHASED_CASES = [
+    # name, B, H, Hkv, Nq, Nk, d, layout, causal, window, descale
+    ("d128_causal", 1, 2, 2, 333, 333, 128, "bhsd", True, None, (1.0, 1.0, 1.0)),
+    ("d64_gqa_window_bshd", 2, 4, 2, 300, 300, 64, "bshd", True, (100, -1), (0.5, -2.0, 3.0)),
+    ("d128_ragged_empty_rows", 1, 2, 1, 300, 100, 128, "bhsd", False, (10, 10), (1.0, 1.0, 1.0)),
+]
+
+
+@pytest.mark.parametrize("case", PHASED_CASES, ids=[c[0] for c in PHASED_CASES])
+def test_fp8_fwd_phased_schedule(case):
+    """From 512 workgroups of 128 queries the fp8 forward runs its phased
+    schedule: a small case repeated along the batch to that size, the first
+    copy against the oracle and every copy bitwise equal to it."""
+    name, B, H, Hkv, Nq, Nk, d, layout, causal, window, descale = case
+    R = math.ceil(512 / (math.ceil(Nq / 128) * B * H))
+    say("case phased %s (%d copies)" % (name, R))
+    inp = make_qkv(B, H, Nq, Nk, d, "fp8", layout, seed=71, Hkv=Hkv)
+    rep = {x: inp[x].view(torch.uint8).repeat(R, 1, 1, 1).view(torch.float8_e4m3fn) for x in ("q", "k", "v")}
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd_fp8(*(rep[x].to(DEV) for x in ("q", "k", "v")), causal=causal, scale=scale,
+                                  layout=layout, window=window, descale=descale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    w = window if window is not None else (-1, -1)
+    q8, k8, v8 = (fp8_bytes(inp[x], layout) for x in ("q", "k", "v"))
+    o_ref, lse_ref = attention_fp8_fwd64(q8, k8, v8, scale, causal, window=w, descale=descale)
+    rows = np.tile(np.arange(Nq), (B, H, 1))
+    bound, sigma = fp8_rounding_model(q8, k8, v8, scale, causal, rows, window=w, descale=descale)
+    check(name, to_bhsd64(o[:B], layout), lse[:B].numpy().astype(np.float64), o_ref, lse_ref, bound, sigma)
+    for r in (1, R - 1):
+        assert torch.equal(o[r * B:(r + 1) * B].view(torch.int16), o[:B].view(torch.int16)), r
+        assert torch.equal(lse[r * B:(r + 1) * B], lse[:B]), r
