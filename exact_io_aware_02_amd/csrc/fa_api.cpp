@@ -346,7 +346,7 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
     return fail(FA_ERR_INVALID_ARG, "workspace_bytes = %zu < required %zu", workspace_bytes, need);
   // fewer K/V heads: split each K/V head's query heads over more dK/dV
   // workgroups when the workspace holds their partial sums
-  const int splits = fa::bwd_kv_splits(B, H, H_kv, Nk);
+  const int splits = fa::bwd_kv_splits(B, H, H_kv, Nk, d);
   const size_t need_split = fa::bwd_split_workspace_bytes(B, H, H_kv, Nq, Nk, d);
   const bool split = splits > 1 && (stages & FA_BWD_DKDV) && workspace_bytes >= need_split;
   const size_t used = split ? need_split : need;

@@ -157,22 +157,28 @@ __device__ __forceinline__ void wait_ring(int later) {
   }
 }
 
-// At d = 64 a dK/dV wave needs at most 128 registers, so two workgroups
-// share a CU (four waves per SIMD: measured 20% faster than two; at d = 128,
-// one), and a dQ wave at most 168 (three per SIMD: 10% faster than two).
+// dK/dV workgroups hold NPAIR pairs of waves.  At d = 128 a wave needs
+// ~160 registers: six pairs (twelve waves, three per SIMD) in one
+// workgroup per CU measured 6% faster than four pairs (two per SIMD).  At
+// d = 64 a wave needs at most 128: two workgroups of four pairs share a CU
+// (four waves per SIMD, 20% faster than two).  A dQ wave at d = 64 needs at
+// most 168 registers (three per SIMD: 10% faster than two).
 template <int D>
-constexpr int kDkvWavesPerSimd = D == 64 ? 4 : 2;
+constexpr int kDkvPairs = D == 64 ? 4 : 6;
+template <int D>
+constexpr int kDkvWavesPerSimd = D == 64 ? 4 : 3;
 template <int D>
 constexpr int kDqWavesPerSimd = D == 64 ? 3 : 2;
 
 // ------------------------------------------------------------ dK, dV
-// Eight waves in four pairs.  The two waves of a pair own the same 32 keys
-// and, with waves placed on SIMDs round-robin, the same SIMD; they split
-// the four contractions of a query tile by role:
-//   role A (waves 0-3): K rows in registers;  S = Q K^T, P = 2^(S c - lse2),
-//                       dV^T += dO^T P; P goes to its partner through LDS.
-//   role B (waves 4-7): V rows in registers;  dP - D = dO V^T - D,
-//                       dS = P (dP - D), dK^T += Q^T dS.
+// NPAIR pairs of waves (four at d = 64, six at d = 128).  The two waves of
+// a pair own the same 32 keys and split the four contractions of a query
+// tile by role:
+//   role A (waves 0 .. NPAIR-1): K rows in registers; S = Q K^T,
+//                       P = 2^(S c - lse2), dV^T += dO^T P; P goes to its
+//                       partner through LDS.
+//   role B (waves NPAIR .. 2 NPAIR-1): V rows in registers;
+//                       dP - D = dO V^T - D, dS = P (dP - D), dK^T += Q^T dS.
 // Each wave holds one operand set and one 32 x d accumulator instead of
 // two, and the loop is skewed so that within one phase the MFMAs of one
 // role run while the other role works on the VALU:
@@ -182,9 +188,10 @@ constexpr int kDqWavesPerSimd = D == 64 ? 3 : 2;
 // Query tiles (Q, dO and the two row statistics) stream HBM -> LDS through
 // a 4-slot ring; tile t+3 is requested in phase 2 of step t.
 template <int D, int DT, bool BAND, bool DROP>
-__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(kDkvWavesPerSimd<D>, kDkvWavesPerSimd<D>))) void dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per_eu(kDkvWavesPerSimd<D>, kDkvWavesPerSimd<D>))) void dkdv_kernel(BwdParams p) {
   constexpr int KW = 32;            // keys per pair
-  constexpr int NPAIR = kWaves;     // pairs per workgroup
+  constexpr int NPAIR = kDkvPairs<D>;  // pairs per workgroup
+  constexpr int NCOPY = 4;             // waves of a role that copy its tiles
   constexpr int BNK = NPAIR * KW;   // keys per workgroup
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -192,7 +199,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(kD
   constexpr int PD = NB - 1;        // prefetch distance: tile t+PD is requested in step t
   static_assert(kT == 32, "Q/dO tiles are the 32-row tiles of fa_device.h");
   // a Q or dO tile is copied by the four waves of one role
-  constexpr int NLOADS = TileLayout<D>::template copy_insts<NPAIR>() + 1;  // per wave per tile: its share of Q (A) or dO (B), 8 statistics
+  constexpr int NLOADS = TileLayout<D>::template copy_insts<NCOPY>() + 1;  // per wave per tile: its share of Q (A) or dO (B), 8 statistics
 
   // One LDS object (separate __shared__ variables get separate alias
   // scopes, and the compiler then waits for every in-flight copy into a
@@ -211,8 +218,8 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(kD
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wave & (NPAIR - 1);
   const bool role_a = wave < NPAIR;
+  const int pair = role_a ? wave : wave - NPAIR;
   const int Hkv = p.H / p.G;
   const int BH = p.B * Hkv;
   // workgroups per key tile: one per (batch, K/V head, group of G / S query heads)
@@ -252,9 +259,11 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(kD
     const __amdgpu_buffer_rsrc_t trs = head_rsrc(tp, p.Nq, tstride, D);
     const __amdgpu_buffer_rsrc_t srs =
         f32_rsrc((role_a ? p.lse2 : p.dsum) + ((int64_t)b * p.H + iss_h) * sst, sst);
-    TileLayout<D>::template issue<NPAIR>(trs, trow, (uint32_t)iss_it * kT * trow, role_a ? sm.q[slot] : sm.o[slot], lane,
-                                         pair);
-    vec_to_lds<8>(srs, (uint32_t)(iss_it * kT + 8 * pair) * 4, (role_a ? sm.l[slot] : sm.d[slot]) + 8 * pair, lane);
+    if (pair < NCOPY) {  // four waves of the role, a quarter of the tile and 8 statistics each
+      TileLayout<D>::template issue<NCOPY>(trs, trow, (uint32_t)iss_it * kT * trow, role_a ? sm.q[slot] : sm.o[slot],
+                                           lane, pair);
+      vec_to_lds<8>(srs, (uint32_t)(iss_it * kT + 8 * pair) * 4, (role_a ? sm.l[slot] : sm.d[slot]) + 8 * pair, lane);
+    }
     if (++iss_it == qhi) {
       iss_it = qlo;
       ++iss_h;
@@ -286,7 +295,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(kD
     if constexpr (!A) {
       u32x4* z = (u32x4*)sm.q[NB - 1];
 #pragma unroll
-      for (int i = tid - 256; i < TileLayout<D>::BYTES / 16; i += 256) z[i] = u32x4{0, 0, 0, 0};
+      for (int i = pair * 64 + lane; i < TileLayout<D>::BYTES / 16; i += 64 * NPAIR) z[i] = u32x4{0, 0, 0, 0};
     }
 
     f32x16 acc[DB];  // dV^T (A) or dK^T (B)
@@ -692,7 +701,8 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
   constexpr int RPB = kThreads / (D / 8);
   const int64_t prep_bpb = (stat_stride(p.Nq) + RPB - 1) / RPB;
   const int64_t g0 = prep_bpb * BH;
-  const int64_t g1 = (int64_t)((p.Nk + 127) / 128) * BHkv * p.S;
+  constexpr int BNK = 32 * kDkvPairs<D>;  // keys per dK/dV workgroup
+  const int64_t g1 = (int64_t)((p.Nk + BNK - 1) / BNK) * BHkv * p.S;
   const int64_t rrows = BHkv * (int64_t)p.Nk;  // rows of dK (and of dV)
   const int64_t gr = (2 * rrows * (D / 8) + kThreads - 1) / kThreads;
   const int64_t g2 = (int64_t)((p.Nq + 127) / 128) * BH;
@@ -704,7 +714,7 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((stages & 2) && g1 > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP>), dim3((unsigned)g1), dim3(2 * kThreads), 0, stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP>), dim3((unsigned)g1), dim3(128 * kDkvPairs<D>), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.S > 1) {
       hipLaunchKernelGGL((dkdv_reduce_kernel<D, DT>), dim3((unsigned)gr), dim3(kThreads), 0, stream, p, (int)rrows);
@@ -740,11 +750,12 @@ float* bwd_lse2_region(void* workspace, int B, int H, int Nq) {
 // Enough dK/dV workgroups to balance a causal band over the chip: at least
 // 1024 (four per CU), splitting each K/V head's G query heads into S groups,
 // S the smallest divisor of G that gets there (else G).
-int bwd_kv_splits(int B, int H, int H_kv, int Nk) {
+int bwd_kv_splits(int B, int H, int H_kv, int Nk, int d) {
   if (H_kv <= 0 || H % H_kv != 0) return 1;
   const int G = H / H_kv;
   if (G == 1) return 1;
-  const int64_t base = (int64_t)((Nk + 127) / 128) * B * H_kv;
+  const int bnk = 32 * (d == 64 ? kDkvPairs<64> : kDkvPairs<128>);
+  const int64_t base = (int64_t)((Nk + bnk - 1) / bnk) * B * H_kv;
   for (int S = 1; S < G; ++S)
     if (G % S == 0 && base * S >= 1024) return S;
   return G;
@@ -752,7 +763,7 @@ int bwd_kv_splits(int B, int H, int H_kv, int Nk) {
 
 size_t bwd_split_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d) {
   const size_t stats = bwd_workspace_bytes(B, H, Nq);
-  const int S = bwd_kv_splits(B, H, H_kv, Nk);
+  const int S = bwd_kv_splits(B, H, H_kv, Nk, d);
   if (S <= 1) return stats;
   return stats + 2 * (size_t)S * (size_t)B * (size_t)H_kv * (size_t)Nk * (size_t)d * sizeof(float);
 }

@@ -85,7 +85,7 @@ size_t bwd_workspace_bytes(int B, int H, int Nq);
 float* bwd_lse2_region(void* workspace, int B, int H, int Nq);
 // Split of each K/V head's query heads for the dK/dV stage (1 = none) and
 // the workspace bytes that split needs in total (statistics included).
-int bwd_kv_splits(int B, int H, int H_kv, int Nk);
+int bwd_kv_splits(int B, int H, int H_kv, int Nk, int d);
 size_t bwd_split_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d);
 // stages: OR of 1 (row statistics), 2 (dK, dV), 4 (dQ), run in that order.
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int stages, hipStream_t stream);

@@ -299,9 +299,14 @@ def test_ex_workspace_bytes():
     base = fa.fa_bwd_workspace_bytes(1, 16, 16384, 16384, 128, fa.FA_BF16)
     # equal heads: nothing extra
     assert fa.fa_bwd_ex_workspace_bytes(1, 16, 16, 16384, 16384, 128, fa.FA_BF16) == base
-    # 16 query heads on 2 K/V heads at 16K: 128 key blocks x 2 = 256 dK/dV workgroups, split 4 ways
+    # 16 query heads on 2 K/V heads at 16K, d = 128 (192 keys per dK/dV
+    # workgroup): 86 key blocks x 2 = 172 workgroups, split 8 ways to reach 1024
     big = fa.fa_bwd_ex_workspace_bytes(1, 16, 2, 16384, 16384, 128, fa.FA_BF16)
-    assert big == base + 2 * 4 * 1 * 2 * 16384 * 128 * 4
+    assert big == base + 2 * 8 * 1 * 2 * 16384 * 128 * 4
+    # d = 64 (128 keys per workgroup): 128 x 2 = 256 workgroups, split 4 ways
+    base64 = fa.fa_bwd_workspace_bytes(1, 16, 16384, 16384, 64, fa.FA_BF16)
+    assert fa.fa_bwd_ex_workspace_bytes(1, 16, 2, 16384, 16384, 64, fa.FA_BF16) == \
+        base64 + 2 * 4 * 1 * 2 * 16384 * 64 * 4
     # a problem that already fills the chip is not split
     assert fa.fa_bwd_ex_workspace_bytes(8, 64, 8, 16384, 16384, 128, fa.FA_BF16) == \
         fa.fa_bwd_workspace_bytes(8, 64, 16384, 16384, 128, fa.FA_BF16)
