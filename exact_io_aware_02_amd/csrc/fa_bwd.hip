@@ -383,8 +383,6 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
       } else {
         auto phase = [&](const uint16_t* __restrict__ Ot, const float* __restrict__ Dt,
                          const uint16_t* __restrict__ Qprev) {
-          // dK^T += Q^T dS of the previous tile
-          tile_t_times<D, DT>(acc, Qprev, pk, ta);
           // dP - D in one pass: the accumulator starts at -D of its row
           // (with dropout at 0: -D is added after the mask)
           f32x16 dinit = f32x16{};
@@ -399,6 +397,9 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
             }
           }
           sd = rows_times_regs<D, DT>(Ot, kv, ta, dinit);
+          // dK^T += Q^T dS of the previous tile, after dP: dS of this tile
+          // (the next phase) waits only for dP, so its MFMAs go first
+          tile_t_times<D, DT>(acc, Qprev, pk, ta);
           // issue order: operand reads kReadLead MFMAs ahead of their use
           sched_reads_ahead<2 * DB + KS, (4 * DB + 4 + KS)>();
         };
