@@ -39,6 +39,7 @@ the same cap.
 """
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -62,10 +63,15 @@ def log(*a):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code with comments and whitespace
+    removed: a change of a comment leaves the counters valid, a change of
+    code does not."""
     h = hashlib.sha256()
     for f in ("fa_device.h", "fa_kernels.h", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip"):
-        with open(os.path.join(ROOT, "exact_io_aware_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "exact_io_aware_02_amd", "csrc", f), encoding="utf-8") as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

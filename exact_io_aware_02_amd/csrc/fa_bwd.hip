@@ -11,11 +11,12 @@
 // Three kernels, deterministic (no atomics):
 //   prep_kernel  -D_i = -dO_i . O_i and lse_i * log2(e) per query row, into
 //                the workspace (HBM bound, tiny).
-//   dkdv_kernel  a workgroup of eight waves owns 128 keys; the two waves
-//                of a pair share 32 keys and one SIMD and split the work by
-//                role (A: K in registers, S, P, dV; B: V in registers, dP,
-//                dS, dK, with P handed over through LDS), skewed so that
-//                one role's MFMAs run under the other's VALU work.
+//   dkdv_kernel  a workgroup of NPAIR pairs of waves owns 32 * NPAIR keys
+//                (six pairs at d = 128, four at d = 64); the two waves of a
+//                pair share 32 keys and split the work by role (A: K in
+//                registers, S, P, dV; B: V in registers, dP, dS, dK, with P
+//                handed over through LDS), skewed so that one role's MFMAs
+//                run under the other's VALU work.
 //                32-query tiles of Q, dO and the two row statistics stream
 //                HBM -> LDS through a 4-slot ring.  S = Q K^T and dP = dO V^T
 //                come out with a key per lane, which is the B-operand
