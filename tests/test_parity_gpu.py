@@ -132,6 +132,24 @@ def long_ctx():
     return w, inp, s, o, lse, (dq, dk, dv)
 
 
+def test_long_context_repeat_runs_bitwise(long_ctx):
+    """Thirty forward runs (the phased schedule of grids of 512+ workgroups)
+    and ten backward runs of the 16K workload are bitwise identical to the
+    first: no result depends on how the waves happen to interleave."""
+    w, inp, s, o, lse, grads = long_ctx
+    q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
+    o0, l0 = gpu(o), gpu(lse)
+    for i in range(30):
+        o1, l1 = fa.attention_fwd(q, k, v, causal=True, scale=s, layout=w.layout)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o0) and torch.equal(l1, l0), "forward run %d differs" % i
+    g0 = [gpu(g) for g in grads]
+    for i in range(10):
+        g1 = fa.attention_bwd(q, k, v, o0, l0, do, causal=True, scale=s, layout=w.layout)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(g1, g0)), "backward run %d differs" % i
+
+
 def test_long_context_sampled_rows(long_ctx):
     """256 seeded query rows per head (rows 0 and N-1 always), every head."""
     w, inp, s, o, lse, _ = long_ctx
