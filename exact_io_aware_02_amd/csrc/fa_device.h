@@ -318,8 +318,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // including the prefetch that should stay in flight.  Ordering of the LDS
 // rings comes from the explicit vmcnt waits before it; the empty asm
 // statements keep the compiler from moving memory accesses across it.
+// The wave's own LDS reads must also be complete (lgkmcnt 0) when it
+// arrives: the compiler may place the MFMAs that consume the last reads
+// after the barrier, and their lgkmcnt waits with them, while the copies
+// issued after the barrier may refill the slot those reads come from.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
