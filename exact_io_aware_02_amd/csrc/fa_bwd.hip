@@ -30,6 +30,7 @@
 //                reads K^T transposed from the K tile.  Each step forms
 //                dS of tile j on the VALU, then issues dQ(j) and the S and
 //                dP MFMAs of tile j+1 as one interleaved run.
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -696,6 +697,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
   if (qi < p.Nq) store_rows<DT, DB>(p.dq + b * p.sdq.b + h * p.sdq.h + qi * p.sdq.s, adq, p.scale, half);
 }
 
+// dK/dV and dQ are independent once the row statistics exist.  When the
+// dK/dV grid is at most two waves of the chip, each kernel leaves most CUs
+// idle, so dQ runs beside dK/dV on a side stream: an event recorded on the
+// caller's stream forks it, and one recorded on the side stream joins it
+// back, so every result is ordered on the caller's stream as before.  One
+// side stream and two events per device, created on first use outside
+// graph capture and kept until the process ends; the lock pairs each fork
+// and join with their own event records when host threads call at once.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  int cus = 0;
+  bool ready = false;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxSideDevices];
+
+// The side stream of the current device, creating it if needed; nullptr if
+// there is none (then everything runs on the caller's stream).  Call with
+// g_side_mu held.
+SideStream* side_stream(hipStream_t caller) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (ss.ready) return &ss;
+  // creating streams and events is not allowed while a graph is captured
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  if (hipDeviceGetAttribute(&ss.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ss.cus <= 0)
+    return nullptr;
+  if (!ss.s && hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) {
+    ss.s = nullptr;
+    return nullptr;
+  }
+  if (!ss.fork && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) {
+    ss.fork = nullptr;
+    return nullptr;
+  }
+  if (!ss.join && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+    ss.join = nullptr;
+    return nullptr;
+  }
+  ss.ready = true;
+  return &ss;
+}
+
 template <int D, int DT, bool BAND, bool DROP>
 hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
   const int64_t BH = (int64_t)p.B * p.H;
@@ -715,14 +763,37 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
     hipLaunchKernelGGL((prep_kernel<D, DT>), dim3((unsigned)g0), dim3(kThreads), 0, stream, p, (int)prep_bpb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((stages & 2) && g1 > 0) {
+  const bool both = (stages & 2) && g1 > 0 && (stages & 4) && g2 > 0;
+  std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
+  if (both) {
+    lk.lock();
+    side = side_stream(stream);
+    // dK/dV workgroups resident per CU: one at d = 128, two at d = 64
+    if (side && g1 > (int64_t)2 * side->cus * (D == 64 ? 2 : 1)) side = nullptr;
+    if (!side) lk.unlock();
+  }
+  if (side) {
+    if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
+    // from here on the side stream is joined back even if a launch fails
+    hipLaunchKernelGGL((dq_kernel<D, DT, BAND, DROP>), dim3((unsigned)g2), dim3(kThreads), 0, side->s, p);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && (stages & 2) && g1 > 0) {
     hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP>), dim3((unsigned)g1), dim3(128 * kDkvPairs<D>), 0, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (p.S > 1) {
+    e = hipGetLastError();
+    if (e == hipSuccess && p.S > 1) {
       hipLaunchKernelGGL((dkdv_reduce_kernel<D, DT>), dim3((unsigned)gr), dim3(kThreads), 0, stream, p, (int)rrows);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      e = hipGetLastError();
     }
   }
+  if (side) {
+    hipError_t ej = hipEventRecord(side->join, side->s);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(stream, side->join, 0);
+    return e != hipSuccess ? e : ej;
+  }
+  if (e != hipSuccess) return e;
   if ((stages & 4) && g2 > 0) {
     hipLaunchKernelGGL((dq_kernel<D, DT, BAND, DROP>), dim3((unsigned)g2), dim3(kThreads), 0, stream, p);
     e = hipGetLastError();

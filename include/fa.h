@@ -169,7 +169,14 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
  *   workspace: caller-owned device memory of at least
  *   fa_bwd_workspace_bytes(...) bytes, 256-byte aligned; contents on entry
  *   are ignored and on return unspecified.  P is recomputed as
- *   exp(scale q.k - lse); dS = P * (dP - D) with dP = dO V^T. */
+ *   exp(scale q.k - lse); dS = P * (dP - D) with dP = dO V^T.
+ * Streams: all work is ordered on `stream`.  When the dK/dV grid is at most
+ * two waves of the chip, the dQ kernel runs on a side stream that the
+ * library forks from `stream` and joins back to it with events (one
+ * non-blocking stream and two events per device, created by the first such
+ * call made outside graph capture and kept until the process exits; calls
+ * from several host threads take a short internal lock).  The fork and join
+ * are capturable, so a captured call replays the same way. */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv,
            int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
@@ -192,7 +199,8 @@ int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, c
  * and lse_i * log2(e) into the workspace; FA_BWD_DKDV (dK, dV) and FA_BWD_DQ (dQ) read it and are
  * independent of each other, so after PREP has completed they may run on
  * two streams at once.  Stages in one call run in the order PREP, DKDV, DQ
- * on `stream`.  Same arguments and checks as fa_bwd_strided; `stages` is a
+ * on `stream`, except that a call with both DKDV and DQ may run DQ on the
+ * side stream described at fa_bwd.  Same arguments and checks as fa_bwd_strided; `stages` is a
  * nonzero OR of the flags below. */
 enum { FA_BWD_PREP = 1, FA_BWD_DKDV = 2, FA_BWD_DQ = 4, FA_BWD_ALL = 7 };
 int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const float* lse,

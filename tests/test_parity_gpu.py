@@ -430,3 +430,43 @@ def test_d64_full_chip_every_head(dtype, causal):
     ro, rl = attention_fwd64(q, k, v, 1 / 8.0, causal)
     check_o(o, ro, dtype, "bhsd")
     check_lse(lse, rl)
+
+
+@pytest.mark.parametrize("B,H,N,d,dt", [(2, 8, 1024, 64, "fp16"), (1, 4, 1000, 128, "bf16")])
+def test_small_backward_side_stream(B, H, N, d, dt):
+    """A backward whose dK/dV grid is under two waves of the chip runs dQ on
+    the library's side stream.  Its results equal the three stages run one
+    after another on the caller's stream, bit for bit, and so do replays of
+    a captured graph of it, with eager work on the outputs between them."""
+    say("case B%d H%d N%d d%d %s" % (B, H, N, d, dt))
+    inp = make_qkv(B, H, N, N, d, dt, seed=5, with_do=True)
+    q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
+    s = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd(q, k, v, causal=True, scale=s)
+    code = fa.FA_FP16 if dt == "fp16" else fa.FA_BF16
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d, code), dtype=torch.uint8, device=DEV)
+    ref = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    for st in (fa.FA_BWD_PREP, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
+        fa.fa_bwd_stages(q, k, v, o, lse, do, *ref, s, True, ws, st)
+    got = [torch.empty_like(t) for t in ref]
+    fa.fa_bwd(q, k, v, o, lse, do, *got, s, True, ws)
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.fa_bwd(q, k, v, o, lse, do, *got, s, True, ws, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.fa_bwd(q, k, v, o, lse, do, *got, s, True, ws, torch.cuda.current_stream())
+    for i in range(3):
+        for t in got:
+            t.fill_(float(i + 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), "replay %d" % i
