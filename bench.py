@@ -487,14 +487,16 @@ def main():
 
     def roof(name):
         kk = kernels[name]
+        tr = measured_traffic(name)
+        gbs = None if tr is None else tr / (kk["ms"] * 1e-3) / 1e9  # measured HBM GB/s
         if "flop" in kk:
             ach = kk["flop"] / (kk["ms"] * 1e-3) / 1e12
             return {"kernel": name, "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                    "frac": ach / peak, "traffic": measured_traffic(name), "ms_per_launch": kk["ms"],
+                    "frac": ach / peak, "traffic": tr, "traffic_gbs": gbs, "ms_per_launch": kk["ms"],
                     "algorithmic_flop_per_launch": kk["flop"]}
         ach = kk["bytes"] / (kk["ms"] * 1e-3) / 1e9
         return {"kernel": name, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": ach / PEAK_HBM_GBS, "traffic": measured_traffic(name), "ms_per_launch": kk["ms"],
+                "frac": ach / PEAK_HBM_GBS, "traffic": tr, "traffic_gbs": gbs, "ms_per_launch": kk["ms"],
                 "algorithmic_bytes_per_launch": kk["bytes"]}
 
     dominant = max(kernels, key=lambda n: kernels[n]["ms"])
