@@ -20,7 +20,8 @@ event-measured average duration; the dominant one is reported as `roofline`
 rows_f: the same step for the built extensions on the same inputs: 16 query
 heads on 2 K/V heads (causal), a causal sliding window of 256 keys (the skill
 guide's window example), and causal dropout with p = 0.1 (the skill guide's
-dropout_p); plus the fp8 forward alone on the inputs cast to float8_e4m3fn
+dropout_p); the plain step on 2 of the 16 heads (one GPU's share under 8-way
+head sharding); plus the fp8 forward alone on the inputs cast to float8_e4m3fn
 (priced against the fp8 MFMA peak, 5.0 PFLOP/s).  FLOPs count admitted
 (query, key) pairs.
 
@@ -314,20 +315,28 @@ def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
                                desc="B1 H16 N16384 d128 bf16 causal, window %r" % (WINDOW,)),
         "dropout": dict(k=k, v=v, window=(-1, -1), pairs=pairs_causal, dropout=DROPOUT,
                         desc="B1 H16 N16384 d128 bf16 causal, dropout_p %g" % DROPOUT[0]),
+        # one GPU's share if the 16 heads were split over 8 GPUs (no exchange
+        # is needed between them): the same kernels on 2 heads
+        "head_shard_8": dict(q=q[:, :2].contiguous(), do=do[:, :2].contiguous(), k=k[:, :2].contiguous(),
+                             v=v[:, :2].contiguous(), window=(-1, -1), pairs=pairs_causal, dropout=None,
+                             desc="B1 H2 N16384 d128 bf16 causal (2 of the 16 heads: one GPU of 8 under head "
+                                  "sharding)"),
     }
     for name, c in cases.items():
-        o = torch.empty_like(q)
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(c["k"]), torch.empty_like(c["v"])
+        qc, dc = c.get("q", q), c.get("do", do)
+        Hc = qc.shape[1]
+        o = torch.empty_like(qc)
+        lse = torch.empty((B, Hc, N), dtype=torch.float32, device=q.device)
+        dq, dk, dv = torch.empty_like(qc), torch.empty_like(c["k"]), torch.empty_like(c["v"])
         # with fewer K/V heads, the workspace that lets the dK/dV stage split
-        ws = torch.empty(fa.fa_bwd_ex_workspace_bytes(B, H, c["k"].shape[1], N, N, d, fa.FA_BF16), dtype=torch.uint8,
+        ws = torch.empty(fa.fa_bwd_ex_workspace_bytes(B, Hc, c["k"].shape[1], N, N, d, fa.FA_BF16), dtype=torch.uint8,
                          device=q.device)
 
         def fwd():
-            fa.fa_fwd_ex(q, c["k"], c["v"], o, lse, s, True, c["window"], "bhsd", stream, c["dropout"])
+            fa.fa_fwd_ex(qc, c["k"], c["v"], o, lse, s, True, c["window"], "bhsd", stream, c["dropout"])
 
         def bwd():
-            fa.fa_bwd_ex(q, c["k"], c["v"], o, lse, do, dq, dk, dv, s, True, ws, c["window"], fa.FA_BWD_ALL,
+            fa.fa_bwd_ex(qc, c["k"], c["v"], o, lse, dc, dq, dk, dv, s, True, ws, c["window"], fa.FA_BWD_ALL,
                          "bhsd", stream, c["dropout"])
 
         for _ in range(2):
@@ -345,7 +354,7 @@ def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
             tf += ev[0].elapsed_time(ev[1])
             tb += ev[1].elapsed_time(ev[2])
         tf, tb = tf / steps, tb / steps
-        ff = 4.0 * B * H * d * c["pairs"]
+        ff = 4.0 * B * Hc * d * c["pairs"]
         res[name] = {"workload": c["desc"], "fwd_ms": tf, "bwd_ms": tb,
                      "fwd_tflops": ff / tf / 1e9, "bwd_tflops": 2.5 * ff / tb / 1e9,
                      "step_tflops": 3.5 * ff / (tf + tb) / 1e9, "fwd_frac_of_peak": ff / tf / 1e9 / peak}
