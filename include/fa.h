@@ -28,7 +28,9 @@
  *    library never allocates, frees or retains them, and never synchronises.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued asynchronously on it; a kernel fault shows at the
- *    caller's next synchronisation, as usual in HIP.
+ *    caller's next synchronisation, as usual in HIP.  The current HIP device
+ *    (hipSetDevice) must be the one that owns `stream` and the pointers:
+ *    kernels and fa_bwd's side stream go to the current device.
  *  - Element type of Q, K, V, O, dO, dQ, dK, dV is `dtype` (FA_FP16 or
  *    FA_BF16; fp32 is not supported, as the skill guide's "精度が落ちる"
  *    issue and the glossary article's FP32 anti-pattern state), except in
