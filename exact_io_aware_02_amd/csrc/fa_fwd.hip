@@ -5,7 +5,8 @@
 // sum never leave the wave (FlashAttention-2's point of less communication
 // between warps, refbase Q&A on FA2's improvements).  K/V tiles of BN = 32
 // keys stream from HBM straight into LDS (buffer_load ... lds, no staging
-// registers) through a 4-slot ring.  Per tile and wave:
+// registers) through a ring of 4 slots (3 in the phased schedule at
+// d = 128, see FwdCfg).  Per tile and wave:
 //
 //   S^T = K_j Q^T          32x32x16 MFMAs; A = K rows from LDS, B = Q held
 //                          in registers for the whole loop.  Each lane
