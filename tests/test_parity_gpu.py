@@ -470,3 +470,38 @@ def test_small_backward_side_stream(B, H, N, d, dt):
         torch.cuda.synchronize()
         for a, b in zip(got, ref):
             assert torch.equal(a, b), "replay %d" % i
+
+
+def test_small_backward_from_two_host_threads():
+    """Two host threads run small backwards (side-stream path) on their own
+    streams at the same time, 20 calls each; every result equals the
+    single-threaded one bit for bit (the fork and join stay paired)."""
+    import threading
+
+    B, H, N, d = 2, 8, 1024, 64
+    inp = make_qkv(B, H, N, N, d, "fp16", seed=6, with_do=True)
+    q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
+    s = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd(q, k, v, causal=True, scale=s)
+    ref = fa.attention_bwd(q, k, v, o, lse, do, causal=True, scale=s)
+    torch.cuda.synchronize()
+    bad = []
+
+    def worker(idx):
+        torch.cuda.set_device(DEV)
+        st = torch.cuda.Stream(device=DEV)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_FP16), dtype=torch.uint8, device=DEV)
+        outs = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+        st.wait_stream(torch.cuda.default_stream(DEV))
+        for i in range(20):
+            fa.fa_bwd(q, k, v, o, lse, do, *outs, s, True, ws, st)
+            st.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(outs, ref)):
+                bad.append((idx, i))
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not bad, bad
