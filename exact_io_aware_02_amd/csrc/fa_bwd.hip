@@ -386,7 +386,7 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
         auto phase = [&](const uint16_t* __restrict__ Ot, const float* __restrict__ Dt,
                          const uint16_t* __restrict__ Qprev) {
           // at d = 64 (four waves per SIMD) a wave issuing MFMAs goes first
-          // (1-2.5% measured); at d = 128 it made no difference
+          // (1-2.5% measured); at d = 128 it was 1% slower
           if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
           // dP - D in one pass: the accumulator starts at -D of its row
           // (with dropout at 0: -D is added after the mask)
