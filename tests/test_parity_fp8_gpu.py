@@ -173,11 +173,11 @@ PHASED_CASES = [
 
 @pytest.mark.parametrize("case", PHASED_CASES, ids=[c[0] for c in PHASED_CASES])
 def test_fp8_fwd_phased_schedule(case):
-    """From 512 workgroups of 128 queries the fp8 forward runs its phased
-    schedule: a small case repeated along the batch to that size, the first
+    """From 768 (d = 128) or 1536 (d = 64) workgroups of 128 queries the
+    fp8 forward runs its phased schedule: a small case repeated along the batch to that size, the first
     copy against the oracle and every copy bitwise equal to it."""
     name, B, H, Hkv, Nq, Nk, d, layout, causal, window, descale = case
-    R = math.ceil(512 / (math.ceil(Nq / 128) * B * H))
+    R = math.ceil({64: 1536, 128: 768}[d] / (math.ceil(Nq / 128) * B * H))
     say("case phased %s (%d copies)" % (name, R))
     inp = make_qkv(B, H, Nq, Nk, d, "fp8", layout, seed=71, Hkv=Hkv)
     rep = {x: inp[x].view(torch.uint8).repeat(R, 1, 1, 1).view(torch.float8_e4m3fn) for x in ("q", "k", "v")}

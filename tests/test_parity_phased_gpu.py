@@ -1,9 +1,9 @@
-"""GPU parity of the forward's phased schedule, used from 512 workgroups of
-128 queries upward (the other GPU tests mostly launch smaller grids, which
+"""GPU parity of the forward's phased schedule, used from 1024 (d = 128) or
+1536 (d = 64) workgroups of 128 queries upward (the other GPU tests mostly launch smaller grids, which
 run the interleaved schedule).
 
 Each case is a small problem repeated along the batch until the grid
-reaches 512 workgroups.  The first copy is checked against the fp64 oracle
+reaches that many workgroups.  The first copy is checked against the fp64 oracle
 (tolerances of the other parity tests).  Without dropout every copy must
 then equal the first bit for bit.  With dropout the copies draw different
 masks, since the generator's counter holds the batch index.
@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 TOL_O = {"fp16": 2e-3, "bf16": 1.6e-2}
 TOL_LSE = 1e-3
 DEV = "cuda:0"
-PHASED_MIN_BLOCKS = 512
+PHASED_MIN_BLOCKS = {64: 1536, 128: 1024}
 
 
 def say(*a):
@@ -50,7 +50,7 @@ CASES = [
 def test_phased_forward_matches_oracle(case):
     name, B, H, Hkv, Nq, Nk, d, dt, layout, causal, window, dr = case
     blocks = math.ceil(Nq / 128) * B * H
-    R = math.ceil(PHASED_MIN_BLOCKS / blocks)
+    R = math.ceil(PHASED_MIN_BLOCKS[d] / blocks)
     say("case %s: %d copies, %d workgroups" % (name, R, R * blocks))
     inp = make_qkv(B, H, Nq, Nk, d, dt, layout, seed=61, Hkv=Hkv)
     q, k, v = (inp[x].repeat(R, 1, 1, 1).to(DEV) for x in ("q", "k", "v"))
