@@ -47,16 +47,23 @@ _u64, _u32 = ctypes.c_uint64, ctypes.c_uint32
 _I64x3 = ctypes.c_int64 * 3
 
 
+_STATUS_NAMES = {FA_OK: "FA_OK", FA_ERR_INVALID_ARG: "FA_ERR_INVALID_ARG", FA_ERR_UNSUPPORTED: "FA_ERR_UNSUPPORTED",
+                 FA_ERR_DEVICE: "FA_ERR_DEVICE", FA_ERR_LAUNCH: "FA_ERR_LAUNCH"}
+
+
 class FaError(RuntimeError):
-    """A nonzero status from libfa.so."""
+    """A nonzero status from libfa.so, or an argument the binding rejects
+    before calling it (with the status the library uses for such errors)."""
 
     def __init__(self, status, detail):
         self.status = status
-        super().__init__("%s: %s" % (fa_status_string(status), detail))
+        super().__init__("%s: %s" % (_STATUS_NAMES.get(status, "FA_UNKNOWN_STATUS"), detail))
 
 
 def lib_path():
-    return os.path.join(_HERE, "libfa.so")
+    """The in-tree libfa.so, or the file EXACT_IO_AWARE_FA_LIB names (the
+    sanitizer build of the host code uses this)."""
+    return os.environ.get("EXACT_IO_AWARE_FA_LIB") or os.path.join(_HERE, "libfa.so")
 
 
 def load_library():
@@ -153,10 +160,89 @@ def _axes(layout):
 
 def _dims(t, layout):
     """(B, H, N, d) of a 4-D tensor in the given layout."""
-    if t.dim() != 4:
-        raise ValueError("expected a 4-D tensor, got shape %r" % (tuple(t.shape),))
     ab, ah, as_, ad = _axes(layout)
+    if t.dim() != 4:
+        raise FaError(FA_ERR_INVALID_ARG, "expected a 4-D tensor, got shape %r" % (tuple(t.shape),))
     return t.shape[ab], t.shape[ah], t.shape[as_], t.shape[ad]
+
+
+# ---------------------------------------------------------------- validation
+# Every extent the library uses comes from q's and k's sizes, so each other
+# tensor is checked against them here, before the call: a smaller v, dO or
+# dV, an lse that is not fp32 [B, H, Nq], or a mixed fp16/bf16 set would
+# otherwise be read or written out of bounds, or reinterpreted.
+
+def _bad(msg):
+    raise FaError(FA_ERR_INVALID_ARG, msg)
+
+
+def _want_shape(name, t, shape):
+    if tuple(t.shape) != tuple(shape):
+        _bad("%s has shape %r, expected %r" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _want_dtype(dtype, **ts):
+    for name, t in ts.items():
+        if t.dtype != dtype:
+            _bad("%s is %s, expected %s" % (name, t.dtype, dtype))
+
+
+def _want_contiguous(**ts):
+    for name, t in ts.items():
+        if not t.is_contiguous():
+            _bad("%s must be contiguous for this entry point (use the _strided/_ex variant)" % name)
+
+
+def _want_lse(lse, B, H, Nq):
+    if lse.dtype != torch.float32:
+        _bad("lse is %s, expected torch.float32" % lse.dtype)
+    _want_shape("lse", lse, (B, H, Nq))
+    if not lse.is_contiguous():
+        _bad("lse must be a contiguous [B, H, Nq] array")
+
+
+def _want_device(q, **ts):
+    if not q.is_cuda:
+        _bad("tensors must live on a HIP device (q is on %s)" % q.device)
+    for name, t in ts.items():
+        if not t.is_cuda:
+            _bad("tensors must live on a HIP device (%s is on %s)" % (name, t.device))
+        if t.device != q.device:
+            _bad("%s is on %s, q on %s" % (name, t.device, q.device))
+
+
+def _check_fwd(q, k, v, o, lse, layout, contiguous=False, same_heads=True, out_dtype=None, device=True):
+    """Validate a forward call; returns (B, H, H_kv, Nq, Nk, d)."""
+    B, H, Nq, d = _dims(q, layout)
+    Bk, Hkv, Nk, dk = _dims(k, layout)
+    _want_dtype(q.dtype, k=k, v=v)
+    _want_dtype(q.dtype if out_dtype is None else out_dtype, o=o)
+    if Bk != B or dk != d or (same_heads and Hkv != H):
+        _bad("k has %s dims (B, H, N, d) = %r, incompatible with q's %r" % (layout, (Bk, Hkv, Nk, dk), (B, H, Nq, d)))
+    _want_shape("v", v, k.shape)
+    _want_shape("o", o, q.shape)
+    _want_lse(lse, B, H, Nq)
+    if contiguous:
+        _want_contiguous(q=q, k=k, v=v, o=o)
+    if device:
+        _want_device(q, k=k, v=v, o=o, lse=lse)
+    return B, H, Hkv, Nq, Nk, d
+
+
+def _check_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, layout, contiguous=False, same_heads=True):
+    """Validate a backward call; returns (B, H, H_kv, Nq, Nk, d)."""
+    dims = _check_fwd(q, k, v, o, lse, layout, contiguous, same_heads, device=False)
+    _want_dtype(q.dtype, do=do, dq=dq, dk=dk, dv=dv)
+    _want_shape("dout", do, q.shape)
+    _want_shape("dq", dq, q.shape)
+    _want_shape("dk", dk, k.shape)
+    _want_shape("dv", dv, k.shape)
+    if contiguous:
+        _want_contiguous(do=do, dq=dq, dk=dk, dv=dv)
+    if not workspace.is_contiguous():
+        _bad("workspace must be contiguous")
+    _want_device(q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    return dims
 
 
 def _strides(t, layout):
@@ -174,9 +260,7 @@ def fa_fwd(q, k, v, o, lse, scale, causal, stream=None):
     """C ``fa_fwd`` on contiguous BHSD tensors: q/o [B,H,Nq,d], k/v [B,H,Nk,d],
     lse fp32 [B,H,Nq].  Enqueues on ``stream`` (default: current stream)."""
     dt = _dtype_code(q)
-    _on_device(q, k, v, o, lse)
-    B, H, Nq, d = _dims(q, "bhsd")
-    Nk = k.shape[2]
+    B, H, _, Nq, Nk, d = _check_fwd(q, k, v, o, lse, "bhsd", contiguous=True)
     with torch.cuda.device(q.device):
         _check(load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
                                      float(scale), int(bool(causal)), dt, _stream(q, stream)))
@@ -185,9 +269,7 @@ def fa_fwd(q, k, v, o, lse, scale, causal, stream=None):
 def fa_fwd_strided(q, k, v, o, lse, scale, causal, layout="bshd", stream=None):
     """C ``fa_fwd_strided``: the tensors' own strides, read in ``layout``."""
     dt = _dtype_code(q)
-    _on_device(q, k, v, o, lse)
-    B, H, Nq, d = _dims(q, layout)
-    Nk = _dims(k, layout)[2]
+    B, H, _, Nq, Nk, d = _check_fwd(q, k, v, o, lse, layout)
     with torch.cuda.device(q.device):
         _check(load_library().fa_fwd_strided(
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale), int(bool(causal)),
@@ -209,9 +291,7 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, stream=Non
     """C ``fa_bwd`` on contiguous BHSD tensors; ``workspace`` is a device
     tensor of at least ``fa_bwd_workspace_bytes`` bytes."""
     dt = _dtype_code(q)
-    _on_device(q, k, v, o, lse, do, dq, dk, dv, workspace)
-    B, H, Nq, d = _dims(q, "bhsd")
-    Nk = k.shape[2]
+    B, H, _, Nq, Nk, d = _check_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, "bhsd", contiguous=True)
     nbytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
         _check(load_library().fa_bwd(
@@ -223,9 +303,7 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, stream=Non
 def fa_bwd_strided(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, layout="bshd", stream=None):
     """C ``fa_bwd_strided``: every d-major tensor's own strides, read in ``layout``."""
     dt = _dtype_code(q)
-    _on_device(q, k, v, o, lse, do, dq, dk, dv, workspace)
-    B, H, Nq, d = _dims(q, layout)
-    Nk = _dims(k, layout)[2]
+    B, H, _, Nq, Nk, d = _check_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, layout)
     nbytes = workspace.numel() * workspace.element_size()
     st = [_strides(t, layout) for t in (q, k, v, o, do, dq, dk, dv)]
     with torch.cuda.device(q.device):
@@ -238,9 +316,7 @@ def fa_bwd_strided(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, la
 def fa_bwd_stages(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, stages, layout="bhsd", stream=None):
     """C ``fa_bwd_stages``: run the selected backward stages (OR of FA_BWD_*)."""
     dt = _dtype_code(q)
-    _on_device(q, k, v, o, lse, do, dq, dk, dv, workspace)
-    B, H, Nq, d = _dims(q, layout)
-    Nk = _dims(k, layout)[2]
+    B, H, _, Nq, Nk, d = _check_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, layout)
     nbytes = workspace.numel() * workspace.element_size()
     st = [_strides(t, layout) for t in (q, k, v, o, do, dq, dk, dv)]
     with torch.cuda.device(q.device):
@@ -265,9 +341,7 @@ def fa_fwd_ex(q, k, v, o, lse, scale, causal, window=(-1, -1), layout="bhsd", st
     ``window`` = (left, right), a negative side unbounded; ``dropout`` =
     (p, seed, offset) or None."""
     dt = _dtype_code(q)
-    _on_device(q, k, v, o, lse)
-    B, H, Nq, d = _dims(q, layout)
-    Hkv, Nk = _dims(k, layout)[1:3]
+    B, H, Hkv, Nq, Nk, d = _check_fwd(q, k, v, o, lse, layout, same_heads=False)
     wl, wr = _window(window)
     dp, seed, off = _dropout(dropout)
     with torch.cuda.device(q.device):
@@ -282,9 +356,7 @@ def fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, window=
     """C ``fa_bwd_ex``: the backward of ``fa_fwd_ex`` (dk, dv shaped like k,
     v; the same ``window`` and ``dropout``)."""
     dt = _dtype_code(q)
-    _on_device(q, k, v, o, lse, do, dq, dk, dv, workspace)
-    B, H, Nq, d = _dims(q, layout)
-    Hkv, Nk = _dims(k, layout)[1:3]
+    B, H, Hkv, Nq, Nk, d = _check_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, layout, same_heads=False)
     wl, wr = _window(window)
     dp, seed, off = _dropout(dropout)
     nbytes = workspace.numel() * workspace.element_size()
@@ -311,9 +383,7 @@ def fa_fwd_fp8(q, k, v, o, lse, scale, causal, window=(-1, -1), descale=(1.0, 1.
     _fp8_input(q, k, v)
     if o.dtype != torch.bfloat16:
         raise FaError(FA_ERR_UNSUPPORTED, "fp8 forward writes a bfloat16 o, got %s" % o.dtype)
-    _on_device(q, k, v, o, lse)
-    B, H, Nq, d = _dims(q, layout)
-    Hkv, Nk = _dims(k, layout)[1:3]
+    B, H, Hkv, Nq, Nk, d = _check_fwd(q, k, v, o, lse, layout, same_heads=False, out_dtype=torch.bfloat16)
     wl, wr = _window(window)
     qd, kd, vd = (float(x) for x in descale)
     with torch.cuda.device(q.device):

@@ -78,9 +78,12 @@ int check_tensor(const char* name, const void* ptr, const int64_t st[3], int B, 
                   (long long)st[i], unit);
   }
   if (N > 1 && st[2] < d) return fail(FA_ERR_INVALID_ARG, "%s seq stride %lld < d = %d (rows overlap)", name, (long long)st[2], d);
-  // within one (b, h) slice the kernels use 32-bit-safe offsets
+  // within one (b, h) slice the kernels use 32-bit-safe offsets, and a
+  // buffer resource's byte count (an unsigned 32-bit field) spans the slice
+  constexpr int64_t kMaxSliceElems = 0x7fffffffLL;
+  static_assert(kMaxSliceElems * 2 <= 0xffffffffLL, "a 16-bit head slice must fit a 32-bit byte count");
   const int64_t slice_max = (int64_t)(N - 1) * st[2] + d;
-  if (slice_max > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "%s: per-head extent exceeds 2^31 elements", name);
+  if (slice_max > kMaxSliceElems) return fail(FA_ERR_INVALID_ARG, "%s: per-head extent exceeds 2^31 elements", name);
   const int64_t last = (int64_t)(B - 1) * st[0] + (int64_t)(H - 1) * st[1] + (int64_t)(N - 1) * st[2] + d;
   if (last > (INT64_MAX / 4)) return fail(FA_ERR_INVALID_ARG, "%s: extent overflows", name);
   ext->lo_bytes = 0;

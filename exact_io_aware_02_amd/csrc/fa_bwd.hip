@@ -751,7 +751,7 @@ SideStream* side_stream(hipStream_t caller) {
 }
 
 template <int D, int DT, bool BAND, bool DROP>
-hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
+hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t stream) {
   const int64_t BH = (int64_t)p.B * p.H;
   const int64_t BHkv = (int64_t)p.B * (p.H / p.G);
   constexpr int RPB = kThreads / (D / 8);
@@ -769,7 +769,7 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
     hipLaunchKernelGGL((prep_kernel<D, DT>), dim3((unsigned)g0), dim3(kThreads), 0, stream, p, (int)prep_bpb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const bool both = (stages & 2) && g1 > 0 && (stages & 4) && g2 > 0;
+  const bool both = side_ok && (stages & 2) && g1 > 0 && (stages & 4) && g2 > 0;
   std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
   SideStream* side = nullptr;
   if (both) {
@@ -777,6 +777,13 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
     side = side_stream(stream);
     // dK/dV workgroups resident per CU: one at d = 128, two at d = 64
     if (side && g1 > (int64_t)2 * side->cus * (D == 64 ? 2 : 1)) side = nullptr;
+    // A captured call's fork makes the side stream part of that capture
+    // until the capture ends; meanwhile another call (eager, or captured
+    // elsewhere) must not enqueue onto it, so it runs dQ on its own stream.
+    if (side) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(side->s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) side = nullptr;
+    }
     if (!side) lk.unlock();
   }
   if (side) {
@@ -808,10 +815,12 @@ hipError_t launch_t(const BwdParams& p, int stages, hipStream_t stream) {
 }
 
 template <int D, int DT>
-hipError_t launch_dc(const BwdParams& p, bool banded, int stages, hipStream_t stream) {
+hipError_t launch_dc(const BwdParams& p, bool banded, int stages, bool side_ok, hipStream_t stream) {
   if (p.drop.thr > 0)
-    return banded ? launch_t<D, DT, true, true>(p, stages, stream) : launch_t<D, DT, false, true>(p, stages, stream);
-  return banded ? launch_t<D, DT, true, false>(p, stages, stream) : launch_t<D, DT, false, false>(p, stages, stream);
+    return banded ? launch_t<D, DT, true, true>(p, stages, side_ok, stream)
+                  : launch_t<D, DT, false, true>(p, stages, side_ok, stream);
+  return banded ? launch_t<D, DT, true, false>(p, stages, side_ok, stream)
+                : launch_t<D, DT, false, false>(p, stages, side_ok, stream);
 }
 
 }  // namespace
@@ -847,12 +856,13 @@ size_t bwd_split_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d) 
   return stats + 2 * (size_t)S * (size_t)B * (size_t)H_kv * (size_t)Nk * (size_t)d * sizeof(float);
 }
 
-hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int stages, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int stages, hipStream_t stream,
+                      bool side_ok) {
   if (d == 64)
-    return dtype == DT_F16 ? launch_dc<64, DT_F16>(p, banded, stages, stream)
-                           : launch_dc<64, DT_BF16>(p, banded, stages, stream);
-  return dtype == DT_F16 ? launch_dc<128, DT_F16>(p, banded, stages, stream)
-                         : launch_dc<128, DT_BF16>(p, banded, stages, stream);
+    return dtype == DT_F16 ? launch_dc<64, DT_F16>(p, banded, stages, side_ok, stream)
+                           : launch_dc<64, DT_BF16>(p, banded, stages, side_ok, stream);
+  return dtype == DT_F16 ? launch_dc<128, DT_F16>(p, banded, stages, side_ok, stream)
+                         : launch_dc<128, DT_BF16>(p, banded, stages, side_ok, stream);
 }
 
 }  // namespace fa

@@ -285,14 +285,18 @@ __device__ __forceinline__ float sum_pair32(float x) { return x + __shfl_xor(x, 
 // ---------------------------------------------------------------- HBM -> LDS
 
 // Buffer resource over one head's rows of a [N][d] 16-bit tensor with row
-// stride `stride` elements: loads past row n-1 return zeros.
+// stride `stride` elements: loads past row n-1 return zeros.  The byte
+// count is unsigned: the host admits per-head extents of up to 2^31 - 1
+// elements, i.e. up to 2^32 - 2 bytes, which the 32-bit field holds.
+__device__ __forceinline__ uint32_t rsrc_bytes(int64_t bytes) { return (uint32_t)bytes; }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int n, int64_t stride, int d) {
-  const int bytes = (int)(((int64_t)(n - 1) * stride + d) * 2);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+  const uint32_t bytes = rsrc_bytes(((int64_t)(n - 1) * stride + d) * 2);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, __builtin_bit_cast(int, bytes), 0x00020000);
 }
 // Buffer resource over n fp32 values (zeros past the end).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t f32_rsrc(const float* base, int n) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n * 4, 0x00020000);
+  const uint32_t bytes = rsrc_bytes((int64_t)n * 4);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, __builtin_bit_cast(int, bytes), 0x00020000);
 }
 
 // Asynchronous copy of N fp32 values (N a multiple of 4, at most 256) into

@@ -55,12 +55,23 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 // LDS tile [64 rows][D bytes]: 16-byte chunk c of row r lives at chunk
-// c ^ swz8(r), which keeps 16 consecutive rows at one chunk (the K operand
-// reads) and the transposing reads' 8 rows free of bank conflicts.
+// c ^ swz8(r).  Two read patterns must be free of bank conflicts (64 banks
+// of 4 bytes; a ds_read_b128 serves 16 lanes per cycle, a 64-bit read 32):
+//   K operand (ds_read_b128): 16 consecutive rows, one chunk;
+//   V^T operand (ds_read_b64_tr_b8): a half-wave reads the 8 rows
+//     {0..3, 8..11} (or {4..7, 12..15}) + 16 u of two adjacent chunks.
+// At d = 128 two rows share a 256-byte bank line; with e = (r >> 1) & 7 the
+// swizzle g(e) = 2 (e & 1) + (e & 4) + ((e >> 1) & 1) is a permutation of
+// 0..7 (K reads: the 8 rows of one parity land on 8 distinct chunks) whose
+// bits 1-2 take all four values on e in {0, 1, 4, 5} and on {2, 3, 6, 7}
+// (transposing reads: the 2 x 8 chunks of a half-wave are distinct).  The
+// plain e, used before, put chunk pairs of rows 0 and 2 on one bank group.
+// At d = 64 four rows share a bank line and (r >> 2) & 3 satisfies both.
 template <int D>
 __device__ __forceinline__ int swz8(int r) {
   if constexpr (D == 128) {
-    return (r >> 1) & 7;
+    const int e = (r >> 1) & 7;
+    return ((e & 1) << 1) | (e & 4) | ((e >> 1) & 1);
   } else {
     return (r >> 2) & 3;
   }
@@ -91,8 +102,8 @@ struct Tile8Copy {
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc8(const uint8_t* base, int n, int64_t stride, int d) {
-  const int bytes = (int)((int64_t)(n - 1) * stride + d);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+  const uint32_t bytes = rsrc_bytes((int64_t)(n - 1) * stride + d);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, __builtin_bit_cast(int, bytes), 0x00020000);
 }
 
 __device__ __forceinline__ u32x4 lds16(const uint8_t* base, int off) { return *(const u32x4*)(base + off); }

@@ -88,6 +88,8 @@ float* bwd_lse2_region(void* workspace, int B, int H, int Nq);
 int bwd_kv_splits(int B, int H, int H_kv, int Nk, int d);
 size_t bwd_split_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d);
 // stages: OR of 1 (row statistics), 2 (dK, dV), 4 (dQ), run in that order.
-hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int stages, hipStream_t stream);
+// side_ok = false keeps every stage on `stream` (no side stream for dQ).
+hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int stages, hipStream_t stream,
+                      bool side_ok = true);
 
 }  // namespace fa

@@ -130,7 +130,8 @@ def test_fp8_fwd_exact_weights(d, causal, Hkv):
 
 def test_fp8_fwd_16k_causal_sampled_rows():
     """The 16K-token causal d=128 shape (B=1, H=16, inputs 0.5 N(0,1) cast to
-    e4m3fn) in the launch the benchmark times, checked on sampled rows."""
+    e4m3fn) in the launch the benchmark times, checked on 256 seeded rows
+    of every head (rows 0 and N-1 always)."""
     B, H, N, d = 1, 16, 16384, 128
     say("case fp8_16k_causal (sampled rows)")
     inp = make_qkv(B, H, N, N, d, "fp8", "bhsd", seed=3, in_scale=0.5)
@@ -138,7 +139,7 @@ def test_fp8_fwd_16k_causal_sampled_rows():
     scale = 1.0 / math.sqrt(d)
     o, lse = fa.attention_fwd_fp8(q, k, v, causal=True, scale=scale)
     torch.cuda.synchronize()
-    rows = sample_rows(B, H, N, 12, seed=5)
+    rows = sample_rows(B, H, N, 256, seed=5)
     q8, k8, v8 = (fp8_bytes(inp[x]) for x in ("q", "k", "v"))
     o_ref, lse_ref = attention_fp8_rows_fwd64(q8, k8, v8, scale, True, rows)
     bound, sigma = fp8_rounding_model(q8, k8, v8, scale, True, rows)

@@ -505,3 +505,63 @@ def test_small_backward_from_two_host_threads():
     for t in ts:
         t.join()
     assert not bad, bad
+
+
+def test_small_backward_captured_while_another_thread_runs_eagerly():
+    """One thread captures a small backward (its dQ forks onto the library's
+    side stream, which then belongs to that capture until it ends) while a
+    second thread runs eager small backwards: the eager calls must keep off
+    the captured side stream.  Both the eager results and replays of the
+    graph equal the plain result bit for bit."""
+    import threading
+
+    B, H, N, d = 2, 8, 1024, 64
+    inp = make_qkv(B, H, N, N, d, "fp16", seed=8, with_do=True)
+    q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
+    s = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd(q, k, v, causal=True, scale=s)
+    ref = fa.attention_bwd(q, k, v, o, lse, do, causal=True, scale=s)  # also creates the side stream
+    torch.cuda.synchronize()
+    ws_a = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_FP16), dtype=torch.uint8, device=DEV)
+    ws_b = torch.empty_like(ws_a)
+    outs_a = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    outs_b = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    st_b = torch.cuda.Stream(device=DEV)
+    captured, eager_done = threading.Event(), threading.Event()
+    bad = []
+    g = torch.cuda.CUDAGraph()
+
+    def capturer():
+        torch.cuda.set_device(DEV)
+        with torch.cuda.graph(g, capture_error_mode="thread_local"):
+            fa.fa_bwd(q, k, v, o, lse, do, *outs_a, s, True, ws_a, torch.cuda.current_stream())
+            captured.set()
+            eager_done.wait(timeout=60)
+
+    def eager():
+        torch.cuda.set_device(DEV)
+        captured.wait(timeout=60)
+        try:
+            for i in range(5):
+                fa.fa_bwd(q, k, v, o, lse, do, *outs_b, s, True, ws_b, st_b)
+                st_b.synchronize()
+                if not all(torch.equal(a, b) for a, b in zip(outs_b, ref)):
+                    bad.append(("eager", i))
+        finally:
+            eager_done.set()
+
+    ta, tb = threading.Thread(target=capturer), threading.Thread(target=eager)
+    ta.start()
+    tb.start()
+    ta.join()
+    tb.join()
+    assert captured.is_set() and eager_done.is_set()
+    for i in range(3):
+        for t in outs_a:
+            t.fill_(float(i + 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(outs_a, ref)):
+            bad.append(("replay", i))
+    assert not bad, bad
