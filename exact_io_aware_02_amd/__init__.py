@@ -23,7 +23,8 @@ __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_DEVICE", "FA_ERR_LAUNCH",
     "FA_FP16", "FA_BF16", "FaError", "lib_path", "load_library",
     "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_fwd_fp8", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
-    "fa_bwd_ex", "fa_bwd_workspace_bytes", "fa_bwd_ex_workspace_bytes",
+    "fa_bwd_ex", "fa_bwd_workspace_bytes", "fa_bwd_ex_workspace_bytes", "fa_bwd_noalloc",
+    "FA_BWD_NOALLOC_SCRATCH_BYTES",
     "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
     "fa_status_string", "fa_last_error_message", "fa_abi_version",
     "attention_fwd", "attention_bwd", "attention_fwd_fp8", "EXPORTED_SYMBOLS",
@@ -35,9 +36,10 @@ FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED_SYMBOLS = (
     "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
-    "fa_bwd_ex", "fa_fwd_fp8", "fa_bwd_ex_workspace_bytes", "fa_status_string", "fa_last_error_message",
-    "fa_abi_version",
+    "fa_bwd_ex", "fa_fwd_fp8", "fa_bwd_ex_workspace_bytes", "fa_bwd_noalloc", "fa_status_string",
+    "fa_last_error_message", "fa_abi_version",
 )
+FA_BWD_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -97,6 +99,8 @@ def load_library():
     lib.fa_bwd_ex.restype = _i
     lib.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _i, _i, _f, _f, _f] + [_I64x3] * 4 + [_vp]
     lib.fa_fwd_fp8.restype = _i
+    lib.fa_bwd_noalloc.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp]
+    lib.fa_bwd_noalloc.restype = _i
     lib.fa_status_string.argtypes = [_i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error_message.argtypes = []
@@ -298,6 +302,24 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, stream=Non
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
             B, H, Nq, Nk, d, float(scale), int(bool(causal)), dt, _ptr(workspace), nbytes,
             _stream(q, stream)))
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale, causal, stream=None):
+    """C ``fa_bwd_noalloc``: ``fa_bwd`` with the library's own scratch as the
+    workspace (no allocation; calls that overlap on one GPU race)."""
+    dt = _dtype_code(q)
+    B, H, _, Nq, Nk, d = _check_fwd(q, k, v, o, lse, "bhsd", contiguous=True, device=False)
+    _want_dtype(q.dtype, do=do, dq=dq, dk=dk, dv=dv)
+    _want_shape("dout", do, q.shape)
+    _want_shape("dq", dq, q.shape)
+    _want_shape("dk", dk, k.shape)
+    _want_shape("dv", dv, k.shape)
+    _want_contiguous(do=do, dq=dq, dk=dk, dv=dv)
+    _want_device(q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv)
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_bwd_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, H, Nq, Nk, d, float(scale), int(bool(causal)), dt, _stream(q, stream)))
 
 
 def fa_bwd_strided(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, layout="bshd", stream=None):

@@ -13,6 +13,8 @@
 #include "../../include/fa.h"
 #include "fa_kernels.h"
 
+static_assert(fa::kNoAllocScratchBytes == FA_BWD_NOALLOC_SCRATCH_BYTES, "scratch size of fa.h and the kernels");
+
 namespace {
 
 thread_local char g_msg[512] = "";
@@ -163,7 +165,7 @@ void contiguous_strides(int H, int N, int d, int64_t st[3]) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 4; }
+int fa_abi_version(void) { return 5; }
 
 const char* fa_status_string(int status) {
   switch (status) {
@@ -313,13 +315,21 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
   return fa::bwd_workspace_bytes(B, H, Nq);
 }
 
-int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-              void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
-              int window_left, int window_right, float dropout_p, uint64_t seed, uint32_t offset, int dtype,
-              const int64_t q_strides[3], const int64_t k_strides[3],
-              const int64_t v_strides[3], const int64_t o_strides[3], const int64_t do_strides[3],
-              const int64_t dq_strides[3], const int64_t dk_strides[3], const int64_t dv_strides[3],
-              void* workspace, size_t workspace_bytes, int stages, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward behind fa_bwd_ex and fa_bwd_noalloc.  With `noalloc` the
+// workspace is the library's file-scope scratch array (workspace and
+// workspace_bytes are ignored), every stage stays on `stream`, and sizes
+// whose workspace exceeds the array are rejected.
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+             int window_left, int window_right, float dropout_p, uint64_t seed, uint32_t offset, int dtype,
+             const int64_t q_strides[3], const int64_t k_strides[3],
+             const int64_t v_strides[3], const int64_t o_strides[3], const int64_t do_strides[3],
+             const int64_t dq_strides[3], const int64_t dk_strides[3], const int64_t dv_strides[3],
+             void* workspace, size_t workspace_bytes, int stages, void* stream, bool noalloc) {
   g_msg[0] = '\0';
   int st = check_common(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st) return st;
@@ -343,10 +353,21 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   if (Nq > 0 && !lse) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   const size_t need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype);
-  if (need > 0 && !workspace) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(FA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-  if (workspace_bytes < need)
-    return fail(FA_ERR_INVALID_ARG, "workspace_bytes = %zu < required %zu", workspace_bytes, need);
+  if (noalloc) {
+    if (need > fa::kNoAllocScratchBytes)
+      return fail(FA_ERR_INVALID_ARG,
+                  "these sizes need %zu bytes of workspace, more than the %zu of the allocation-free scratch "
+                  "(B * H * round_up(Nq, 64) must be at most %zu)",
+                  need, fa::kNoAllocScratchBytes, fa::kNoAllocScratchBytes / 8);
+    workspace = nullptr;
+    workspace_bytes = 0;
+  } else {
+    if (need > 0 && !workspace) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(FA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_INVALID_ARG, "workspace_bytes = %zu < required %zu", workspace_bytes, need);
+  }
   // fewer K/V heads: split each K/V head's query heads over more dK/dV
   // workgroups when the workspace holds their partial sums
   const int splits = fa::bwd_kv_splits(B, H, H_kv, Nk, d);
@@ -356,7 +377,7 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   const void* ins[6] = {q, k, v, o, dout, lse};
   const Extent eins[6] = {eq, ek, ev, eo, edo, Extent{0, (int64_t)B * H * Nq * 4}};
   void* outs[4] = {dq, dk, dv, workspace};
-  const Extent eouts[4] = {edq, edk, edv, Extent{0, (int64_t)used}};
+  const Extent eouts[4] = {edq, edk, edv, Extent{0, noalloc ? 0 : (int64_t)used}};
   const char* onames[4] = {"dq", "dk", "dv", "workspace"};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
@@ -366,6 +387,13 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
         return fail(FA_ERR_INVALID_ARG, "%s overlaps %s", onames[i], onames[j]);
   }
   if ((st = check_device())) return st;
+  if (noalloc) {
+    hipError_t es = fa::bwd_scratch(&workspace);
+    if (es != hipSuccess || !workspace) {
+      (void)hipGetLastError();
+      return fail(FA_ERR_DEVICE, "scratch lookup (hipGetSymbolAddress) failed: %s", hipGetErrorString(es));
+    }
+  }
 
   fa::BwdParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -400,9 +428,35 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   p.c = scale * 1.4426950408889634f;
   p.S = split ? splits : 1;
   p.part = split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need) : nullptr;
-  hipError_t e = fa::launch_bwd(p, d, dtype, band.present(), stages, static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_bwd(p, d, dtype, band.present(), stages, static_cast<hipStream_t>(stream), !noalloc);
   if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+              int window_left, int window_right, float dropout_p, uint64_t seed, uint32_t offset, int dtype,
+              const int64_t q_strides[3], const int64_t k_strides[3],
+              const int64_t v_strides[3], const int64_t o_strides[3], const int64_t do_strides[3],
+              const int64_t dq_strides[3], const int64_t dk_strides[3], const int64_t dv_strides[3],
+              void* workspace, size_t workspace_bytes, int stages, void* stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, Nq, Nk, d, scale, causal, window_left, window_right,
+                  dropout_p, seed, offset, dtype, q_strides, k_strides, v_strides, o_strides, do_strides, dq_strides,
+                  dk_strides, dv_strides, workspace, workspace_bytes, stages, stream, false);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   int dtype, void* stream) {
+  int64_t sq[3], sk[3];
+  contiguous_strides(H, Nq, d, sq);
+  contiguous_strides(H, Nk, d, sk);
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, Nq, Nk, d, scale, causal, -1, -1, 0.0f, 0, 0, dtype,
+                  sq, sk, sk, sq, sq, sq, sk, sk, nullptr, 0, FA_BWD_ALL, stream, true);
 }
 
 int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -823,6 +823,18 @@ hipError_t launch_dc(const BwdParams& p, bool banded, int stages, bool side_ok, 
                 : launch_t<D, DT, false, false>(p, stages, side_ok, stream);
 }
 
+// ------------------------------------------------------------ scratch
+// The workspace of the allocation-free backward: a file-scope device array,
+// one copy per GPU, kept until the process ends.  Host code never uses its
+// name as an address (on the host it is only a stand-in for the symbol):
+// the device address comes from hipGetSymbolAddress, once per device, with
+// that device current.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+static_assert(kNoAllocScratchBytes % 256 == 0, "scratch size");
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxSideDevices];
+
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int Nq) {
@@ -863,6 +875,24 @@ hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int sta
                            : launch_dc<64, DT_BF16>(p, banded, stages, side_ok, stream);
   return dtype == DT_F16 ? launch_dc<128, DT_F16>(p, banded, stages, side_ok, stream)
                          : launch_dc<128, DT_BF16>(p, banded, stages, side_ok, stream);
+}
+
+hipError_t bwd_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxSideDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

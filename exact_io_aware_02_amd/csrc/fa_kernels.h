@@ -91,5 +91,10 @@ size_t bwd_split_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d);
 // side_ok = false keeps every stage on `stream` (no side stream for dQ).
 hipError_t launch_bwd(const BwdParams& p, int d, int dtype, bool banded, int stages, hipStream_t stream,
                       bool side_ok = true);
+// Bytes of the file-scope scratch array that serves as the workspace of
+// the allocation-free backward, and its address on the current device
+// (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;  // FA_BWD_NOALLOC_SCRATCH_BYTES of fa.h
+hipError_t bwd_scratch(void** ptr);
 
 }  // namespace fa

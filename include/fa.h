@@ -245,14 +245,34 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
  * problem already fills the chip). */
 size_t fa_bwd_ex_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d, int dtype);
 
+/* fa_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results as fa_bwd on contiguous BHSD
+ * tensors, with the workspace taken from a device array of
+ * FA_BWD_NOALLOC_SCRATCH_BYTES that the library holds at file scope (one
+ * per GPU, kept until the process ends; its address is looked up once per
+ * device, on the first call made with that device current).  It calls no
+ * allocating routine.
+ *   Sizes whose workspace (fa_bwd_workspace_bytes) exceeds the array, i.e.
+ *   B * H * round_up(Nq, 64) > FA_BWD_NOALLOC_SCRATCH_BYTES / 8, are
+ *   rejected with FA_ERR_INVALID_ARG.  All stages run on `stream` (no side
+ *   stream).  Every call on one GPU shares that GPU's array: calls that
+ *   can overlap on one GPU (other streams, other threads, graphs replayed
+ *   concurrently) race and must be ordered by the caller.  Nothing in the
+ *   array needs to start at zero: each call writes every value it reads. */
+#define FA_BWD_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream);
+
 /* Static name of a status code ("FA_OK", ...); "FA_UNKNOWN_STATUS" otherwise. */
 const char* fa_status_string(int status);
 
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* fa_last_error_message(void);
 
-/* Library ABI version, currently 4 (3 added fa_fwd_fp8, 4
- * fa_bwd_ex_workspace_bytes). */
+/* Library ABI version, currently 5 (3 added fa_fwd_fp8, 4
+ * fa_bwd_ex_workspace_bytes, 5 fa_bwd_noalloc). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

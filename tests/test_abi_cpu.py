@@ -46,7 +46,7 @@ def test_exported_dynamic_symbols_are_c_names():
 
 
 def test_status_strings_and_version():
-    assert fa.fa_abi_version() == 4
+    assert fa.fa_abi_version() == 5
     assert fa.fa_status_string(0) == "FA_OK"
     assert fa.fa_status_string(1) == "FA_ERR_INVALID_ARG"
     assert fa.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
