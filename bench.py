@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """One-GPU benchmark of the attention hot path (forward + recompute backward).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows-f]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows-f] [--no-oracle]
 
 A step is one forward (fa_fwd) and one backward (fa_bwd: D = rowsum(dO*O),
 dK/dV, dQ) over the long-context workload: B=1, H=16, N=16384, d=128, bf16,
@@ -28,9 +28,14 @@ head sharding); plus the fp8 forward alone on the inputs cast to float8_e4m3fn
 cpu_baseline: the fp64 numpy oracle (test infrastructure) on four heads of the
 same workload, forward + backward, timed on the host cores.
 
-small_configs: the four smaller workloads (forward; forward and backward
-for the training-step one), timed per launch from a replayed HIP graph and
-from a Python loop.
+configs: the per-configuration report.  The four smaller workloads
+(forward; forward and backward for the training-step one), timed per launch
+from a replayed HIP graph and from a Python loop, at the clock sampled while
+each runs back to back, with parity against the oracle on the same seeded
+inputs, the oracle's host time, and MFMA busy / HBM GB/s from the committed
+counter summary; the 16K workload's entry (parity on 256 sampled rows per
+head and on the cpu_baseline heads); and a chip-filling non-causal row (the
+16K inputs without the mask).
 
 power_context: under load the chip runs at its power cap and lowers its
 clock; the forward is run back to back for a few seconds while amd-smi reads
@@ -152,17 +157,77 @@ def power_context(torch, fa, q, k, v, o, lse, s, causal, stream, fwd_flop, peak)
     return out
 
 
-def small_configs(fa, torch, stream, peak_of):
-    """The four smaller workloads (the 16K one is the step above).  They
-    run in microseconds, less than the Python binding takes to launch them,
-    so each is timed two ways: 20 launches captured in a HIP graph and
-    replayed 10 times (GPU time per launch, no host gaps), and 100 launches
-    from Python back to back (what an eager caller sees).  With at most 512
-    workgroups they are occupancy- and latency-bound; their fraction of
-    peak is context, not a target."""
-    from attn_inputs import WORKLOADS, make_qkv
+TOL_O = {"fp16": 2e-3, "bf16": 1.6e-2}
+TOL_LSE = 1e-3
+TOL_GRAD = 2e-2
+CONFIG_COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_configs.json")
 
-    def graph_ms(fn):
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+    except Exception:
+        return None
+
+
+def config_counters(key):
+    """MFMA busy share and HBM bytes of one workload's kernels, from the
+    committed rocprofv3 counter summary, only if it was taken on the current
+    kernel sources (else None)."""
+    try:
+        with open(CONFIG_COUNTERS_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("configs", {}).get(key)
+
+
+def parity_fwd(o, lse, ro, rl, dtype, layout):
+    import numpy as np
+
+    from attn_inputs import to_bhsd64
+
+    eo = float(np.abs(to_bhsd64(o.cpu(), layout) - ro).max())
+    el = float(np.abs(lse.cpu().double().numpy() - rl).max())
+    return {"o_maxabs": eo, "lse_maxabs": el, "tol_o": TOL_O[dtype], "tol_lse": TOL_LSE,
+            "pass": bool(eo <= TOL_O[dtype] and el <= TOL_LSE)}
+
+
+def parity_bwd(grads, refs, layout):
+    import numpy as np
+
+    from attn_inputs import to_bhsd64
+
+    out = {}
+    for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
+        out[name + "_relF"] = float(np.linalg.norm(to_bhsd64(g.cpu(), layout) - r) / np.linalg.norm(r))
+    out["tol_relF"] = TOL_GRAD
+    out["pass"] = bool(max(out[n + "_relF"] for n in ("dq", "dk", "dv")) <= TOL_GRAD)
+    return out
+
+
+def config_report(fa, torch, stream, peak_of, with_oracle=True, sustain_s=2.0):
+    """The four smaller workloads (the 16K one is the step above), one entry
+    per configuration and pass.  They run in microseconds, less than the
+    Python binding takes to launch them, so each is timed two ways: 20
+    launches captured in a HIP graph and replayed 10 times (GPU time per
+    launch, no host gaps), and 100 launches from Python back to back (what
+    an eager caller sees).  The graph is then replayed back to back for
+    ``sustain_s`` seconds while amd-smi reads the GFX clock, which gives the
+    fraction of the MFMA peak at the clock the part actually ran.  Parity:
+    the same seeded inputs through the fp64 oracle (test infrastructure,
+    timed on the host cores) against the GPU outputs, with the parity
+    tests' tolerances.  MFMA busy and HBM GB/s come from the committed
+    counter summary of these launches when it matches the kernel sources.
+    With at most 512 workgroups they are occupancy- and latency-bound;
+    their fraction of peak is context, not a target."""
+    from attn_inputs import WORKLOADS, make_qkv, to_bhsd64
+
+    def graph_of(fn):
         side = torch.cuda.Stream(device=stream.device)
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -177,6 +242,9 @@ def small_configs(fa, torch, stream, peak_of):
                 fn(cap)
         g.replay()
         torch.cuda.synchronize()
+        return g
+
+    def graph_ms(g):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(10):
@@ -197,7 +265,27 @@ def small_configs(fa, torch, stream, peak_of):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 100
 
+    def timed(fn, flop, peak, key):
+        g = graph_of(fn)
+        gm, em = graph_ms(g), eager_ms(fn)
+        r = {"graph_ms": gm, "eager_loop_ms": em, "tflops": flop / gm / 1e9, "frac_of_peak": flop / gm / 1e9 / peak,
+             "flop": flop}
+        if sustain_s > 0:
+            ms, mhz, w = sustained(torch, lambda: g.replay(), sustain_s, stream)
+            r["sustained_ms"] = ms / 20
+            r["sclk_mhz"], r["socket_power_w"] = mhz, w
+            if mhz:
+                r["frac_of_peak_at_sclk"] = flop / (ms / 20) / 1e9 / (peak * mhz / 2400.0)
+        c = config_counters(key)
+        if c is not None:
+            r["mfma_busy"] = c.get("mfma_busy")
+            if c.get("hbm_bytes") is not None:
+                r["hbm_bytes"] = c["hbm_bytes"]
+                r["hbm_gbs"] = c["hbm_bytes"] / (gm * 1e-3) / 1e9
+        return r
+
     out = {}
+    cores = blas_threads()
     for name, w in WORKLOADS.items():
         if w.N >= 16384:
             continue
@@ -210,24 +298,93 @@ def small_configs(fa, torch, stream, peak_of):
         peak = peak_of(w.dtype)
         for causal in w.causal:
             flop = 4.0 * w.B * w.H * w.N * w.N * w.d / (2 if causal else 1)
-            fwd = lambda st: fa.fa_fwd_ex(q, k, v, o, lse, s, causal, (-1, -1), w.layout, st)
-            gm, em = graph_ms(fwd), eager_ms(fwd)
+            # the key-split forward with its workspace (plain fa_fwd_ex kernels where it needs none)
+            nws = fa.fa_fwd_splitk_workspace_bytes(w.B, w.H, w.N, w.N, w.d, causal)
+            fws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+            fwd = lambda st: fa.fa_fwd_splitk(q, k, v, o, lse, s, causal, fws, (-1, -1), w.layout, st)
             key = "%s%s fwd" % (name, "" if len(w.causal) == 1 else (" causal" if causal else " noncausal"))
-            out[key] = {"graph_ms": gm, "eager_loop_ms": em, "tflops": flop / gm / 1e9,
-                        "frac_of_peak": flop / gm / 1e9 / peak}
+            out[key] = timed(fwd, flop, peak, key)
+            out[key]["workload"] = "B%d H%d N%d d%d %s %s %s" % (w.B, w.H, w.N, w.d, w.dtype, w.layout.upper(),
+                                                                  "causal" if causal else "non-causal")
             if w.backward:
                 do = inp["do"].to(q.device)
                 dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
                 ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.N, w.d, fa.FA_FP16 if w.dtype == "fp16"
                                                            else fa.FA_BF16), dtype=torch.uint8, device=q.device)
                 bwd = lambda st: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, st)
-                gm, em = graph_ms(bwd), eager_ms(bwd)
-                out[name + " bwd"] = {"graph_ms": gm, "eager_loop_ms": em, "tflops": 2.5 * flop / gm / 1e9,
-                                      "frac_of_peak": 2.5 * flop / gm / 1e9 / peak}
+                out[name + " bwd"] = timed(bwd, 2.5 * flop, peak, name + " bwd")
+                out[name + " bwd"]["workload"] = out[key]["workload"] + " backward"
+            if with_oracle:
+                from oracle import attention_bwd64, attention_fwd64
+
+                fwd(stream)
+                args = [to_bhsd64(inp[x], w.layout) for x in ("q", "k", "v")]
+                t0 = time.perf_counter()
+                ro, rl = attention_fwd64(*args, s, causal)
+                t_o = time.perf_counter() - t0
+                out[key]["parity"] = parity_fwd(o, lse, ro, rl, w.dtype, w.layout)
+                out[key]["oracle"] = {"seconds": t_o, "gflops": flop / t_o / 1e9, "cores": cores}
+                if w.backward:
+                    bwd(stream)
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    refs = attention_bwd64(*args, to_bhsd64(inp["do"], w.layout), s, causal)
+                    t_b = time.perf_counter() - t0
+                    out[name + " bwd"]["parity"] = parity_bwd((dq, dk, dv), refs, w.layout)
+                    out[name + " bwd"]["oracle"] = {"seconds": t_b, "gflops": 2.5 * flop / t_b / 1e9, "cores": cores}
     for kk, r in out.items():
-        log("  %-52s graph %.4f ms, eager loop %.4f ms, %.1f TFLOP/s (%.1f%% of peak)" % (
-            kk, r["graph_ms"], r["eager_loop_ms"], r["tflops"], 100 * r["frac_of_peak"]))
+        par = r.get("parity", {}).get("pass")
+        log("  %-52s graph %.4f ms, eager %.4f ms, %.1f TFLOP/s (%.1f%% of peak%s), parity %s" % (
+            kk, r["graph_ms"], r["eager_loop_ms"], r["tflops"], 100 * r["frac_of_peak"],
+            ", %.1f%% at %.0f MHz" % (100 * r["frac_of_peak_at_sclk"], r["sclk_mhz"]) if r.get("sclk_mhz") else "",
+            "pass" if par else ("FAIL" if par is not None else "n/a")))
     return out
+
+
+def profile_configs(fa, torch, stream):
+    """Launch each configuration's kernels a few times, eagerly and in a
+    fixed order (the 16K step is left out), for a counter profile of this
+    command: the report's MFMA busy and HBM figures come from such a run."""
+    from attn_inputs import WORKLOADS, make_qkv
+
+    order = []
+    for name, w in WORKLOADS.items():
+        if w.N >= 16384:
+            continue
+        inp = make_qkv(w.B, w.H, w.N, w.N, w.d, w.dtype, w.layout, seed=w.seed, in_scale=w.in_scale,
+                       with_do=w.backward)
+        q, k, v = (inp[x].to(stream.device) for x in ("q", "k", "v"))
+        s = 1.0 / math.sqrt(w.d)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+        for causal in w.causal:
+            key = "%s%s fwd" % (name, "" if len(w.causal) == 1 else (" causal" if causal else " noncausal"))
+            nws = fa.fa_fwd_splitk_workspace_bytes(w.B, w.H, w.N, w.N, w.d, causal)
+            fws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+            for _ in range(5):
+                fa.fa_fwd_splitk(q, k, v, o, lse, s, causal, fws, (-1, -1), w.layout, stream)
+            torch.cuda.synchronize()
+            order.append(key)
+            if w.backward:
+                do = inp["do"].to(q.device)
+                dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+                ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.N, w.d, fa.FA_FP16), dtype=torch.uint8,
+                                 device=q.device)
+                for _ in range(5):
+                    fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, stream)
+                torch.cuda.synchronize()
+                order.append(name + " bwd")
+    # the fp8 forward of the 16K workload (its inputs cast to e4m3fn)
+    w = WORKLOADS[WORKLOAD]
+    inp = make_qkv(w.B, w.H, w.N, w.N, w.d, w.dtype, w.layout, seed=w.seed, in_scale=w.in_scale)
+    q8, k8, v8 = (inp[x].to(stream.device).to(torch.float8_e4m3fn) for x in ("q", "k", "v"))
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q8.device)
+    for _ in range(5):
+        fa.fa_fwd_fp8(q8, k8, v8, o, lse, 1.0 / math.sqrt(w.d), True, (-1, -1), (1.0, 1.0, 1.0), "bhsd", stream)
+    torch.cuda.synchronize()
+    order.append("fp8_fwd")
+    return order
 
 
 def measured_traffic(kernel):
@@ -290,6 +447,85 @@ def cpu_baseline(inp, s, causal, gpu_out):
     }
 
 
+C4_SAMPLE_ROWS = 256
+
+
+def c4_sampled_parity(inp, o, lse, s, w):
+    """The 16K forward on C4_SAMPLE_ROWS seeded query rows of every head
+    (rows 0 and N-1 always) against the oracle, as the parity tests check it."""
+    import numpy as np
+
+    from attn_inputs import sample_rows, to_bhsd64
+    from oracle import attention_rows_fwd64
+
+    rows = sample_rows(w.B, w.H, w.N, C4_SAMPLE_ROWS, w.seed + 1000)
+    q, k, v = (to_bhsd64(inp[x]) for x in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    ro, rl = attention_rows_fwd64(q, k, v, s, True, rows)
+    dt = time.perf_counter() - t0
+    og, lg = to_bhsd64(o.cpu()), lse.cpu().double().numpy()
+    go = np.stack([np.stack([og[b, h][rows[b, h]] for h in range(w.H)]) for b in range(w.B)])
+    gl = np.stack([np.stack([lg[b, h][rows[b, h]] for h in range(w.H)]) for b in range(w.B)])
+    eo, el = float(np.abs(go - ro).max()), float(np.abs(gl - rl).max())
+    flop = 4.0 * w.d * float(sum(int(r) + 1 for r in rows.ravel()))
+    return {"rows_per_head": int(rows.shape[2]), "o_maxabs": eo, "lse_maxabs": el, "tol_o": TOL_O[w.dtype],
+            "tol_lse": TOL_LSE, "pass": bool(eo <= TOL_O[w.dtype] and el <= TOL_LSE),
+            "oracle": {"seconds": dt, "gflops": flop / dt / 1e9, "cores": blas_threads()}}
+
+
+def noncausal_row(fa, torch, q, k, v, do, s, stream, peak, steps, with_oracle=True):
+    """A chip-filling non-causal row: the 16K inputs without the causal
+    mask (2048 forward workgroups), forward and backward, timed with HIP
+    events; forward parity on 64 seeded rows per head."""
+    import numpy as np
+
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_BF16), dtype=torch.uint8, device=q.device)
+    for _ in range(2):
+        fa.fa_fwd(q, k, v, o, lse, s, False, stream)
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, False, ws, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tf = tb = 0.0
+    for _ in range(steps):
+        ev[0].record(stream)
+        fa.fa_fwd(q, k, v, o, lse, s, False, stream)
+        ev[1].record(stream)
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, False, ws, stream)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        tf += ev[0].elapsed_time(ev[1])
+        tb += ev[1].elapsed_time(ev[2])
+    tf, tb = tf / steps, tb / steps
+    ff = 4.0 * B * H * N * N * d
+    key = "fwd_b1h16_n16384_d128_bf16_bhsd noncausal"
+    r = {"workload": "B1 H16 N16384 d128 bf16 BHSD non-causal (the 16K inputs)", "fwd_ms": tf,
+         "fwd_tflops": ff / tf / 1e9, "fwd_frac_of_peak": ff / tf / 1e9 / peak, "bwd_ms": tb,
+         "bwd_tflops": 2.5 * ff / tb / 1e9, "bwd_frac_of_peak": 2.5 * ff / tb / 1e9 / peak}
+    log("  %-52s fwd %.3f ms (%.1f TFLOP/s, %.1f%%), bwd %.3f ms (%.1f TFLOP/s)" % (
+        key, tf, ff / tf / 1e9, 100 * ff / tf / 1e9 / peak, tb, 2.5 * ff / tb / 1e9))
+    if with_oracle:
+        from attn_inputs import sample_rows, to_bhsd64
+        from oracle import attention_rows_fwd64
+
+        rows = sample_rows(B, H, N, 64, 7)
+        qc, kc, vc = (to_bhsd64(x.cpu()) for x in (q, k, v))
+        t0 = time.perf_counter()
+        ro, rl = attention_rows_fwd64(qc, kc, vc, s, False, rows)
+        dt = time.perf_counter() - t0
+        og, lg = to_bhsd64(o.cpu()), lse.cpu().double().numpy()
+        go = np.stack([np.stack([og[b, h][rows[b, h]] for h in range(H)]) for b in range(B)])
+        gl = np.stack([np.stack([lg[b, h][rows[b, h]] for h in range(H)]) for b in range(B)])
+        eo, el = float(np.abs(go - ro).max()), float(np.abs(gl - rl).max())
+        r["parity_fwd_sampled_rows"] = {"rows_per_head": 64, "o_maxabs": eo, "lse_maxabs": el,
+                                        "pass": bool(eo <= TOL_O["bf16"] and el <= TOL_LSE),
+                                        "oracle": {"seconds": dt, "gflops": 4.0 * d * N * rows.size / dt / 1e9,
+                                                   "cores": blas_threads()}}
+    return {key + "+bwd": r}
+
+
 GQA_KV_HEADS = 2          # 16 query heads on 2 K/V heads (G = 8)
 WINDOW = (256, 256)       # the skill guide's sliding-window example, with causal
 DROPOUT = (0.1, 2024, 0)  # the skill guide's dropout_p = 0.1 (seed, offset arbitrary)
@@ -332,8 +568,12 @@ def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
         ws = torch.empty(fa.fa_bwd_ex_workspace_bytes(B, Hc, c["k"].shape[1], N, N, d, fa.FA_BF16), dtype=torch.uint8,
                          device=q.device)
 
+        # the key-split forward where the grid is too small for the chip (the head-shard row)
+        nws = fa.fa_fwd_splitk_workspace_bytes(B, Hc, N, N, d, True, c["window"])
+        fws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+
         def fwd():
-            fa.fa_fwd_ex(qc, c["k"], c["v"], o, lse, s, True, c["window"], "bhsd", stream, c["dropout"])
+            fa.fa_fwd_splitk(qc, c["k"], c["v"], o, lse, s, True, fws, c["window"], "bhsd", stream, c["dropout"])
 
         def bwd():
             fa.fa_bwd_ex(qc, c["k"], c["v"], o, lse, dc, dq, dk, dv, s, True, ws, c["window"], fa.FA_BWD_ALL,
@@ -390,6 +630,20 @@ def next_rows(fa, torch, q, k, v, do, s, stream, peak, steps):
     return res
 
 
+def copy_calibration(torch, dev, mib):
+    """A plain device copy of `mib` MiB, three times: a counter profile of
+    the command reads FETCH_SIZE / WRITE_SIZE of known bytes from it."""
+    if mib <= 0:
+        return
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,8 +659,15 @@ def main():
     ap.add_argument("--no-power-context", action="store_true",
                     help="skip the clock/power readings and the GEMM comparison")
     ap.add_argument("--no-small-configs", action="store_true",
-                    help="skip timing the four smaller workloads")
+                    help="skip the report on the four smaller workloads and the non-causal row")
+    ap.add_argument("--no-oracle", action="store_true",
+                    help="skip every oracle computation (parity entries of the report, cpu_baseline)")
+    ap.add_argument("--profile-configs", action="store_true",
+                    help="only launch each smaller workload's kernels 5 times in a fixed order (for a counter "
+                         "profile of this command) and print that order")
     args = ap.parse_args()
+    if args.no_oracle:
+        args.no_cpu_baseline = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(attention heads shard with no communication; see the design notes). "
@@ -423,6 +684,11 @@ def main():
     causal = True
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile_configs:
+        copy_calibration(torch, dev, args.copy_calibration_mib)
+        order = profile_configs(fa, torch, torch.cuda.current_stream(dev))
+        print(json.dumps({"profile_configs_order": order}), flush=True)
+        return
     inp = workload_inputs(w)
     rng = np.random.default_rng(w.seed + 2000)
     inp["do"] = torch.from_numpy(rng.standard_normal(inp["q"].shape, dtype=np.float32)).to(torch.bfloat16)
@@ -439,14 +705,7 @@ def main():
         fa.fa_fwd(q, k, v, o, lse, s, causal, stream)
         fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, stream)
 
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * (1 << 20) // 2
-        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(torch, dev, args.copy_calibration_mib)
 
     for _ in range(args.warmup):
         step()
@@ -543,16 +802,36 @@ def main():
             pc["fwd"]["tflops"], pc["fwd"]["sclk_mhz"], pc["fwd"]["socket_power_w"], pc["gemm_bf16"]["tflops"],
             pc["gemm_bf16"]["sclk_mhz"], pc["gemm_bf16"]["socket_power_w"]))
     if not args.no_small_configs:
-        log("smaller workloads:")
-        out["small_configs"] = small_configs(fa, torch, stream, lambda dt: PEAK_TFLOPS[dt])
+        log("configurations:")
+        out["configs"] = config_report(fa, torch, stream, lambda dt: PEAK_TFLOPS[dt], with_oracle=not args.no_oracle)
+        nc = noncausal_row(fa, torch, q, k, v, do, s, stream, peak, min(K, 10), with_oracle=not args.no_oracle)
+        out["configs"].update(nc)
     if not args.no_rows_f:
         out["rows_f"] = next_rows(fa, torch, q, k, v, do, s, stream, peak, min(K, 10))
+    # the 16K workload's entry of the per-configuration report
+    c4 = {"workload": "B1 H16 N16384 d128 bf16 BHSD causal, inputs x0.5",
+          "fwd_ms": fwd_ms, "fwd_tflops": fwd_flop / fwd_ms / 1e9, "fwd_frac_of_peak": fwd_flop / fwd_ms / 1e9 / peak,
+          "bwd_ms": bwd_ms, "bwd_tflops": bwd_flop / bwd_ms / 1e9, "bwd_frac_of_peak": bwd_flop / bwd_ms / 1e9 / peak}
+    pc = out.get("power_context")
+    if pc and pc["fwd"].get("sclk_mhz"):
+        c4["fwd_sclk_mhz"] = pc["fwd"]["sclk_mhz"]
+        c4["fwd_frac_of_peak_at_sclk"] = pc["fwd_frac_of_peak_at_sclk"]
+    cnt = config_counters(WORKLOAD)
+    if cnt is not None:
+        c4["counters"] = cnt
+    if not args.no_oracle:
+        c4["parity_fwd_sampled_rows"] = c4_sampled_parity(inp, o, lse, s, w)
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         gpu_out = (o.cpu(), lse.cpu(), dq.cpu(), dk.cpu(), dv.cpu())
         out["cpu_baseline"] = cpu_baseline(inp, s, causal, gpu_out)
+        ph = out["cpu_baseline"]["parity_sampled_heads"]
+        c4["parity_heads_0_3"] = dict(ph, **{"pass": bool(
+            ph["o_maxabs"] <= TOL_O[w.dtype] and ph["lse_maxabs"] <= TOL_LSE
+            and max(ph["dq_relF"], ph["dk_relF"], ph["dv_relF"]) <= TOL_GRAD)})
         log("cpu_baseline: %.4f TFLOP/s over %.1f s; sampled-head parity %s" % (
             out["cpu_baseline"]["value"], out["cpu_baseline"]["seconds"], out["cpu_baseline"]["parity_sampled_heads"]))
+    out.setdefault("configs", {})[WORKLOAD + " fwd+bwd"] = c4
     print(json.dumps(out), flush=True)
 
 

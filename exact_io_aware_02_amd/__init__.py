@@ -2,8 +2,8 @@
 
 Thin ctypes marshalling over the C ABI in ``include/fa.h``.  The functions
 named like the C entry points (``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_ex``,
-``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_strided``, ``fa_bwd_stages``, ``fa_bwd_ex``,
-``fa_bwd_workspace_bytes``, ``fa_status_string``, ``fa_last_error_message``)
+``fa_fwd_splitk``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_strided``, ``fa_bwd_stages``, ``fa_bwd_ex``,
+``fa_bwd_noalloc``, the workspace-size queries, ``fa_status_string``, ``fa_last_error_message``)
 take torch tensors, read their sizes and strides,
 and call the library on the tensors' device and current stream.  Every step
 of the computation runs in the library's HIP kernels; there is no other
@@ -24,6 +24,7 @@ __all__ = [
     "FA_FP16", "FA_BF16", "FaError", "lib_path", "load_library",
     "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_fwd_fp8", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
     "fa_bwd_ex", "fa_bwd_workspace_bytes", "fa_bwd_ex_workspace_bytes", "fa_bwd_noalloc",
+    "fa_fwd_splitk", "fa_fwd_splitk_workspace_bytes",
     "FA_BWD_NOALLOC_SCRATCH_BYTES",
     "FA_BWD_PREP", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
     "fa_status_string", "fa_last_error_message", "fa_abi_version",
@@ -36,8 +37,8 @@ FA_BWD_PREP, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED_SYMBOLS = (
     "fa_fwd", "fa_fwd_strided", "fa_fwd_ex", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_strided", "fa_bwd_stages",
-    "fa_bwd_ex", "fa_fwd_fp8", "fa_bwd_ex_workspace_bytes", "fa_bwd_noalloc", "fa_status_string",
-    "fa_last_error_message", "fa_abi_version",
+    "fa_bwd_ex", "fa_fwd_fp8", "fa_bwd_ex_workspace_bytes", "fa_bwd_noalloc", "fa_fwd_splitk",
+    "fa_fwd_splitk_workspace_bytes", "fa_status_string", "fa_last_error_message", "fa_abi_version",
 )
 FA_BWD_NOALLOC_SCRATCH_BYTES = 8 << 20
 
@@ -101,6 +102,11 @@ def load_library():
     lib.fa_fwd_fp8.restype = _i
     lib.fa_bwd_noalloc.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp]
     lib.fa_bwd_noalloc.restype = _i
+    lib.fa_fwd_splitk.argtypes = ([_vp] * 5 + [_i] * 6 + [_f, _i, _i, _i, _f, _u64, _u32, _i] + [_I64x3] * 4 +
+                                  [_vp, _sz, _vp])
+    lib.fa_fwd_splitk.restype = _i
+    lib.fa_fwd_splitk_workspace_bytes.argtypes = [_i] * 8
+    lib.fa_fwd_splitk_workspace_bytes.restype = _sz
     lib.fa_status_string.argtypes = [_i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error_message.argtypes = []
@@ -373,6 +379,32 @@ def fa_fwd_ex(q, k, v, o, lse, scale, causal, window=(-1, -1), layout="bhsd", st
             _strides(o, layout), _stream(q, stream)))
 
 
+def fa_fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, causal, window=(-1, -1)):
+    """C ``fa_fwd_splitk_workspace_bytes`` (0: the sizes need no workspace)."""
+    wl, wr = _window(window)
+    return int(load_library().fa_fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, int(bool(causal)), wl, wr))
+
+
+def fa_fwd_splitk(q, k, v, o, lse, scale, causal, workspace, window=(-1, -1), layout="bhsd", stream=None,
+                  dropout=None):
+    """C ``fa_fwd_splitk``: ``fa_fwd_ex`` with the keys of heavy query blocks
+    split over workgroups; ``workspace`` is a device tensor of at least
+    ``fa_fwd_splitk_workspace_bytes`` bytes, or None when that is 0."""
+    dt = _dtype_code(q)
+    B, H, Hkv, Nq, Nk, d = _check_fwd(q, k, v, o, lse, layout, same_heads=False, device=False)
+    if workspace is not None and not workspace.is_contiguous():
+        _bad("workspace must be contiguous")
+    _want_device(q, k=k, v=v, o=o, lse=lse, **({} if workspace is None else {"workspace": workspace}))
+    wl, wr = _window(window)
+    dp, seed, off = _dropout(dropout)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        _check(load_library().fa_fwd_splitk(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+            wl, wr, dp, seed, off, dt, _strides(q, layout), _strides(k, layout), _strides(v, layout),
+            _strides(o, layout), _ptr(workspace), nbytes, _stream(q, stream)))
+
+
 def fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, causal, workspace, window=(-1, -1), stages=FA_BWD_ALL,
               layout="bhsd", stream=None, dropout=None):
     """C ``fa_bwd_ex``: the backward of ``fa_fwd_ex`` (dk, dv shaped like k,
@@ -429,14 +461,18 @@ def attention_fwd_fp8(q, k, v, causal=False, scale=None, layout="bhsd", stream=N
     return o, lse
 
 
-def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None, window=None, dropout=None):
+def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None, window=None, dropout=None,
+                  splitk=True):
     """O = softmax(scale Q K^T) V (top-left causal mask if ``causal``).
 
     Allocates o (like q) and lse (fp32 [B,H,Nq]); returns (o, lse).  ``scale``
     defaults to 1/sqrt(d).  k and v may carry fewer heads than q (dividing
     them); ``window`` = (left, right) restricts query i to keys
     i - left .. i + right (negative: unbounded); ``dropout`` = (p, seed,
-    offset) drops attention weights (see ``include/fa.h``).
+    offset) drops attention weights (see ``include/fa.h``).  ``splitk``:
+    for grids too small to fill the chip, allocate the workspace of
+    ``fa_fwd_splitk`` and split heavy query blocks' keys over workgroups
+    (False: the C ``fa_fwd`` family, without a workspace).
     """
     _dtype_code(q)
     _on_device(q, k, v)
@@ -444,6 +480,13 @@ def attention_fwd(q, k, v, causal=False, scale=None, layout="bhsd", stream=None,
     s = _default_scale(d, scale)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if splitk:
+        Nk = _dims(k, layout)[2]
+        nbytes = fa_fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, causal, _window(window))
+        if nbytes > 0:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+            fa_fwd_splitk(q, k, v, o, lse, s, causal, ws, _window(window), layout, stream, dropout)
+            return o, lse
     if _dims(k, layout)[1] != H or window is not None or dropout is not None:
         fa_fwd_ex(q, k, v, o, lse, s, causal, window, layout, stream, dropout)
     elif layout == "bhsd" and q.is_contiguous() and k.is_contiguous() and v.is_contiguous():

@@ -165,7 +165,7 @@ void contiguous_strides(int H, int N, int d, int64_t st[3]) {
 
 extern "C" {
 
-int fa_abi_version(void) { return 5; }
+int fa_abi_version(void) { return 6; }
 
 const char* fa_status_string(int status) {
   switch (status) {
@@ -180,11 +180,17 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error_message(void) { return g_msg; }
 
-int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int Nq,
-              int Nk, int d, float scale, int causal, int window_left, int window_right, float dropout_p,
-              uint64_t seed, uint32_t offset, int dtype,
-              const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
-              const int64_t o_strides[3], void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward behind fa_fwd_ex and fa_fwd_splitk.  `splitk`: the key-chunked
+// launch with the caller's workspace when the sizes have a chunk plan.
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int Nq,
+             int Nk, int d, float scale, int causal, int window_left, int window_right, float dropout_p,
+             uint64_t seed, uint32_t offset, int dtype,
+             const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+             const int64_t o_strides[3], void* workspace, size_t workspace_bytes, bool splitk, void* stream) {
   g_msg[0] = '\0';
   int st = check_common(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st) return st;
@@ -205,6 +211,23 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
     return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
   if (overlaps(lse, el, q, eq) || overlaps(lse, el, k, ek) || overlaps(lse, el, v, ev) || overlaps(lse, el, o, eo))
     return fail(FA_ERR_INVALID_ARG, "lse overlaps another tensor");
+  const Band band = make_band(causal, window_left, window_right, Nq, Nk);
+  fa::FwdSplitPlan plan{0, 0, 0, 0};
+  if (splitk) {
+    plan = fa::fwd_split_plan(B, H, Nq, Nk, d, band.wl, band.wr);
+    const size_t need = fa::fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, band.wl, band.wr);
+    if (need > 0) {
+      if (!workspace) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
+      if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(FA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+      if (workspace_bytes < need)
+        return fail(FA_ERR_INVALID_ARG, "workspace_bytes = %zu < required %zu", workspace_bytes, need);
+      const Extent ew{0, (int64_t)need};
+      if (overlaps(workspace, ew, q, eq) || overlaps(workspace, ew, k, ek) || overlaps(workspace, ew, v, ev) ||
+          overlaps(workspace, ew, o, eo) || overlaps(workspace, ew, lse, el))
+        return fail(FA_ERR_INVALID_ARG, "workspace overlaps a tensor");
+    }
+  }
   if ((st = check_device())) return st;
 
   fa::FwdParams p;
@@ -222,15 +245,48 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.Nq = Nq;
   p.Nk = Nk;
   p.G = H / H_kv;
-  const Band band = make_band(causal, window_left, window_right, Nq, Nk);
   p.wl = band.wl;
   p.wr = band.wr;
   p.drop = drop;
   p.c = softmax_c(scale);
   p.qflip = std::signbit(scale) ? 0x80008000u : 0u;
-  hipError_t e = fa::launch_fwd(p, d, dtype, band.present(), static_cast<hipStream_t>(stream));
+  p.chunk = plan.chunk;
+  p.P = plan.P;
+  p.part = static_cast<float*>(workspace);
+  hipError_t e = plan.chunk > 0
+                     ? fa::launch_fwd_splitk(p, plan, d, dtype, band.present(), static_cast<hipStream_t>(stream))
+                     : fa::launch_fwd(p, d, dtype, band.present(), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int Nq,
+              int Nk, int d, float scale, int causal, int window_left, int window_right, float dropout_p,
+              uint64_t seed, uint32_t offset, int dtype,
+              const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+              const int64_t o_strides[3], void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, window_left, window_right, dropout_p, seed,
+                  offset, dtype, q_strides, k_strides, v_strides, o_strides, nullptr, 0, false, stream);
+}
+
+size_t fa_fwd_splitk_workspace_bytes(int B, int H, int Nq, int Nk, int d, int causal, int window_left,
+                                     int window_right) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || (d != 64 && d != 128) || (causal != 0 && causal != 1)) return 0;
+  const Band band = make_band(causal, window_left, window_right, Nq, Nk);
+  return fa::fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, band.wl, band.wr);
+}
+
+int fa_fwd_splitk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int Nq,
+                  int Nk, int d, float scale, int causal, int window_left, int window_right, float dropout_p,
+                  uint64_t seed, uint32_t offset, int dtype,
+                  const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+                  const int64_t o_strides[3], void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, window_left, window_right, dropout_p, seed,
+                  offset, dtype, q_strides, k_strides, v_strides, o_strides, workspace, workspace_bytes, true, stream);
 }
 
 int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,

@@ -48,6 +48,10 @@
 // pipeline of the glossary article's "FlashAttention の仕組み" figure
 // (steps 1-4) and its "Online Softmax" section, with tile sizes and data
 // movement chosen for CDNA4 (64-wide waves, 160 KB LDS, 32x32x16 MFMA).
+#include <algorithm>
+#include <atomic>
+#include <vector>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -488,9 +492,102 @@ __device__ __forceinline__ void fwd_step_phased(int j, int n_kt, f32x16 (&s)[kNQ
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int DT, bool BAND, bool DROP, bool PHASED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdCfg<D, PHASED>::WAVES_PER_SIMD,
-                                                                          FwdCfg<D, PHASED>::WAVES_PER_SIMD))) void fwd_kernel(FwdParams p) {
+// Key tiles [lo, hi) of query block qb (kBM queries): those some query of
+// the block admits (all of them without a band).
+__host__ __device__ __forceinline__ void block_tiles(int qb, int Nq, int Nk, int wl, int wr, bool band, int& lo,
+                                                     int& hi) {
+  const int q0 = qb * kBM;
+  int kend = Nk, j0 = 0;
+  if (band) {
+    const int qlast = min(q0 + kBM, Nq) - 1;
+    if (wr >= 0) kend = min(Nk, qlast + wr + 1);
+    if (wl >= 0) j0 = max(0, q0 - wl) / kBN;
+  }
+  lo = j0;
+  hi = max(j0, (kend + kBN - 1) / kBN);
+}
+
+// Chunks of a query block of n key tiles (at least one, so that a block
+// with no admitted key still writes O = 0, LSE = -inf).
+__host__ __device__ __forceinline__ int block_chunks(int n, int chunk) { return n > 0 ? (n + chunk - 1) / chunk : 1; }
+
+// Position of item `target` in the chunk order (query blocks n_qt-1 .. 0,
+// each with block_chunks(...) chunks): with split_only, items are the
+// split blocks (two or more chunks) instead of the chunks.  Returns the
+// block (-1 if none), the item's index within it, the block's chunk count
+// and the partial slots of the split blocks before it.  Each wave scans 64
+// blocks per step, one per lane, with a prefix sum over the lanes; the
+// results are the same in every lane and every wave.
+struct ChunkPos {
+  int qb, idx, sb, base;
+};
+template <bool BAND>
+__device__ __forceinline__ ChunkPos locate_chunk(const FwdParams& p, int n_qt, int target, bool split_only) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int g = 0; g < n_qt; g += 64) {
+    const int qb = n_qt - 1 - (g + lane);
+    int sb = 0;
+    if (qb >= 0) {
+      int lo, hi;
+      block_tiles(qb, p.Nq, p.Nk, p.wl, p.wr, BAND, lo, hi);
+      sb = block_chunks(hi - lo, p.chunk);
+    }
+    const int unit = split_only ? (sb > 1 ? 1 : 0) : sb;
+    const int slots = sb > 1 ? sb : 0;
+    int pu = unit, ps = slots;  // inclusive prefix sums over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int x = __shfl_up(pu, o), y = __shfl_up(ps, o);
+      if (lane >= o) {
+        pu += x;
+        ps += y;
+      }
+    }
+    const uint64_t hit = __ballot(pu > target);
+    if (hit) {
+      const int L = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+      ChunkPos r;
+      r.qb = __builtin_amdgcn_readfirstlane(__shfl(qb, L));
+      r.sb = __builtin_amdgcn_readfirstlane(__shfl(sb, L));
+      r.idx = __builtin_amdgcn_readfirstlane(target - (__shfl(pu, L) - __shfl(unit, L)));
+      r.base = __builtin_amdgcn_readfirstlane(base + __shfl(ps, L) - __shfl(slots, L));
+      return r;
+    }
+    target -= __builtin_amdgcn_readfirstlane(__shfl(pu, 63));
+    base += __builtin_amdgcn_readfirstlane(__shfl(ps, 63));
+  }
+  return ChunkPos{-1, 0, 0, 0};
+}
+
+// Intra-workgroup key split for grids that give a CU at most one
+// workgroup (one wave per SIMD otherwise): KSPLIT = 3 groups of four waves own
+// the same 128 queries, and group g takes the g-th of KSPLIT equal runs of
+// the block's key tiles through a ring of its own.  Each group forms the
+// partial state (O^T, m, l) of its keys; the groups > 0 hand theirs to
+// group 0 through LDS, which merges them in group order by the online
+// softmax rule (m = max m_g, O^T = sum 2^(m_g - m) O^T_g, l likewise) and
+// writes O and LSE.  Every wave executes the same number of barriers:
+// groups with fewer tiles add barrier-only steps.
+template <int D>
+constexpr int kKSplit = 3;
+// The groups run the phased schedule at d = 128 (three waves per SIMD,
+// 3-slot rings): 8% faster than two groups on the interleaved one at
+// B1 H2 N16384.  At d = 64 four phased groups need <= 128 registers and
+// spill; three interleaved ones measured faster.
+template <int D>
+constexpr bool kKSplitPhased = D == 128;
+
+// Key-chunked forward (CHUNK, fa_fwd_splitk): workgroup t takes chunk
+// t / BH of head t % BH, the chunks listed from the last query block to
+// the first (the heaviest first under a causal band), each block's n key
+// tiles cut into ceil(n / p.chunk) near-equal runs.  A block of one chunk writes O and
+// LSE; the chunks of a split block write their partial state (O^T, m, l)
+// to p.part, which fwd_merge_kernel combines.
+template <int D, int DT, bool BAND, bool DROP, bool PHASED, int KSPLIT, bool CHUNK>
+__global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_eu(
+    FwdCfg<D, PHASED>::WAVES_PER_SIMD, FwdCfg<D, PHASED>::WAVES_PER_SIMD))) void fwd_kernel(FwdParams p) {
+  static_assert(!CHUNK || KSPLIT == 1, "key chunks run whole workgroups");
   constexpr int kNQB = 1;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -502,16 +599,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdCfg
   // wait for the in-flight copies into the same variable, which would
   // serialise the prefetch with the compute it is meant to hide under.
   struct Smem {
-    uint16_t k[NBUF][TILE];
-    uint16_t v[NBUF][TILE];
+    uint16_t k[KSPLIT][NBUF][TILE];
+    uint16_t v[KSPLIT][NBUF][TILE];
   };
   __shared__ __attribute__((aligned(1024))) Smem sm;
-  auto& Ks = sm.k;
-  auto& Vs = sm.v;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave_all / kWaves;          // key group (0 without a split)
+  const int wave = wave_all - grp * kWaves;   // wave within the group: its 32 queries
+  auto& Ks = sm.k[grp];
+  auto& Vs = sm.v[grp];
 
   // Heaviest query tiles first: block t covers query tile (last - t / BH),
   // head t % BH.  Consecutive blocks land on different XCDs round-robin,
@@ -519,8 +618,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdCfg
   const int BH = p.B * p.H;
   const int n_qt = (p.Nq + kBM - 1) / kBM;
   const int t = blockIdx.x;
-  const int qt = n_qt - 1 - t / BH;
   const int bh = t - (t / BH) * BH;
+  int qt = n_qt - 1 - t / BH;
+  int ck_lo = 0, ck_hi = 0, slot = -1;  // CHUNK: this chunk's key tiles and partial slot (-1: O directly)
+  if constexpr (CHUNK) {  // chunk c of sb near-equal runs of its block's tiles
+    const ChunkPos cp = locate_chunk<BAND>(p, n_qt, t / BH, false);
+    int lo, hi;
+    block_tiles(cp.qb, p.Nq, p.Nk, p.wl, p.wr, BAND, lo, hi);
+    qt = cp.qb;
+    ck_lo = lo + (int)((int64_t)cp.idx * (hi - lo) / cp.sb);
+    ck_hi = lo + (int)((int64_t)(cp.idx + 1) * (hi - lo) / cp.sb);
+    if (cp.sb > 1) slot = cp.base + cp.idx;
+  }
   const int b = bh / p.H, h = bh - b * p.H;
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kQW;
@@ -530,14 +639,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdCfg
   const uint16_t* kp = p.k + b * p.sk.b + hk * p.sk.h;
   const uint16_t* vp = p.v + b * p.sv.b + hk * p.sv.h;
 
-  // key tiles [jt0, n_kt): those some query of the block admits
+  // key tiles [jt0, n_kt): those some query of the block admits; with a
+  // split, this group's run of them
   int kend = p.Nk, jt0 = 0;
   if (BAND) {
     const int qlast = min(q0 + kBM, p.Nq) - 1;
     if (p.wr >= 0) kend = min(p.Nk, qlast + p.wr + 1);
     if (p.wl >= 0) jt0 = max(0, q0 - p.wl) / kBN;
   }
-  const int n_kt = (kend + kBN - 1) / kBN;
+  int n_kt = (kend + kBN - 1) / kBN;
+  if constexpr (CHUNK) {
+    jt0 = ck_lo;
+    n_kt = ck_hi;
+  }
+  int per = 0;  // tiles of the longest run
+  if constexpr (KSPLIT > 1) {
+    const int all = max(0, n_kt - jt0);
+    per = (all + KSPLIT - 1) / KSPLIT;
+    const int ja = min(n_kt, jt0 + grp * per);
+    n_kt = min(n_kt, ja + per);
+    jt0 = ja;
+  }
 
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(kp, p.Nk, p.sk.s, D);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vp, p.Nk, p.sv.s, D);
@@ -685,6 +807,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdCfg
         for (int nb = 0; nb < kNQB; ++nb) acc[db][nb] = mfma32<DT>(va[kk][db], pf[kk][nb], acc[db][nb]);
   }
 
+  if constexpr (KSPLIT > 1) {
+    // Barriers of a run of m tiles: one per step, plus the one after S of
+    // the first tile when S(j+1) has registers of its own.  Pad the
+    // shorter runs to the longest.
+    auto barriers = [&](int m) { return m > 0 ? m + (kSep ? 1 : 0) : 0; };
+    for (int i = barriers(max(0, n_kt - jt0)); i < barriers(per); ++i) lds_barrier();
+    // every group is done with its ring: reuse it for the hand-over
+    constexpr int NV = DB * 16 + 2;  // floats per lane: O^T, m, l
+    static_assert((size_t)(KSPLIT - 1) * kWaves * NV * 64 * 4 <= sizeof(Smem), "hand-over fits the rings");
+    float* xo = reinterpret_cast<float*>(&sm) + (size_t)((grp - 1) * kWaves + wave) * NV * 64 + lane;
+    lds_barrier();
+    if (grp > 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64] = acc[db][0][r];
+      xo[(DB * 16) * 64] = st.m[0];
+      xo[(DB * 16 + 1) * 64] = st.l[0];
+    }
+    lds_barrier();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < KSPLIT; ++g) {
+      const float* xi = reinterpret_cast<const float*>(&sm) + (size_t)((g - 1) * kWaves + wave) * NV * 64 + lane;
+      const float mg = xi[(DB * 16) * 64], lg = xi[(DB * 16 + 1) * 64];
+      const float mn = fmaxf(st.m[0], mg);
+      const float a0 = exp2_fast(st.m[0] - mn), ag = exp2_fast(mg - mn);
+      st.m[0] = mn;
+      st.l[0] = st.l[0] * a0 + lg * ag;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][0][r] = acc[db][0][r] * a0 + xi[(db * 16 + r) * 64] * ag;
+    }
+  }
+
+  if constexpr (CHUNK) {
+    if (slot >= 0) {  // a chunk of a split block: its partial state
+      float* pb = p.part + ((size_t)bh * p.P + slot) * (size_t)(kBM * (D + 2));
+      const int row = wave * kQW + col;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x16& a = acc[db][0];
+          *(f32x4*)(pb + row * D + db * 32 + 8 * g4 + 4 * half) =
+              f32x4{a[4 * g4], a[4 * g4 + 1], a[4 * g4 + 2], a[4 * g4 + 3]};
+        }
+      const float lt = sum_pair32(st.l[0]);
+      if (half == 0) {
+        pb[kBM * D + row] = st.m[0];
+        pb[kBM * D + kBM + row] = lt;
+      }
+      return;
+    }
+  }
+
   // ---- epilogue: O = O^T / l, LSE
   uint16_t* op = p.o + b * p.so.b + h * p.so.h;
 #pragma unroll
@@ -709,30 +888,219 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FwdCfg
   }
 }
 
-template <int D, int DT, bool BAND, bool DROP, bool PHASED>
+// Merge of a split query block's chunks (fa_fwd_splitk): workgroup t takes
+// rows [RPW (t % NRG), +RPW) of the ((t / NRG) / BH)-th split block of head
+// (t / NRG) % BH, in the chunk kernel's order; a thread merges one 4-wide
+// column group of one row.  Per row, in chunk order: M = max m_s,
+// L = sum 2^(m_s - M) l_s, O = sum 2^(m_s - M) O^T_s / L (times the dropout
+// scale), LSE = (M + log2 L) ln 2 (O = 0, LSE = -inf for a row that admits
+// no key).
+template <int D>
+constexpr int kMergeRows = kThreads / (D / 4);  // rows per merge workgroup
+
+template <int D, int DT, bool BAND, bool DROP>
+__global__ __launch_bounds__(kThreads) void fwd_merge_kernel(FwdParams p) {
+  constexpr int CH = D / 4;  // float4 column groups per row
+  constexpr int RPW = kMergeRows<D>;
+  constexpr int NRG = kBM / RPW;
+  const int BH = p.B * p.H;
+  const int n_qt = (p.Nq + kBM - 1) / kBM;
+  const int t = blockIdx.x;
+  const int rg = t % NRG, rest = t / NRG;
+  const int bh = rest % BH;
+  const ChunkPos cp = locate_chunk<BAND>(p, n_qt, rest / BH, true);
+  const int qt = cp.qb, ns = cp.sb, base = cp.base;
+  const int row = rg * RPW + (int)threadIdx.x / CH;
+  const int qi = qt * kBM + row;
+  if (qt < 0 || qi >= p.Nq) return;
+  const int ch = threadIdx.x % CH;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const size_t SLOT = (size_t)kBM * (D + 2);
+  const float* pb = p.part + ((size_t)bh * p.P + base) * SLOT;
+  const float* pm = pb + kBM * D + row;        // m of slot s at pm[s * SLOT]
+  const float* pl = pb + kBM * D + kBM + row;  // l likewise
+  const float* po = pb + row * D + 4 * ch;     // this thread's 4 columns
+  float M = -1e30f;
+#pragma unroll 4
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s * SLOT]);
+  float L = 0.f;
+  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = 0; s < ns; ++s) {
+    const float a = exp2_fast(pm[s * SLOT] - M);
+    L += a * pl[s * SLOT];
+    const f32x4 x = *(const f32x4*)(po + s * SLOT);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] += a * x[e];
+  }
+  const float inv = L > 0.f ? (DROP ? p.drop.scale : 1.0f) / L : 0.f;
+  uint16_t* op = p.o + b * p.so.b + h * p.so.h + qi * p.so.s + 4 * ch;
+  *(u32x2*)op = u32x2{pack2<DT>(o[0] * inv, o[1] * inv), pack2<DT>(o[2] * inv, o[3] * inv)};
+  if (ch == 0) p.lse[(int64_t)bh * p.Nq + qi] = L > 0.f ? (M + log2_fast(L)) * kLn2 : -__builtin_inff();
+}
+
+template <int D, int DT, bool BAND, bool DROP, bool PHASED, int KSPLIT>
 hipError_t launch_t(const FwdParams& p, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND, DROP, PHASED>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND, DROP, PHASED, KSPLIT, false>), dim3((unsigned)blocks),
+                     dim3(kThreads * KSPLIT), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int DT, bool PHASED>
-hipError_t launch_ds(const FwdParams& p, bool banded, int64_t blocks, hipStream_t stream) {
-  if (p.drop.thr > 0)
-    return banded ? launch_t<D, DT, true, true, PHASED>(p, blocks, stream)
-                  : launch_t<D, DT, false, true, PHASED>(p, blocks, stream);
-  return banded ? launch_t<D, DT, true, false, PHASED>(p, blocks, stream)
-                : launch_t<D, DT, false, false, PHASED>(p, blocks, stream);
+template <int D, int DT, bool BAND, bool DROP>
+hipError_t launch_chunked_t(const FwdParams& p, const FwdSplitPlan& plan, hipStream_t stream) {
+  const int64_t BH = (int64_t)p.B * p.H;
+  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND, DROP, true, 1, true>), dim3((unsigned)(plan.n_chunks * BH)),
+                     dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.n_split == 0) return e;
+  hipLaunchKernelGGL((fwd_merge_kernel<D, DT, BAND, DROP>), dim3((unsigned)(plan.n_split * BH * (kBM / kMergeRows<D>))),
+                     dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 template <int D, int DT>
-hipError_t launch_dc(const FwdParams& p, bool banded, hipStream_t stream) {
-  const int64_t blocks = (int64_t)((p.Nq + kBM - 1) / kBM) * p.B * p.H;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (blocks >= kPhasedMinBlocks<D>) return launch_ds<D, DT, true>(p, banded, blocks, stream);
-  return launch_ds<D, DT, false>(p, banded, blocks, stream);
+hipError_t launch_chunked(const FwdParams& p, const FwdSplitPlan& plan, bool banded, hipStream_t stream) {
+  if (p.drop.thr > 0)
+    return banded ? launch_chunked_t<D, DT, true, true>(p, plan, stream)
+                  : launch_chunked_t<D, DT, false, true>(p, plan, stream);
+  return banded ? launch_chunked_t<D, DT, true, false>(p, plan, stream)
+                : launch_chunked_t<D, DT, false, false>(p, plan, stream);
 }
 
+template <int D, int DT, bool PHASED, int KSPLIT>
+hipError_t launch_ds(const FwdParams& p, bool banded, int64_t blocks, hipStream_t stream) {
+  if (p.drop.thr > 0)
+    return banded ? launch_t<D, DT, true, true, PHASED, KSPLIT>(p, blocks, stream)
+                  : launch_t<D, DT, false, true, PHASED, KSPLIT>(p, blocks, stream);
+  return banded ? launch_t<D, DT, true, false, PHASED, KSPLIT>(p, blocks, stream)
+                : launch_t<D, DT, false, false, PHASED, KSPLIT>(p, blocks, stream);
+}
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cus[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// The intra-workgroup key split pays when the heaviest query block has at
+// least this many key tiles; below, the merge costs more than it saves.
+constexpr int kKSplitMinTiles = 32;
+
+template <int D, int DT>
+hipError_t launch_dc(const FwdParams& p, bool banded, hipStream_t stream) {
+  const int n_qt = (p.Nq + kBM - 1) / kBM;
+  const int64_t blocks = (int64_t)n_qt * p.B * p.H;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (blocks >= kPhasedMinBlocks<D>) return launch_ds<D, DT, true, 1>(p, banded, blocks, stream);
+  // at most one workgroup per CU: split each block's keys over more waves
+  if (blocks <= device_cus()) {
+    int most = 0;  // key tiles of the heaviest block (n_qt <= the CU count here)
+    for (int qb = 0; qb < n_qt && most < kKSplitMinTiles; ++qb) {
+      int lo, hi;
+      block_tiles(qb, p.Nq, p.Nk, p.wl, p.wr, banded, lo, hi);
+      most = max(most, hi - lo);
+    }
+    if (most >= kKSplitMinTiles) return launch_ds<D, DT, kKSplitPhased<D>, kKSplit<D>>(p, banded, blocks, stream);
+  }
+  return launch_ds<D, DT, false, 1>(p, banded, blocks, stream);
+}
+
+// Chunk plan (fa_fwd_splitk).  Grids of at most kSplitMaxBlocks query
+// blocks leave CUs idle behind the heaviest blocks of a causal band.  Each
+// block's key tiles are cut into near-equal chunks of at most `chunk`
+// tiles, with `chunk` the smallest length (but at least kMinChunkTiles)
+// whose chunks all fit the chip at once: at most 3 (d = 128) or 4
+// (d = 64) workgroups per CU, the waves per SIMD of the phased schedule
+// the chunks run; a second round of workgroups would double the time.
+// The partial results cost a merge kernel (~10 us for ~20 MB of them), so
+// the plan is kept only when its longest chunk is at least
+// kChunkMinSaving tiles shorter than the critical path without it (the
+// intra-workgroup split's run where that applies).  Planned for the
+// MI355X's 256 CUs (a fixed number, so the workspace size depends on the
+// sizes alone).
+constexpr int kChipCUs = 256;
+constexpr int kSplitMaxBlocks = 2 * kChipCUs;
+constexpr int kMinChunkTiles = 8;
+constexpr int kChunkMinSaving = 32;
+
 }  // namespace
+
+FwdSplitPlan fwd_split_plan(int B, int H, int Nq, int Nk, int d, int wl, int wr) {
+  FwdSplitPlan pl{0, 0, 0, 0};
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0) return pl;
+  const int n_qt = (Nq + kBM - 1) / kBM;
+  const int64_t BH = (int64_t)B * H;
+  if (n_qt * BH > kSplitMaxBlocks) return pl;
+  const bool band = wl >= 0 || wr >= 0;
+  int64_t W = 0;
+  for (int qb = 0; qb < n_qt; ++qb) {
+    int lo, hi;
+    block_tiles(qb, Nq, Nk, wl, wr, band, lo, hi);
+    W += hi - lo;
+  }
+  const int64_t slots = (int64_t)(d == 64 ? 4 : 3) * kChipCUs;  // resident workgroups
+  const int64_t per_bh = std::max<int64_t>(1, slots / BH);
+  int most = 0;
+  std::vector<int> tiles(n_qt);
+  for (int qb = 0; qb < n_qt; ++qb) {
+    int lo, hi;
+    block_tiles(qb, Nq, Nk, wl, wr, band, lo, hi);
+    tiles[qb] = hi - lo;
+    most = std::max(most, hi - lo);
+  }
+  auto count = [&](int chunk) {
+    int64_t n = 0;
+    for (int x : tiles) n += block_chunks(x, chunk);
+    return n;
+  };
+  int chunk = (int)std::max<int64_t>(kMinChunkTiles, (W + per_bh - 1) / per_bh);
+  while (chunk < most && count(chunk) > per_bh) chunk += std::max(1, chunk / 32);
+  // the critical path without chunks: the heaviest block, in runs of the
+  // intra-workgroup split where fa_fwd_ex would use it
+  const int unsplit = n_qt * BH <= kChipCUs && most >= kKSplitMinTiles
+                          ? (most + (d == 64 ? kKSplit<64> : kKSplit<128>) - 1) / (d == 64 ? kKSplit<64> : kKSplit<128>)
+                          : most;
+  if (chunk + kChunkMinSaving > unsplit) return pl;
+  int n_chunks = 0, n_split = 0, P = 0;
+  for (int x : tiles) {
+    const int sb = block_chunks(x, chunk);
+    n_chunks += sb;
+    if (sb > 1) {
+      ++n_split;
+      P += sb;
+    }
+  }
+  if (n_split == 0) return pl;
+  pl.chunk = chunk;
+  pl.n_chunks = n_chunks;
+  pl.n_split = n_split;
+  pl.P = P;
+  return pl;
+}
+
+size_t fwd_splitk_workspace_bytes(int B, int H, int Nq, int Nk, int d, int wl, int wr) {
+  const FwdSplitPlan pl = fwd_split_plan(B, H, Nq, Nk, d, wl, wr);
+  if (pl.chunk == 0) return 0;
+  const size_t n = (size_t)B * H * pl.P * kBM * (size_t)(d + 2) * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+hipError_t launch_fwd_splitk(const FwdParams& p, const FwdSplitPlan& plan, int d, int dtype, bool banded,
+                             hipStream_t stream) {
+  if (d == 64)
+    return dtype == DT_F16 ? launch_chunked<64, DT_F16>(p, plan, banded, stream)
+                           : launch_chunked<64, DT_BF16>(p, plan, banded, stream);
+  return dtype == DT_F16 ? launch_chunked<128, DT_F16>(p, plan, banded, stream)
+                         : launch_chunked<128, DT_BF16>(p, plan, banded, stream);
+}
 
 hipError_t launch_fwd(const FwdParams& p, int d, int dtype, bool banded, hipStream_t stream) {
   if (d == 64) return dtype == DT_F16 ? launch_dc<64, DT_F16>(p, banded, stream) : launch_dc<64, DT_BF16>(p, banded, stream);

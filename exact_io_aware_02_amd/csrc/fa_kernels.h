@@ -29,7 +29,26 @@ struct FwdParams {
   DropoutParams drop;
   float c;         // |scale| * log2(e), clamped away from 0
   uint32_t qflip;  // 0x80008000 when scale < 0 (Q is negated on load), else 0
+  // Key-chunked forward (fa_fwd_splitk): chunk = key tiles per chunk (0:
+  // not chunked), P = partial slots per (b, h), part = their fp32 storage
+  // ([B*H][P][128 rows][d] partial O^T rows, then [128] m, then [128] l).
+  int chunk;
+  int P;
+  float* part;
 };
+
+// The key-chunk plan of fa_fwd_splitk for these sizes: chunk = 0 when the
+// grid fills the chip or no query block would be split.
+struct FwdSplitPlan {
+  int chunk;     // key tiles (32 keys) per chunk
+  int n_chunks;  // workgroups per (b, h)
+  int n_split;   // query blocks split into two or more chunks, per (b, h)
+  int P;         // partial slots per (b, h)
+};
+FwdSplitPlan fwd_split_plan(int B, int H, int Nq, int Nk, int d, int wl, int wr);
+size_t fwd_splitk_workspace_bytes(int B, int H, int Nq, int Nk, int d, int wl, int wr);
+hipError_t launch_fwd_splitk(const FwdParams& p, const FwdSplitPlan& plan, int d, int dtype, bool banded,
+                             hipStream_t stream);
 
 struct BwdParams {
   const uint16_t* q;

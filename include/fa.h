@@ -123,6 +123,31 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               const int64_t v_strides[3], const int64_t o_strides[3],
               void* stream);
 
+/* Bytes of workspace fa_fwd_splitk needs for these sizes; 0 when it
+ * needs none (the grid of 128-query blocks fills the chip, or no block's
+ * keys would be split).  causal, window_left, window_right as in fa_fwd_ex. */
+size_t fa_fwd_splitk_workspace_bytes(int B, int H, int Nq, int Nk, int d, int causal, int window_left,
+                                     int window_right);
+
+/* fa_fwd_ex for grids too small to fill the chip, with the key range of
+ * each heavy query block split over several workgroups (the glossary
+ * article's online-softmax merge of partial results across blocks; FA2
+ * entry, "並列化改良": parallelism over the sequence as well as over batch
+ * and heads).  Same arguments, results within fp32 rounding of fa_fwd_ex,
+ * deterministic: the partial results (O, row max, row sum) of a block's
+ * chunks are merged in chunk order by a second kernel on `stream`.
+ *   workspace: caller-owned device memory of at least
+ *   fa_fwd_splitk_workspace_bytes(...) bytes, 256-byte aligned, not
+ *   overlapping any tensor; contents on entry ignored, on return
+ *   unspecified.  When that size is 0, workspace may be NULL and the call
+ *   runs exactly fa_fwd_ex's kernels. */
+int fa_fwd_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                  int window_left, int window_right, float dropout_p, uint64_t seed, uint32_t offset, int dtype,
+                  const int64_t q_strides[3], const int64_t k_strides[3],
+                  const int64_t v_strides[3], const int64_t o_strides[3],
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Forward with fp8 inputs (the skill guide's Workflow 3, step 3:
  * FlashAttention-3's FP8 path, forward only, q, k and v cast to
  * float8_e4m3fn).
@@ -271,8 +296,8 @@ const char* fa_status_string(int status);
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* fa_last_error_message(void);
 
-/* Library ABI version, currently 5 (3 added fa_fwd_fp8, 4
- * fa_bwd_ex_workspace_bytes, 5 fa_bwd_noalloc). */
+/* Library ABI version, currently 6 (3 added fa_fwd_fp8, 4
+ * fa_bwd_ex_workspace_bytes, 5 fa_bwd_noalloc, 6 fa_fwd_splitk). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -46,7 +46,7 @@ def test_exported_dynamic_symbols_are_c_names():
 
 
 def test_status_strings_and_version():
-    assert fa.fa_abi_version() == 5
+    assert fa.fa_abi_version() == 6
     assert fa.fa_status_string(0) == "FA_OK"
     assert fa.fa_status_string(1) == "FA_ERR_INVALID_ARG"
     assert fa.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
@@ -328,3 +328,101 @@ def test_ex_accepts_either_workspace_size():
         assert lib.fa_bwd_ex(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), P(6 * A), P(7 * A), P(8 * A), P(9 * A),
                              1, H, Hkv, N, N, 64, 0.125, 1, -1, -1, 0.0, 0, 0, 0, *st, P(10 * A), nbytes,
                              fa.FA_BWD_ALL, None) == fa.FA_ERR_DEVICE
+
+
+# --- key-split forward (fa_fwd_splitk) ------------------------------------------
+
+def _plan_model(B, H, Nq, Nk, d, causal, wl=-1, wr=-1):
+    """The chunk plan restated: 128-query blocks, 32-key tiles; grids of at
+    most 512 blocks; with W the key tiles of one head's blocks and
+    S = floor(F * 256 / (B H)) the resident workgroups per head (F = 4 at
+    d = 64, else 3), the chunk length starts at max(8, ceil(W / S)) and
+    grows by max(1, chunk // 32) while the chunks exceed S and it is below
+    the longest block; the plan is dropped unless chunk + 32 <= the
+    unsplit critical path (the longest block's tiles divided by 3,
+    rounded up, when the grid has at most 256 blocks and that block 32+
+    tiles); a block of n tiles has
+    ceil(n / chunk) chunks (1 if n = 0); the workspace holds
+    (d + 2) * 128 floats per chunk of a block with two or more."""
+    wl = -1 if wl < 0 or wl >= Nq else wl
+    wr = 0 if causal else (-1 if wr < 0 or wr >= Nk else wr)
+    n_qt = -(-Nq // 128)
+    if n_qt * B * H > 512:
+        return 0
+    tiles = []
+    for qb in range(n_qt):
+        kend, j0 = Nk, 0
+        if wl >= 0 or wr >= 0:
+            qlast = min(qb * 128 + 128, Nq) - 1
+            if wr >= 0:
+                kend = min(Nk, qlast + wr + 1)
+            if wl >= 0:
+                j0 = max(0, qb * 128 - wl) // 32
+        tiles.append(max(j0, -(-kend // 32)) - j0)
+    per_bh = max(1, (4 if d == 64 else 3) * 256 // (B * H))
+    chunks = lambda c: sum(max(1, -(-n // c)) for n in tiles)  # noqa: E731
+    chunk = max(8, -(-sum(tiles) // per_bh))
+    while chunk < max(tiles) and chunks(chunk) > per_bh:
+        chunk += max(1, chunk // 32)
+    most = max(tiles)
+    ks = 3
+    unsplit = -(-most // ks) if n_qt * B * H <= 256 and most >= 32 else most
+    if chunk + 32 > unsplit:
+        return 0
+    P = sum(c for c in (max(1, -(-n // chunk)) for n in tiles) if c > 1)
+    return 0 if P == 0 else -(-(B * H * P * 128 * (d + 2) * 4) // 256) * 256
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal,wl,wr", [
+    (2, 8, 2048, 2048, 64, 1, -1, -1),      # the training-step workload
+    (1, 2, 16384, 16384, 128, 1, -1, -1),   # 2 heads of 16K (one GPU of 8 under head sharding)
+    (2, 16, 1024, 1024, 64, 1, -1, -1),
+    (2, 8, 512, 512, 64, 0, -1, -1),
+    (1, 2, 128, 128, 64, 0, -1, -1),        # one block of 4 tiles: nothing to split
+    (1, 16, 16384, 16384, 128, 1, -1, -1),  # 2048 blocks: fills the chip
+    (1, 4, 3000, 2000, 128, 0, 300, 40),    # a window (rows past 2040 admit no key)
+    (3, 1, 5000, 7000, 64, 1, -1, -1),
+])
+def test_fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, causal, wl, wr):
+    assert fa.fa_fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, causal, (wl, wr)) == \
+        _plan_model(B, H, Nq, Nk, d, causal, wl, wr)
+
+
+def test_fwd_splitk_workspace_examples():
+    # 16 blocks of 4 .. 64 tiles per head: the intra-workgroup split's run
+    # (22 tiles) beats any chunking, so no workspace
+    assert fa.fa_fwd_splitk_workspace_bytes(2, 8, 2048, 2048, 64, 1) == 0
+    # 2 heads of 128 blocks of 4 .. 512 tiles, 384 resident workgroups per
+    # head: chunks of at most 115 tiles
+    assert fa.fa_fwd_splitk_workspace_bytes(1, 2, 16384, 16384, 128, 1) > 0
+    assert fa.fa_fwd_splitk_workspace_bytes(1, 16, 16384, 16384, 128, 1) == 0
+    assert fa.fa_fwd_splitk_workspace_bytes(1, 1, 1, 1, 96, 0) == 0
+
+
+S = 1 << 30  # fake addresses far enough apart for tensors of up to 1 GiB
+
+
+def fwd_splitk(ws=10 * S, ws_bytes=1 << 30, B=1, H=2, N=16384, d=128, causal=1):
+    lib = fa.load_library()
+    I3 = ctypes.c_int64 * 3
+    st = I3(H * N * d, N * d, d)
+    return lib.fa_fwd_splitk(P(S), P(2 * S), P(3 * S), P(4 * S), P(5 * S), B, H, H, N, N, d, 0.125, causal, -1, -1,
+                             0.0, 0, 0, 0, st, st, st, st, P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ws=0),                       # needed, NULL
+    dict(ws_bytes=1024),              # too small
+    dict(ws=10 * S + 128),            # not 256-byte aligned
+    dict(ws=4 * S + 256),             # overlaps o
+])
+def test_fwd_splitk_rejects_bad_workspace(kw):
+    assert fwd_splitk(**kw) == fa.FA_ERR_INVALID_ARG
+    assert "workspace" in fa.fa_last_error_message()
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful where no HIP device exists")
+def test_fwd_splitk_valid_call_reaches_device_check():
+    assert fwd_splitk() == fa.FA_ERR_DEVICE
+    # sizes that need no workspace accept NULL
+    assert fwd_splitk(ws=0, ws_bytes=0, B=1, H=16, N=16384, d=128) == fa.FA_ERR_DEVICE

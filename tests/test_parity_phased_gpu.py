@@ -1,9 +1,23 @@
-"""GPU parity of the forward's phased schedule, used from 1024 (d = 128) or
-1536 (d = 64) workgroups of 128 queries upward (the other GPU tests mostly launch smaller grids, which
-run the interleaved schedule).
+"""GPU parity of the forward's launch shapes, each on the same cases:
+
+* small (the binding's default route for grids of at most one workgroup
+  per CU: fa_fwd_splitk, which for these short blocks runs fa_fwd_ex's
+  kernels);
+* interleaved schedule (fa_fwd_ex): grids of more than one workgroup per
+  CU up to the phased threshold;
+* phased schedule: from 1024 (d = 128) or 1536 (d = 64) workgroups of 128
+  queries upward;
+* in test_chunked_forward, fa_fwd_splitk on shapes whose plan splits
+  heavy query blocks' keys over several workgroups (the partial results
+  merged by a second kernel);
+* and, in test_intra_split_forward, the intra-workgroup key split of
+  fa_fwd_ex for grids of at most one workgroup per CU whose heaviest block
+  has 32 or more key tiles: three groups of four waves per workgroup (on
+  the phased schedule at d = 128, the interleaved one at d = 64), each on
+  its own run of the keys, merged through LDS.
 
 Each case is a small problem repeated along the batch until the grid
-reaches that many workgroups.  The first copy is checked against the fp64 oracle
+reaches the shape's size.  The first copy is checked against the fp64 oracle
 (tolerances of the other parity tests).  Without dropout every copy must
 then equal the first bit for bit.  With dropout the copies draw different
 masks, since the generator's counter holds the batch index.
@@ -46,16 +60,32 @@ CASES = [
 ]
 
 
+SPLIT_MAX_BLOCKS = 256  # CUs of the MI355X
+
+
+def copies(shape, blocks, d):
+    """Copies of a case along the batch that put the grid in ``shape``."""
+    if shape == "small":
+        return max(1, SPLIT_MAX_BLOCKS // blocks)
+    if shape == "interleaved":
+        R = SPLIT_MAX_BLOCKS // blocks + 1
+        assert R * blocks < PHASED_MIN_BLOCKS[d]
+        return R
+    return math.ceil(PHASED_MIN_BLOCKS[d] / blocks)
+
+
+@pytest.mark.parametrize("shape", ["small", "interleaved", "phased"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_phased_forward_matches_oracle(case):
+def test_phased_forward_matches_oracle(case, shape):
     name, B, H, Hkv, Nq, Nk, d, dt, layout, causal, window, dr = case
     blocks = math.ceil(Nq / 128) * B * H
-    R = math.ceil(PHASED_MIN_BLOCKS[d] / blocks)
-    say("case %s: %d copies, %d workgroups" % (name, R, R * blocks))
+    R = copies(shape, blocks, d)
+    say("case %s %s: %d copies, %d workgroups" % (name, shape, R, R * blocks))
     inp = make_qkv(B, H, Nq, Nk, d, dt, layout, seed=61, Hkv=Hkv)
     q, k, v = (inp[x].repeat(R, 1, 1, 1).to(DEV) for x in ("q", "k", "v"))
     scale = 1.0 / math.sqrt(d)
-    o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=scale, layout=layout, window=window, dropout=dr)
+    o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=scale, layout=layout, window=window, dropout=dr,
+                              splitk=shape == "small")
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
     w = window if window is not None else (-1, -1)
@@ -77,3 +107,91 @@ def test_phased_forward_matches_oracle(case):
         for r in range(1, R):
             assert torch.equal(o[r * B:(r + 1) * B].view(torch.int16), o[:B].view(torch.int16)), r
             assert torch.equal(lse[r * B:(r + 1) * B], lse[:B]), r
+
+
+INTRA_CASES = [
+    # name, B, H, Hkv, Nq, Nk, d, dtype, layout, causal, window, dropout
+    ("d128_causal", 1, 2, 2, 1100, 1100, 128, "bf16", "bhsd", True, None, None),
+    ("d64_causal_bshd", 2, 3, 3, 1500, 1500, 64, "fp16", "bshd", True, None, None),
+    ("d128_noncausal_rect", 1, 2, 2, 300, 1300, 128, "fp16", "bhsd", False, None, None),
+    ("d64_gqa_window", 1, 4, 2, 1200, 1200, 64, "bf16", "bhsd", True, (900, -1), None),
+    ("d128_window_empty_rows", 1, 2, 2, 1500, 1100, 128, "bf16", "bhsd", False, (1000, 200), None),
+    ("d64_dropout", 1, 2, 2, 1100, 1100, 64, "fp16", "bhsd", True, None, (0.25, (9 << 32) + 1, 4)),
+]
+
+
+@pytest.mark.parametrize("case", INTRA_CASES, ids=[c[0] for c in INTRA_CASES])
+def test_intra_split_forward(case):
+    """fa_fwd_ex on a grid of at most 256 workgroups whose heaviest block
+    has 32+ key tiles (the intra-workgroup split; some groups of the light
+    blocks get no tiles): against the oracle; the same inputs through
+    fa_fwd_splitk agree to within the same tolerance."""
+    name, B, H, Hkv, Nq, Nk, d, dt, layout, causal, window, dr = case
+    say("case intra split %s" % name)
+    inp = make_qkv(B, H, Nq, Nk, d, dt, layout, seed=67, Hkv=Hkv)
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=scale, layout=layout, window=window, dropout=dr,
+                              splitk=False)
+    o2, lse2 = fa.attention_fwd(q, k, v, causal=causal, scale=scale, layout=layout, window=window, dropout=dr)
+    o3, lse3 = fa.attention_fwd(q, k, v, causal=causal, scale=scale, layout=layout, window=window, dropout=dr,
+                                splitk=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o3) and torch.equal(lse, lse3), "run to run"
+    w = window if window is not None else (-1, -1)
+    args = [to_bhsd64(inp[x], layout) for x in ("q", "k", "v")]
+    o_ref, lse_ref = attention_fwd64(*args, scale, causal, window=w, dropout=dr)
+    keep = dropout_threshold(dr[0])[1] if dr else 1.0
+    live = np.isfinite(lse_ref)
+    for tag, oo, ll in (("intra split", o, lse), ("chunked", o2, lse2)):
+        got_o = to_bhsd64(oo.cpu(), layout)
+        got_l = ll.cpu().numpy().astype(np.float64)
+        err_o = np.abs(got_o - o_ref).max()
+        np.testing.assert_array_equal(np.isneginf(got_l), ~live)
+        err_l = np.abs(got_l[live] - lse_ref[live]).max()
+        say("  %s: O max-abs err %.3e, LSE %.3e" % (tag, err_o, err_l))
+        assert err_o <= TOL_O[dt] * keep and err_l <= TOL_LSE, tag
+
+
+CHUNK_CASES = [
+    # name, B, H, Hkv, Nq, Nk, d, dtype, layout, causal, window, dropout
+    ("d64_causal_4k", 1, 1, 1, 4096, 4096, 64, "fp16", "bhsd", True, None, None),
+    ("d128_causal_4k", 1, 2, 2, 4096, 4096, 128, "bf16", "bhsd", True, None, None),
+    ("d128_long_keys", 1, 1, 1, 256, 8192, 128, "fp16", "bhsd", False, None, None),
+    ("d64_gqa_window_bshd", 1, 2, 1, 8192, 8192, 64, "bf16", "bshd", False, (6000, 300), None),
+    ("d128_dropout_causal", 1, 1, 1, 6000, 6000, 128, "bf16", "bhsd", True, None, (0.2, (5 << 32) + 9, 5)),
+    ("d128_window_empty_rows", 1, 2, 2, 6000, 5000, 128, "fp16", "bhsd", False, (300, 5000), None),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_chunked_forward(case):
+    """fa_fwd_splitk where its plan chunks the keys: against the oracle,
+    bitwise repeatable, and within tolerance of fa_fwd_ex."""
+    name, B, H, Hkv, Nq, Nk, d, dt, layout, causal, window, dr = case
+    w = window if window is not None else (-1, -1)
+    nbytes = fa.fa_fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, causal, w)
+    say("case chunked %s: workspace %d bytes" % (name, nbytes))
+    assert nbytes > 0
+    inp = make_qkv(B, H, Nq, Nk, d, dt, layout, seed=73, Hkv=Hkv)
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=scale, layout=layout, window=window, dropout=dr)
+    o2, lse2 = fa.attention_fwd(q, k, v, causal=causal, scale=scale, layout=layout, window=window, dropout=dr)
+    o3, lse3 = fa.attention_fwd(q, k, v, causal=causal, scale=scale, layout=layout, window=window, dropout=dr,
+                                splitk=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "run to run"
+    args = [to_bhsd64(inp[x], layout) for x in ("q", "k", "v")]
+    o_ref, lse_ref = attention_fwd64(*args, scale, causal, window=w, dropout=dr)
+    keep = dropout_threshold(dr[0])[1] if dr else 1.0
+    live = np.isfinite(lse_ref)
+    for tag, oo, ll in (("chunked", o, lse), ("fa_fwd_ex", o3, lse3)):
+        got_o = to_bhsd64(oo.cpu(), layout)
+        got_l = ll.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got_o).all(), tag
+        err_o = np.abs(got_o - o_ref).max()
+        np.testing.assert_array_equal(np.isneginf(got_l), ~live)
+        err_l = np.abs(got_l[live] - lse_ref[live]).max()
+        say("  %s: O max-abs err %.3e, LSE %.3e" % (tag, err_o, err_l))
+        assert err_o <= TOL_O[dt] * keep and err_l <= TOL_LSE, tag
