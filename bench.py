@@ -309,8 +309,10 @@ def config_report(fa, torch, stream, peak_of, with_oracle=True, sustain_s=2.0):
             if w.backward:
                 do = inp["do"].to(q.device)
                 dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-                ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.N, w.d, fa.FA_FP16 if w.dtype == "fp16"
-                                                           else fa.FA_BF16), dtype=torch.uint8, device=q.device)
+                # the workspace that lets an under-filled grid split its dK/dV stage
+                ws = torch.empty(fa.fa_bwd_ex_workspace_bytes(w.B, w.H, w.H, w.N, w.N, w.d,
+                                                              fa.FA_FP16 if w.dtype == "fp16" else fa.FA_BF16),
+                                 dtype=torch.uint8, device=q.device)
                 bwd = lambda st: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, st)
                 out[name + " bwd"] = timed(bwd, 2.5 * flop, peak, name + " bwd")
                 out[name + " bwd"]["workload"] = out[key]["workload"] + " backward"
@@ -368,8 +370,8 @@ def profile_configs(fa, torch, stream):
             if w.backward:
                 do = inp["do"].to(q.device)
                 dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-                ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.N, w.d, fa.FA_FP16), dtype=torch.uint8,
-                                 device=q.device)
+                ws = torch.empty(fa.fa_bwd_ex_workspace_bytes(w.B, w.H, w.H, w.N, w.N, w.d, fa.FA_FP16),
+                                 dtype=torch.uint8, device=q.device)
                 for _ in range(5):
                     fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, s, causal, ws, stream)
                 torch.cuda.synchronize()

@@ -505,8 +505,9 @@ def attention_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bhsd", 
     Hkv, Nk = _dims(k, layout)[1:3]
     s = _default_scale(d, scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    nbytes = (fa_bwd_ex_workspace_bytes(B, H, Hkv, Nq, Nk, d, _dtype_code(q)) if Hkv != H
-              else fa_bwd_workspace_bytes(B, H, Nq, Nk, d, _dtype_code(q)))
+    # the workspace that lets the dK/dV stage split its key blocks' steps
+    # (fewer K/V heads, or a grid too small for the chip)
+    nbytes = fa_bwd_ex_workspace_bytes(B, H, Hkv, Nq, Nk, d, _dtype_code(q))
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     contiguous = all(t.is_contiguous() for t in (q, k, v, o, do))
     if Hkv != H or window is not None or dropout is not None:

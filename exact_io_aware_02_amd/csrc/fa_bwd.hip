@@ -30,6 +30,7 @@
 //                reads K^T transposed from the K tile.  Each step forms
 //                dS of tile j on the VALU, then issues dQ(j) and the S and
 //                dP MFMAs of tile j+1 as one interleaved run.
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -44,6 +45,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kT = 32;        // rows per streamed tile (queries in dkdv, keys in dq)
 constexpr int kStatPad = 64;  // per-(b,h) stride of the workspace statistics, rounded up to this
+constexpr int kChipCUs = 256;  // MI355X (workspace sizes are planned for it, so they depend on the sizes alone)
 
 template <int DT>
 __device__ __forceinline__ float lo_f32(uint32_t w);
@@ -224,13 +226,12 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
   const int pair = role_a ? wave : wave - NPAIR;
   const int Hkv = p.H / p.G;
   const int BH = p.B * Hkv;
-  // workgroups per key tile: one per (batch, K/V head, group of G / S query heads)
+  // workgroups per key tile: one per (batch, K/V head, run sp of the steps)
   const int t = blockIdx.x;
   const int kt = t / (BH * p.S);  // ascending key tiles: the causal-heaviest first
   const int rem = t - kt * BH * p.S;
   const int bhk = rem / p.S;
   const int sp = rem - bhk * p.S;
-  const int GS = p.G / p.S;  // query heads of this workgroup: hk * G + sp * GS + [0, GS)
   const int b = bhk / Hkv, hk = bhk - b * Hkv;
   const int k0 = kt * BNK;
   const int kw0 = k0 + pair * KW;
@@ -250,11 +251,16 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
     if (p.wl >= 0) qhi = min(n_qt, (k0 + BNK - 1 + p.wl) / kT + 1);
   }
   const int nq = max(0, qhi - qlo);
-  const int U = GS * nq;
-  const int h0 = hk * p.G + sp * GS;
+  // this workgroup's run [u0, u0 + U) of the S near-equal runs of the G * nq
+  // steps (the query heads' tile sequences back to back)
+  const int Utot = p.G * nq;
+  const int u0 = (int)((int64_t)sp * Utot / p.S);
+  const int U = (int)((int64_t)(sp + 1) * Utot / p.S) - u0;
+  const int h0 = hk * p.G + (nq > 0 ? u0 / nq : 0);
+  const int it0 = qlo + (nq > 0 ? u0 % nq : 0);
 
   // requests go out in step order; (iss_h, iss_it) is the next one's tile
-  int iss_h = h0, iss_it = qlo;
+  int iss_h = h0, iss_it = it0;
   auto issue = [&](int slot) {
     // role A streams Q and lse2, role B dO and -D
     const uint16_t* tp = role_a ? p.q + b * p.sq.b + iss_h * p.sq.h : p.dout + b * p.sdo.b + iss_h * p.sdo.h;
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
 
     // One step.  (Unrolling by the ring depth would turn the slot bases
     // into immediates, but makes this compiler spill role A's registers.)
-    int it = qlo;            // query tile of the current step
+    int it = it0;            // query tile of the current step
     int hcur = h0;           // its query head
     auto step = [&](int u) {
       const int SL = u & (NB - 1);
@@ -534,27 +540,38 @@ __global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdParams p, int 
 //
 // Each wave alternates a VALU phase and an MFMA phase; the two waves on a
 // SIMD (two workgroups) fill each other's phases.
-template <int D, int DT, bool BAND, bool DROP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWavesPerSimd<D>, kDqWavesPerSimd<D>))) void dq_kernel(BwdParams p) {
+//
+// Grids of at most one workgroup per CU whose heaviest query block has
+// kDqSplitMinTiles key tiles or more run KSPLIT = kDqWavesPerSimd groups of
+// four waves per workgroup (KSPLIT waves per SIMD): group g takes the g-th
+// of KSPLIT near-equal runs of the block's key tiles through a ring of its
+// own, and the groups' dQ^T partial sums are added in group order through
+// LDS.  Every wave executes the same number of barriers (groups with fewer
+// tiles add barrier-only steps).
+template <int D, int DT, bool BAND, bool DROP, int KSPLIT>
+__global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_eu(kDqWavesPerSimd<D>, kDqWavesPerSimd<D>))) void dq_kernel(BwdParams p) {
   constexpr int QW = 32;
   constexpr int BM = kWaves * QW;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NB = 4;  // ring slots
   static_assert(kT == 32, "K/V tiles are the 32-row tiles of fa_device.h");
+  static_assert(KSPLIT == 1 || KSPLIT == kDqWavesPerSimd<D>, "one wave of each group per SIMD");
   constexpr int NI = TileLayout<D>::template copy_insts<kWaves>();  // copy instructions per wave per tile
 
   struct Smem {  // one LDS object, as in dkdv_kernel
-    uint16_t k[NB][kTileElems<D>];
-    uint16_t v[NB][kTileElems<D>];
+    uint16_t k[KSPLIT][NB][kTileElems<D>];
+    uint16_t v[KSPLIT][NB][kTileElems<D>];
   };
   __shared__ __attribute__((aligned(1024))) Smem sm;
-  auto& Ks = sm.k;
-  auto& Vs = sm.v;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave_all / kWaves;        // key group (0 without a split)
+  const int wave = wave_all - grp * kWaves;  // wave within the group: its 32 queries
+  auto& Ks = sm.k[grp];
+  auto& Vs = sm.v[grp];
   const int BH = p.B * p.H;
   const int n_qt = (p.Nq + BM - 1) / BM;
   const int t = blockIdx.x;
@@ -572,14 +589,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vp, p.Nk, p.sv.s, D);
   const uint32_t krow = (uint32_t)(p.sk.s * 2), vrow = (uint32_t)(p.sv.s * 2);
 
-  // key tiles [jt0, n_kt): those some query of the block admits
+  // key tiles [jt0, n_kt): those some query of the block admits; with a
+  // split, this group's run of them
   int kend = p.Nk, jt0 = 0;
   if (BAND) {
     const int qlast = min(q0 + BM, p.Nq) - 1;
     if (p.wr >= 0) kend = min(p.Nk, qlast + p.wr + 1);
     if (p.wl >= 0) jt0 = max(0, q0 - p.wl) / kT;
   }
-  const int n_kt = (kend + kT - 1) / kT;
+  int n_kt = (kend + kT - 1) / kT;
+  int per = 0;  // tiles of the longest run
+  if constexpr (KSPLIT > 1) {
+    const int all = max(0, n_kt - jt0);
+    per = (all + KSPLIT - 1) / KSPLIT;
+    const int ja = min(n_kt, jt0 + grp * per);
+    n_kt = min(n_kt, ja + per);
+    jt0 = ja;
+  }
 
   // tile jt0 + t lives in slot t mod 4
   auto issue = [&](int j, int slot) {
@@ -700,6 +726,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kDqWav
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  if constexpr (KSPLIT > 1) {
+    // one barrier per step: pad the shorter runs to the longest
+    for (int i = max(0, n_kt - jt0); i < per; ++i) lds_barrier();
+    // every group is done with its ring: reuse it for the partial sums
+    constexpr int NV = DB * 16;
+    static_assert((size_t)(KSPLIT - 1) * kWaves * NV * 64 * 4 <= sizeof(Smem), "partials fit the rings");
+    float* xo = reinterpret_cast<float*>(&sm) + (size_t)((grp - 1) * kWaves + wave) * NV * 64 + lane;
+    lds_barrier();
+    if (grp > 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64] = adq[db][r];
+    }
+    lds_barrier();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < KSPLIT; ++g) {
+      const float* xi = reinterpret_cast<const float*>(&sm) + (size_t)((g - 1) * kWaves + wave) * NV * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) adq[db][r] += xi[(db * 16 + r) * 64];
+    }
+  }
+
   if (qi < p.Nq) store_rows<DT, DB>(p.dq + b * p.sdq.b + h * p.sdq.h + qi * p.sdq.s, adq, p.scale, half);
 }
 
@@ -750,6 +802,44 @@ SideStream* side_stream(hipStream_t caller) {
   return &ss;
 }
 
+// The dQ kernel's key split pays when the heaviest query block has at least
+// this many key tiles (as in the forward).
+constexpr int kDqSplitMinTiles = 32;
+
+// Launch the dQ kernel on `st`: with the key split when the grid gives a
+// CU at most one workgroup and some block has enough key tiles.
+template <int D, int DT, bool BAND, bool DROP>
+hipError_t launch_dq(const BwdParams& p, int64_t g2, int cus, hipStream_t st) {
+  bool split = false;
+  if (g2 <= cus) {
+    const int n_qt = (p.Nq + 127) / 128;
+    for (int qb = 0; qb < n_qt && !split; ++qb) {
+      int kend = p.Nk, j0 = 0;
+      if (BAND) {
+        const int qlast = std::min(qb * 128 + 128, p.Nq) - 1;
+        if (p.wr >= 0) kend = std::min(p.Nk, qlast + p.wr + 1);
+        if (p.wl >= 0) j0 = std::max(0, qb * 128 - p.wl) / kT;
+      }
+      split = (kend + kT - 1) / kT - j0 >= kDqSplitMinTiles;
+    }
+  }
+  if (split) {
+    constexpr int KSP = kDqWavesPerSimd<D>;
+    hipLaunchKernelGGL((dq_kernel<D, DT, BAND, DROP, KSP>), dim3((unsigned)g2), dim3(kThreads * KSP), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((dq_kernel<D, DT, BAND, DROP, 1>), dim3((unsigned)g2), dim3(kThreads), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return kChipCUs;
+  return n;
+}
+
 template <int D, int DT, bool BAND, bool DROP>
 hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t stream) {
   const int64_t BH = (int64_t)p.B * p.H;
@@ -775,8 +865,9 @@ hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t st
   if (both) {
     lk.lock();
     side = side_stream(stream);
-    // dK/dV workgroups resident per CU: one at d = 128, two at d = 64
-    if (side && g1 > (int64_t)2 * side->cus * (D == 64 ? 2 : 1)) side = nullptr;
+    // dK/dV workgroups resident per CU: one at d = 128, two at d = 64 (the
+    // grid before any split of its key blocks' steps)
+    if (side && g1 / p.S > (int64_t)2 * side->cus * (D == 64 ? 2 : 1)) side = nullptr;
     // A captured call's fork makes the side stream part of that capture
     // until the capture ends; meanwhile another call (eager, or captured
     // elsewhere) must not enqueue onto it, so it runs dQ on its own stream.
@@ -790,8 +881,7 @@ hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t st
     if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
     // from here on the side stream is joined back even if a launch fails
-    hipLaunchKernelGGL((dq_kernel<D, DT, BAND, DROP>), dim3((unsigned)g2), dim3(kThreads), 0, side->s, p);
-    e = hipGetLastError();
+    e = launch_dq<D, DT, BAND, DROP>(p, g2, side->cus, side->s);
   }
   if (e == hipSuccess && (stages & 2) && g1 > 0) {
     hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP>), dim3((unsigned)g1), dim3(128 * kDkvPairs<D>), 0, stream, p);
@@ -807,10 +897,7 @@ hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t st
     return e != hipSuccess ? e : ej;
   }
   if (e != hipSuccess) return e;
-  if ((stages & 4) && g2 > 0) {
-    hipLaunchKernelGGL((dq_kernel<D, DT, BAND, DROP>), dim3((unsigned)g2), dim3(kThreads), 0, stream, p);
-    e = hipGetLastError();
-  }
+  if ((stages & 4) && g2 > 0) e = launch_dq<D, DT, BAND, DROP>(p, g2, device_cus(), stream);
   return e;
 }
 
@@ -847,9 +934,14 @@ float* bwd_lse2_region(void* workspace, int B, int H, int Nq) {
   return static_cast<float*>(workspace) + (size_t)B * (size_t)H * (size_t)stat_stride(Nq);
 }
 
-// Enough dK/dV workgroups to balance a causal band over the chip: at least
-// 1024 (four per CU), splitting each K/V head's G query heads into S groups,
-// S the smallest divisor of G that gets there (else G).
+// dK/dV runs per key block with fewer K/V heads (G > 1): enough
+// workgroups to balance a causal band over the chip, at least 1024 (four
+// per CU), S the smallest divisor of G that gets there (else G), so each
+// run is whole query heads.  With G = 1 there is no split: cutting a key
+// block's query tiles into runs measured 5% faster at B1 H2 N16384 d128
+// (the dQ kernel on the side stream takes the CUs the runs would use) and
+// 30% slower at B2 H8 N2048 d64 (the partial sums, 67 MB, cost more than
+// the shorter critical path saves).
 int bwd_kv_splits(int B, int H, int H_kv, int Nk, int d) {
   if (H_kv <= 0 || H % H_kv != 0) return 1;
   const int G = H / H_kv;

@@ -69,10 +69,11 @@ struct BwdParams {
   DropoutParams drop;
   float scale;  // the softmax scale as given
   float c;      // scale * log2(e) (signed)
-  // dK/dV of a K/V head split over S groups of its G query heads (S
-  // divides G): each workgroup writes fp32 partial sums to `part`
-  // ([2][S][B*H_kv][Nk][d]: dK^T then dV^T, unscaled) and a reduction kernel
-  // sums them; S = 1 accumulates all G heads in registers (part unused).
+  // dK/dV of a key block split over S workgroups: the block's steps (its
+  // G query heads' query tiles, back to back) cut into S near-equal runs;
+  // each workgroup writes fp32 partial sums to `part` ([2][S][B*H_kv][Nk][d]:
+  // dK^T then dV^T, unscaled) and a reduction kernel adds them in run
+  // order; S = 1 accumulates every step in registers (part unused).
   int S;
   float* part;
 };

@@ -262,12 +262,16 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               const int64_t dk_strides[3], const int64_t dv_strides[3],
               void* workspace, size_t workspace_bytes, int stages, void* stream);
 
-/* Workspace bytes for fa_bwd_ex with H_kv K/V heads that enables the split
- * dK/dV stage (at least fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype); 0 if
- * the sizes are invalid).  The extra part holds 2 * S * B * H_kv * Nk * d
- * fp32 partial sums, S the number of groups each K/V head's H / H_kv query
- * heads are split into (1, i.e. no extra part, when H_kv = H or the
- * problem already fills the chip). */
+/* Workspace bytes for the backward (fa_bwd_ex, or with H_kv = H any fa_bwd
+ * entry point taking a workspace) that enables the split dK/dV stage: at
+ * least fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype); 0 if the sizes are
+ * invalid.  The extra part holds 2 * S * B * H_kv * Nk * d fp32 partial
+ * sums: each key block's steps (its query heads' query tiles) are cut into
+ * S runs on as many workgroups, added in run order by a second kernel
+ * (deterministic; results can differ from the unsplit order in the last
+ * bits of fp32 rounding).  S > 1 with fewer K/V heads (whole query heads
+ * per run, until there are 1024 workgroups); S = 1 (no extra part) when
+ * H_kv = H or the problem already fills the chip. */
 size_t fa_bwd_ex_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d, int dtype);
 
 /* fa_bwd for callers that cannot allocate device memory (code under HIP

@@ -297,8 +297,10 @@ def test_python_fp8_binding_checks_dtypes():
 
 def test_ex_workspace_bytes():
     base = fa.fa_bwd_workspace_bytes(1, 16, 16384, 16384, 128, fa.FA_BF16)
-    # equal heads: nothing extra
+    # equal heads: nothing extra, whether the grid fills the chip or not
     assert fa.fa_bwd_ex_workspace_bytes(1, 16, 16, 16384, 16384, 128, fa.FA_BF16) == base
+    assert fa.fa_bwd_ex_workspace_bytes(1, 2, 2, 16384, 16384, 128, fa.FA_BF16) == \
+        fa.fa_bwd_workspace_bytes(1, 2, 16384, 16384, 128, fa.FA_BF16)
     # 16 query heads on 2 K/V heads at 16K, d = 128 (192 keys per dK/dV
     # workgroup): 86 key blocks x 2 = 172 workgroups, split 8 ways to reach 1024
     big = fa.fa_bwd_ex_workspace_bytes(1, 16, 2, 16384, 16384, 128, fa.FA_BF16)

@@ -1,0 +1,81 @@
+"""GPU parity of the backward's splits.
+
+* dQ: a grid of at most one workgroup per CU whose heaviest query block has
+  32 or more key tiles runs three (d = 64) or two (d = 128) groups of four
+  waves per workgroup, each on its own run of the key tiles, their partial
+  sums added through LDS (every case below).
+* dK/dV with fewer K/V heads and the workspace of fa_bwd_ex_workspace_bytes:
+  each key block's steps (its query heads' query tiles) cut into runs of
+  whole query heads on several workgroups, their fp32 partial sums added in
+  run order by a second kernel (the GQA cases).
+
+Every case checks dQ, dK, dV against the fp64 oracle (relative Frobenius
+error <= 2e-2), that a second run is bitwise identical, and, where the
+larger workspace splits dK/dV, that the unsplit stage agrees within the
+same tolerance.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_02_amd as fa
+from attn_inputs import make_qkv, to_bhsd64
+from oracle import attention_bwd64
+
+pytestmark = pytest.mark.gpu
+
+TOL_GRAD = 2e-2
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+CASES = [
+    # name, B, H, Hkv, Nq, Nk, d, dtype, layout, causal, window, dropout
+    ("d128_causal", 1, 2, 2, 1100, 1100, 128, "bf16", "bhsd", True, None, None),
+    ("d64_causal_bshd", 2, 3, 3, 1500, 1500, 64, "fp16", "bshd", True, None, None),
+    ("d128_rect", 1, 2, 2, 300, 1300, 128, "fp16", "bhsd", False, None, None),
+    ("d64_window", 1, 2, 2, 1200, 1200, 64, "bf16", "bhsd", True, (900, -1), None),
+    ("d128_window_empty_rows", 1, 2, 2, 1500, 1100, 128, "bf16", "bhsd", False, (1000, 200), None),
+    ("d64_dropout", 1, 2, 2, 1100, 1100, 64, "fp16", "bhsd", True, None, (0.25, (3 << 32) + 7, 2)),
+    ("d64_gqa", 1, 4, 2, 1100, 1100, 64, "bf16", "bhsd", True, None, None),
+    ("d128_gqa_window_dropout", 1, 8, 2, 1300, 1300, 128, "fp16", "bhsd", True, (700, -1), (0.1, 77, 1)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_split_backward(case):
+    name, B, H, Hkv, Nq, Nk, d, dt, layout, causal, window, dr = case
+    code = fa.FA_FP16 if dt == "fp16" else fa.FA_BF16
+    big = fa.fa_bwd_ex_workspace_bytes(B, H, Hkv, Nq, Nk, d, code)
+    small = fa.fa_bwd_workspace_bytes(B, H, Nq, Nk, d, code)
+    say("case bwd split %s: workspace %d (unsplit %d)" % (name, big, small))
+    assert (big > small) == (Hkv != H)
+    inp = make_qkv(B, H, Nq, Nk, d, dt, layout, seed=83, with_do=True, Hkv=Hkv)
+    q, k, v, do = (inp[x].to(DEV) for x in ("q", "k", "v", "do"))
+    s = 1.0 / math.sqrt(d)
+    w = window if window is not None else (-1, -1)
+    o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=s, layout=layout, window=window, dropout=dr)
+    outs = []
+    for nbytes in (big, big, small):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        g = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+        fa.fa_bwd_ex(q, k, v, o, lse, do, *g, s, causal, ws, w, fa.FA_BWD_ALL, layout, None, dr)
+        outs.append(g)
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b), "run to run"
+    args = [to_bhsd64(inp[x], layout) for x in ("q", "k", "v", "do")]
+    refs = attention_bwd64(*args, s, causal, window=w, dropout=dr)
+    for tag, g in (("split", outs[0]), ("unsplit dK/dV", outs[2])):
+        for nm, x, r in zip(("dq", "dk", "dv"), g, refs):
+            got = to_bhsd64(x.cpu(), layout)
+            assert np.isfinite(got).all(), (tag, nm)
+            rel = np.linalg.norm(got - r) / max(np.linalg.norm(r), 1e-30)
+            say("  %s %s rel-F err %.3e" % (tag, nm, rel))
+            assert rel <= TOL_GRAD, (tag, nm)

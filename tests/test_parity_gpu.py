@@ -483,7 +483,9 @@ def test_small_backward_from_two_host_threads():
     q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
     s = 1.0 / math.sqrt(d)
     o, lse = fa.attention_fwd(q, k, v, causal=True, scale=s)
-    ref = fa.attention_bwd(q, k, v, o, lse, do, causal=True, scale=s)
+    ws0 = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_FP16), dtype=torch.uint8, device=DEV)
+    ref = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    fa.fa_bwd(q, k, v, o, lse, do, *ref, s, True, ws0)  # the same (unsplit) workspace size as the workers'
     torch.cuda.synchronize()
     bad = []
 
@@ -520,9 +522,10 @@ def test_small_backward_captured_while_another_thread_runs_eagerly():
     q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
     s = 1.0 / math.sqrt(d)
     o, lse = fa.attention_fwd(q, k, v, causal=True, scale=s)
-    ref = fa.attention_bwd(q, k, v, o, lse, do, causal=True, scale=s)  # also creates the side stream
-    torch.cuda.synchronize()
     ws_a = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_FP16), dtype=torch.uint8, device=DEV)
+    ref = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    fa.fa_bwd(q, k, v, o, lse, do, *ref, s, True, ws_a)  # also creates the side stream
+    torch.cuda.synchronize()
     ws_b = torch.empty_like(ws_a)
     outs_a = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
     outs_b = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]

@@ -31,7 +31,12 @@ def _case(B, H, N, d, dt, causal, seed):
     q, k, v, do = (inp[x].to(DEV) for x in ("q", "k", "v", "do"))
     s = 1.0 / math.sqrt(d)
     o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=s)
-    ref = fa.attention_bwd(q, k, v, o, lse, do, causal=causal, scale=s)
+    # fa_bwd with the workspace of fa_bwd_workspace_bytes, the size the
+    # scratch array stands in for
+    code = fa.FA_FP16 if dt == "fp16" else fa.FA_BF16
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, N, d, code), dtype=torch.uint8, device=DEV)
+    ref = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    fa.fa_bwd(q, k, v, o, lse, do, *ref, s, causal, ws)
     got = [torch.full_like(q, 7.0), torch.full_like(k, 7.0), torch.full_like(v, 7.0)]
     fa.fa_bwd_noalloc(q, k, v, o, lse, do, *got, s, causal)
     torch.cuda.synchronize()
