@@ -113,7 +113,9 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
  *     byte (j & 3) of word ((j >> 3) & 3) of Philox4x32-10 (Salmon et al.,
  *     SC'11) at counter {2*(j >> 5) + ((j >> 2) & 1), i, b*H + h, offset}
  *     with key {seed mod 2^32, seed >> 32} is >= thr.  The same (seed,
- *     offset) in fa_bwd_ex reproduces the mask.  dropout_p = 0: no dropout.
+ *     offset) in fa_bwd_ex reproduces the mask.  This counter layout is part
+ *     of the ABI: it does not follow how a kernel assigns keys to lanes, and
+ *     it changes only with fa_abi_version().  dropout_p = 0: no dropout.
  *   k, v: [B][H_kv][Nk][d] through their strides; everything else as in
  *   fa_fwd_strided. */
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
