@@ -418,7 +418,10 @@ __device__ __forceinline__ void fwd8_step_phased(int j, int n_kt, f32x16 (&s)[2]
           w4[e] = exp2_fast(__builtin_fmaf(s[mb][r + e], c, mneg));
           ls += w4[e];
         }
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(w4[0], w4[1], 0, false);
+        // both halves of the word are written: the first conversion's
+        // "old" operand is w4[0]'s own register (dead after it), not a
+        // zero that would cost a move
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(w4[0], w4[1], __builtin_bit_cast(int, w4[0]), false);
         pf[4 * mb + r / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(w4[2], w4[3], w, true);
       }
   };
