@@ -214,8 +214,9 @@ def config_report(fa, torch, stream, peak_of, with_oracle=True, sustain_s=2.0):
     """The four smaller workloads (the 16K one is the step above), one entry
     per configuration and pass.  They run in microseconds, less than the
     Python binding takes to launch them, so each is timed two ways: 20
-    launches captured in a HIP graph and replayed 10 times (GPU time per
-    launch, no host gaps), and 100 launches from Python back to back (what
+    launches captured in a HIP graph and replayed (GPU time per launch, no
+    host gaps: the median of five batches of four replays, after three warm
+    ones), and 100 launches from Python back to back (what
     an eager caller sees).  The graph is then replayed back to back for
     ``sustain_s`` seconds while amd-smi reads the GFX clock, which gives the
     fraction of the MFMA peak at the clock the part actually ran.  Parity:
@@ -245,13 +246,22 @@ def config_report(fa, torch, stream, peak_of, with_oracle=True, sustain_s=2.0):
         return g
 
     def graph_ms(g):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(10):
+        # warm replays first, then the median of five batches of four
+        # replays (80 launches each), so that one slow batch (a clock
+        # change, another process) does not set the figure
+        for _ in range(3):
             g.replay()
-        e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 200
+        per = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(4):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / 80)
+        return sorted(per)[2]
 
     def eager_ms(fn):
         for _ in range(10):
