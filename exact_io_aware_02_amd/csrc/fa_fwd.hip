@@ -897,6 +897,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
 // no key).
 template <int D>
 constexpr int kMergeRows = kThreads / (D / 4);  // rows per merge workgroup
+constexpr int kMergeBatch = 8;                  // partial slots loaded together
 
 template <int D, int DT, bool BAND, bool DROP>
 __global__ __launch_bounds__(kThreads) void fwd_merge_kernel(FwdParams p) {
@@ -920,18 +921,43 @@ __global__ __launch_bounds__(kThreads) void fwd_merge_kernel(FwdParams p) {
   const float* pm = pb + kBM * D + row;        // m of slot s at pm[s * SLOT]
   const float* pl = pb + kBM * D + kBM + row;  // l likewise
   const float* po = pb + row * D + 4 * ch;     // this thread's 4 columns
-  float M = -1e30f;
-#pragma unroll 4
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s * SLOT]);
-  float L = 0.f;
+  // Slots in batches of kMergeBatch whose loads all go out before the
+  // first use (one memory latency per batch instead of one per pass);
+  // batches fold in by the online-softmax rule.  With one batch (the
+  // usual case) this is max over the slots, then the sums in slot order.
+  float M = -1e30f, L = 0.f;
   f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = 0; s < ns; ++s) {
-    const float a = exp2_fast(pm[s * SLOT] - M);
-    L += a * pl[s * SLOT];
-    const f32x4 x = *(const f32x4*)(po + s * SLOT);
+  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+    // unconditional loads (past the last slot they repeat it, which
+    // leaves the max unchanged), so that none waits for another
+    float mv[kMergeBatch], lv[kMergeBatch];
+    f32x4 ov[kMergeBatch];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] += a * x[e];
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const size_t si = (size_t)min(s0 + i, ns - 1) * SLOT;
+      mv[i] = pm[si];
+      lv[i] = pl[si];
+      ov[i] = *(const f32x4*)(po + si);
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, mv[i]);
+    if (s0 > 0) {  // rescale what the earlier batches summed
+      const float r = exp2_fast(M - Mb);
+      L *= r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= r;
+    }
+    M = Mb;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (s0 + i < ns) {
+        const float a = exp2_fast(mv[i] - M);
+        L += a * lv[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += a * ov[i][e];
+      }
+    }
   }
   const float inv = L > 0.f ? (DROP ? p.drop.scale : 1.0f) / L : 0.f;
   uint16_t* op = p.o + b * p.so.b + h * p.so.h + qi * p.so.s + 4 * ch;
