@@ -195,6 +195,47 @@ def test_long_context_backward_one_head_and_invariants(long_ctx):
     assert rel_k < 2e-2 and rel_v < 2e-2
 
 
+def test_long_context_head_shard_split(long_ctx):
+    """One GPU's share of the 16K workload under 8-way head sharding (heads
+    0-1) in the launch configuration the benchmark times: fa_fwd_splitk
+    with its workspace (the key range of heavy query blocks cut over
+    workgroups, partials merged in chunk order) and the small-grid backward
+    (dQ's intra-workgroup key split, beside dK/dV on the side stream).
+    Forward against the oracle on 256 seeded rows per head; backward with
+    the full 16-head run's O and LSE: dK, dV bit for bit equal to that run's
+    first two heads (the same workgroups), dQ within fp32 reordering of it
+    (the split only changes the order of the key-tile sums)."""
+    w, inp, s, o, lse, (dq, dk, dv) = long_ctx
+    B, H, N, d = w.B, 2, w.N, w.d
+    q, k, v, do = (gpu(inp[x][:, :H].contiguous()) for x in ("q", "k", "v", "do"))
+    nws = fa.fa_fwd_splitk_workspace_bytes(B, H, N, N, d, True)
+    say("case head shard: workspace %d bytes" % nws)
+    assert nws > 0
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    o2 = torch.empty_like(q)
+    l2 = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    fa.fa_fwd_splitk(q, k, v, o2, l2, s, True, ws)
+    torch.cuda.synchronize()
+    og, lg = to_bhsd64(o2.cpu()), l2.cpu().numpy().astype(np.float64)
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    rows = sample_rows(B, H, N, 256, w.seed + 3000)
+    ro, rl = attention_rows_fwd64(*(to_bhsd64(inp[x][:, :H]) for x in "qkv"), s, True, rows)
+    got_o = np.stack([np.stack([og[b, h][rows[b, h]] for h in range(H)]) for b in range(B)])
+    got_l = np.stack([np.stack([lg[b, h][rows[b, h]] for h in range(H)]) for b in range(B)])
+    err_o, err_l = np.abs(got_o - ro).max(), np.abs(got_l - rl).max()
+    say("  split forward: sampled O max-abs err %.3e, LSE err %.3e" % (err_o, err_l))
+    assert err_o <= TOL_O[w.dtype] and err_l <= TOL_LSE
+    g2 = fa.attention_bwd(q, k, v, gpu(o[:, :H].contiguous()), gpu(lse[:, :H].contiguous()), do, causal=True,
+                          scale=s)
+    torch.cuda.synchronize()
+    dq2, dk2, dv2 = (g.cpu() for g in g2)
+    assert torch.equal(dk2, dk[:, :H]) and torch.equal(dv2, dv[:, :H]), "dK/dV differ from the 16-head run"
+    a, r = to_bhsd64(dq2), to_bhsd64(dq[:, :H])
+    rel = np.linalg.norm(a - r) / np.linalg.norm(r)
+    say("  split dQ vs 16-head run: relative Frobenius %.2e" % rel)
+    assert rel <= 4e-3
+
+
 # ------------------------------------------------------------------ sweeps
 
 SIZES = [1, 2, 3, 17, 63, 64, 65, 127, 129, 255]
