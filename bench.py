@@ -480,9 +480,13 @@ def c4_sampled_parity(inp, o, lse, s, w):
     gl = np.stack([np.stack([lg[b, h][rows[b, h]] for h in range(w.H)]) for b in range(w.B)])
     eo, el = float(np.abs(go - ro).max()), float(np.abs(gl - rl).max())
     flop = 4.0 * w.d * float(sum(int(r) + 1 for r in rows.ravel()))
+    full = 4.0 * w.B * w.H * w.N * w.N * w.d / 2  # the whole causal forward
     return {"rows_per_head": int(rows.shape[2]), "o_maxabs": eo, "lse_maxabs": el, "tol_o": TOL_O[w.dtype],
             "tol_lse": TOL_LSE, "pass": bool(eo <= TOL_O[w.dtype] and el <= TOL_LSE),
-            "oracle": {"seconds": dt, "gflops": flop / dt / 1e9, "cores": blas_threads()}}
+            "oracle": {"seconds": dt, "gflops": flop / dt / 1e9, "cores": blas_threads(),
+                       "extrapolated_full_forward_seconds": dt * full / flop,
+                       "note": "extrapolated: the sampled rows' time scaled by the whole forward's FLOP "
+                               "over the sampled rows' FLOP"}}
 
 
 def noncausal_row(fa, torch, q, k, v, do, s, stream, peak, steps, with_oracle=True):
