@@ -869,21 +869,27 @@ hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t st
     // grid before any split of its key blocks' steps)
     if (side && g1 / p.S > (int64_t)2 * side->cus * (D == 64 ? 2 : 1)) side = nullptr;
     // A captured call's fork makes the side stream part of that capture
-    // until the capture ends; meanwhile another call (eager, or captured
-    // elsewhere) must not enqueue onto it, so it runs dQ on its own stream.
+    // until the capture ends.  Later calls of the same capture may go on
+    // using it; another call (eager, or captured elsewhere) must not
+    // enqueue onto it, so it runs dQ on its own stream.
     if (side) {
-      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-      if (hipStreamIsCapturing(side->s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) side = nullptr;
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone, cc = hipStreamCaptureStatusNone;
+      unsigned long long is = 0, ic = 0;
+      if (hipStreamGetCaptureInfo(side->s, &cs, &is) != hipSuccess) {
+        side = nullptr;
+      } else if (cs != hipStreamCaptureStatusNone) {
+        if (hipStreamGetCaptureInfo(stream, &cc, &ic) != hipSuccess || cc != hipStreamCaptureStatusActive ||
+            cs != hipStreamCaptureStatusActive || ic != is)
+          side = nullptr;
+      }
     }
     if (!side) lk.unlock();
   }
-  if (side) {
-    if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return e;
-    // from here on the side stream is joined back even if a launch fails
-    e = launch_dq<D, DT, BAND, DROP>(p, g2, side->cus, side->s);
-  }
-  if (e == hipSuccess && (stages & 2) && g1 > 0) {
+  // The fork follows the statistics; dK/dV is issued before dQ so that its
+  // workgroups (the heaviest key blocks, the critical path) take the CUs
+  // first, and dQ's fill the CUs that the light key blocks free.
+  if (side && (e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
+  if ((stages & 2) && g1 > 0) {
     hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP>), dim3((unsigned)g1), dim3(128 * kDkvPairs<D>), 0, stream, p);
     e = hipGetLastError();
     if (e == hipSuccess && p.S > 1) {
@@ -892,9 +898,13 @@ hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t st
     }
   }
   if (side) {
-    hipError_t ej = hipEventRecord(side->join, side->s);
-    if (ej == hipSuccess) ej = hipStreamWaitEvent(stream, side->join, 0);
-    return e != hipSuccess ? e : ej;
+    // the fork was recorded, so the side stream is joined back even if a
+    // launch fails
+    hipError_t ej = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (ej == hipSuccess && e == hipSuccess) ej = launch_dq<D, DT, BAND, DROP>(p, g2, side->cus, side->s);
+    hipError_t er = hipEventRecord(side->join, side->s);
+    if (er == hipSuccess) er = hipStreamWaitEvent(stream, side->join, 0);
+    return e != hipSuccess ? e : ej != hipSuccess ? ej : er;
   }
   if (e != hipSuccess) return e;
   if ((stages & 4) && g2 > 0) e = launch_dq<D, DT, BAND, DROP>(p, g2, device_cus(), stream);

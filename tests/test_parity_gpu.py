@@ -513,6 +513,41 @@ def test_small_backward_side_stream(B, H, N, d, dt):
             assert torch.equal(a, b), "replay %d" % i
 
 
+def test_small_backward_several_calls_in_one_graph():
+    """Three small backwards captured in one graph, each on its own outputs
+    and workspace: every call of the capture (not only the first) may fork
+    dQ onto the side stream that the capture already holds.  Replays, with
+    eager work on the outputs between them, equal the eager result bit for
+    bit."""
+    B, H, N, d = 2, 8, 1024, 64
+    inp = make_qkv(B, H, N, N, d, "fp16", seed=9, with_do=True)
+    q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
+    s = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd(q, k, v, causal=True, scale=s)
+    nb = fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_FP16)
+    ref = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    for st in (fa.FA_BWD_PREP, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
+        fa.fa_bwd_stages(q, k, v, o, lse, do, *ref, s, True, torch.empty(nb, dtype=torch.uint8, device=DEV), st)
+    wss = [torch.empty(nb, dtype=torch.uint8, device=DEV) for _ in range(3)]
+    outs = [[torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)] for _ in range(3)]
+    fa.fa_bwd(q, k, v, o, lse, do, *outs[0], s, True, wss[0])  # creates the side stream outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(3):
+            fa.fa_bwd(q, k, v, o, lse, do, *outs[i], s, True, wss[i], torch.cuda.current_stream())
+    for r in range(3):
+        for ts in outs:
+            for t in ts:
+                t.fill_(float(r + 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, ts in enumerate(outs):
+            for a, b in zip(ts, ref):
+                assert torch.equal(a, b), "replay %d call %d" % (r, i)
+
+
 def test_small_backward_from_two_host_threads():
     """Two host threads run small backwards (side-stream path) on their own
     streams at the same time, 20 calls each; every result equals the
