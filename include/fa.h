@@ -247,9 +247,9 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
  * lse.  dk, dv are [B][H_kv][Nk][d] through their strides; a K/V
  * head's gradients sum the contributions of all query heads that use it.
  * The workspace is sized by fa_bwd_workspace_bytes(B, H, Nq, ...) with H
- * the number of query heads, or, with fewer K/V heads, preferably by
- * fa_bwd_ex_workspace_bytes: a workspace that large lets the dK/dV stage
- * split each K/V head's query heads over more workgroups (their fp32
+ * the number of query heads, or preferably by fa_bwd_ex_workspace_bytes:
+ * a workspace that large lets the dK/dV stage split each key block's
+ * query tiles (over its query heads) over more workgroups (their fp32
  * partial sums are added in a fixed order by a second kernel, so results
  * stay deterministic; they can differ from the unsplit order in the last
  * bits of fp32 rounding).  lse must be what fa_fwd_ex wrote (-inf for a
@@ -272,8 +272,10 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
  * S runs on as many workgroups, added in run order by a second kernel
  * (deterministic; results can differ from the unsplit order in the last
  * bits of fp32 rounding).  S > 1 with fewer K/V heads (whole query heads
- * per run, until there are 1024 workgroups); S = 1 (no extra part) when
- * H_kv = H or the problem already fills the chip. */
+ * per run, until there are 1024 workgroups); with H_kv = H, S = 2 when the
+ * dK/dV grid (one workgroup per 192 keys at d = 128, 128 at d = 64, per
+ * (b, head)) has fewer workgroups than the MI355X's 256 CUs and Nk >= 2048;
+ * otherwise S = 1 (no extra part). */
 size_t fa_bwd_ex_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d, int dtype);
 
 /* fa_bwd for callers that cannot allocate device memory (code under HIP

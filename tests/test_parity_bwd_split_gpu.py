@@ -4,10 +4,13 @@
   32 or more key tiles runs three (d = 64) or two (d = 128) groups of four
   waves per workgroup, each on its own run of the key tiles, their partial
   sums added through LDS (every case below).
-* dK/dV with fewer K/V heads and the workspace of fa_bwd_ex_workspace_bytes:
-  each key block's steps (its query heads' query tiles) cut into runs of
-  whole query heads on several workgroups, their fp32 partial sums added in
-  run order by a second kernel (the GQA cases).
+* dK/dV with the workspace of fa_bwd_ex_workspace_bytes: each key block's
+  steps (its query heads' query tiles) cut into runs on several
+  workgroups, their fp32 partial sums added in run order by a second
+  kernel.  With fewer K/V heads the runs are whole query heads (the GQA
+  cases); with equal heads a grid of fewer dK/dV workgroups than CUs with
+  Nk >= 2048 cuts each key block's query tiles into two runs (the eq_split
+  cases, whose runs can start and end inside the causal band).
 
 Every case checks dQ, dK, dV against the fp64 oracle (relative Frobenius
 error <= 2e-2), that a second run is bitwise identical, and, where the
@@ -45,7 +48,21 @@ CASES = [
     ("d64_dropout", 1, 2, 2, 1100, 1100, 64, "fp16", "bhsd", True, None, (0.25, (3 << 32) + 7, 2)),
     ("d64_gqa", 1, 4, 2, 1100, 1100, 64, "bf16", "bhsd", True, None, None),
     ("d128_gqa_window_dropout", 1, 8, 2, 1300, 1300, 128, "fp16", "bhsd", True, (700, -1), (0.1, 77, 1)),
+    ("d128_eq_split_causal", 1, 2, 2, 2500, 2500, 128, "bf16", "bhsd", True, None, None),
+    ("d64_eq_split_bshd_ragged", 1, 2, 2, 2100, 2100, 64, "fp16", "bshd", True, None, None),
+    ("d128_eq_split_window_rect", 1, 1, 1, 3000, 2200, 128, "bf16", "bhsd", False, (800, 100), None),
+    ("d64_eq_split_dropout", 2, 1, 1, 2048, 2048, 64, "bf16", "bhsd", True, None, (0.2, (9 << 32) + 1, 4)),
 ]
+
+CUS = 256  # MI355X
+
+
+def splits_expected(B, H, Hkv, Nk, d):
+    """Whether fa_bwd_ex_workspace_bytes asks for partial sums: fewer K/V
+    heads, or equal heads whose dK/dV grid (32 keys per wave pair, 4 pairs
+    at d = 64, 6 at d = 128) has fewer workgroups than CUs, with Nk >= 2048."""
+    blocks = -(-Nk // (32 * (4 if d == 64 else 6))) * B * Hkv
+    return Hkv != H or (Nk >= 2048 and blocks < CUS)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -55,7 +72,7 @@ def test_split_backward(case):
     big = fa.fa_bwd_ex_workspace_bytes(B, H, Hkv, Nq, Nk, d, code)
     small = fa.fa_bwd_workspace_bytes(B, H, Nq, Nk, d, code)
     say("case bwd split %s: workspace %d (unsplit %d)" % (name, big, small))
-    assert (big > small) == (Hkv != H)
+    assert (big > small) == splits_expected(B, H, Hkv, Nk, d)
     inp = make_qkv(B, H, Nq, Nk, d, dt, layout, seed=83, with_do=True, Hkv=Hkv)
     q, k, v, do = (inp[x].to(DEV) for x in ("q", "k", "v", "do"))
     s = 1.0 / math.sqrt(d)

@@ -201,10 +201,13 @@ def test_long_context_head_shard_split(long_ctx):
     with its workspace (the key range of heavy query blocks cut over
     workgroups, partials merged in chunk order) and the small-grid backward
     (dQ's intra-workgroup key split, beside dK/dV on the side stream).
-    Forward against the oracle on 256 seeded rows per head; backward with
-    the full 16-head run's O and LSE: dK, dV bit for bit equal to that run's
-    first two heads (the same workgroups), dQ within fp32 reordering of it
-    (the split only changes the order of the key-tile sums)."""
+    Forward against the oracle on 256 seeded rows per head.  Backward with
+    the full 16-head run's O and LSE, as the benchmark runs it (fa_bwd_ex
+    with the workspace of fa_bwd_ex_workspace_bytes: each key block's query
+    tiles in two runs, fp32 partials added in run order): dQ, dK, dV within
+    fp32 reordering of the 16-head run; and with the statistics-only
+    workspace (no dK/dV split) dK, dV bit for bit equal to that run's first
+    two heads (the same workgroups)."""
     w, inp, s, o, lse, (dq, dk, dv) = long_ctx
     B, H, N, d = w.B, 2, w.N, w.d
     q, k, v, do = (gpu(inp[x][:, :H].contiguous()) for x in ("q", "k", "v", "do"))
@@ -225,15 +228,23 @@ def test_long_context_head_shard_split(long_ctx):
     err_o, err_l = np.abs(got_o - ro).max(), np.abs(got_l - rl).max()
     say("  split forward: sampled O max-abs err %.3e, LSE err %.3e" % (err_o, err_l))
     assert err_o <= TOL_O[w.dtype] and err_l <= TOL_LSE
-    g2 = fa.attention_bwd(q, k, v, gpu(o[:, :H].contiguous()), gpu(lse[:, :H].contiguous()), do, causal=True,
-                          scale=s)
-    torch.cuda.synchronize()
-    dq2, dk2, dv2 = (g.cpu() for g in g2)
-    assert torch.equal(dk2, dk[:, :H]) and torch.equal(dv2, dv[:, :H]), "dK/dV differ from the 16-head run"
-    a, r = to_bhsd64(dq2), to_bhsd64(dq[:, :H])
-    rel = np.linalg.norm(a - r) / np.linalg.norm(r)
-    say("  split dQ vs 16-head run: relative Frobenius %.2e" % rel)
-    assert rel <= 4e-3
+    oh, lh = gpu(o[:, :H].contiguous()), gpu(lse[:, :H].contiguous())
+    big = fa.fa_bwd_ex_workspace_bytes(B, H, H, N, N, d, fa.FA_BF16)
+    small = fa.fa_bwd_workspace_bytes(B, H, N, N, d, fa.FA_BF16)
+    assert big > small  # the dK/dV split applies
+    for tag, nbytes in (("split", big), ("unsplit dK/dV", small)):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        g2 = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+        fa.fa_bwd_ex(q, k, v, oh, lh, do, *g2, s, True, ws)
+        torch.cuda.synchronize()
+        dq2, dk2, dv2 = (g.cpu() for g in g2)
+        if tag != "split":
+            assert torch.equal(dk2, dk[:, :H]) and torch.equal(dv2, dv[:, :H]), "dK/dV differ from the 16-head run"
+        for nm, x, r in (("dQ", dq2, dq), ("dK", dk2, dk), ("dV", dv2, dv)):
+            a, rr = to_bhsd64(x), to_bhsd64(r[:, :H])
+            rel = np.linalg.norm(a - rr) / np.linalg.norm(rr)
+            say("  %s %s vs 16-head run: relative Frobenius %.2e" % (tag, nm, rel))
+            assert rel <= 4e-3, (tag, nm)
 
 
 # ------------------------------------------------------------------ sweeps
