@@ -758,8 +758,9 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
 // dK/dV and dQ are independent once the row statistics exist.  When the
 // dK/dV grid is at most two waves of the chip, each kernel leaves most CUs
 // idle, so dQ runs beside dK/dV on a side stream: an event recorded on the
-// caller's stream forks it, and one recorded on the side stream joins it
-// back, so every result is ordered on the caller's stream as before.  One
+// caller's stream after the statistics forks it (dK/dV is issued first),
+// and one recorded on the side stream joins it back, so every result is
+// ordered on the caller's stream as before.  One
 // side stream and two events per device, created on first use outside
 // graph capture and kept until the process ends; the lock pairs each fork
 // and join with their own event records when host threads call at once.

@@ -197,15 +197,19 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype);
  *   dq [B][H][Nq][d], dk/dv [B][H][Nk][d]  out, in dtype
  *   workspace: caller-owned device memory of at least
  *   fa_bwd_workspace_bytes(...) bytes, 256-byte aligned; contents on entry
- *   are ignored and on return unspecified.  P is recomputed as
- *   exp(scale q.k - lse); dS = P * (dP - D) with dP = dO V^T.
+ *   are ignored and on return unspecified.  A workspace of at least
+ *   fa_bwd_ex_workspace_bytes(B, H, H, ...) bytes also lets the dK/dV stage
+ *   split its key blocks when the grid leaves CUs idle (see there).  P is
+ *   recomputed as exp(scale q.k - lse); dS = P * (dP - D) with dP = dO V^T.
  * Streams: all work is ordered on `stream`.  When the dK/dV grid is at most
  * two waves of the chip, the dQ kernel runs on a side stream that the
- * library forks from `stream` and joins back to it with events (one
- * non-blocking stream and two events per device, created by the first such
- * call made outside graph capture and kept until the process exits; calls
- * from several host threads take a short internal lock).  The fork and join
- * are capturable, so a captured call replays the same way. */
+ * library forks from `stream` (after the row statistics, dK/dV issued
+ * first) and joins back to it with events (one non-blocking stream and two
+ * events per device, created by the first such call made outside graph
+ * capture and kept until the process exits; calls from several host
+ * threads take a short internal lock).  The fork and join are capturable:
+ * every call of one capture may fork onto the side stream, and a call made
+ * while a different capture holds it runs dQ on `stream` instead. */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv,
            int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
