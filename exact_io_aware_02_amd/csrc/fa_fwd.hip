@@ -492,6 +492,26 @@ __device__ __forceinline__ void fwd_step_phased(int j, int n_kt, f32x16 (&s)[kNQ
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// A step of the phased ring for a wave with no work on tile j: its share
+// of the copy of tile j + NBUF - 1 (into the slot of tile j - 1), the wait
+// for tile j + 1 and the barrier, as in fwd_step_phased.
+template <int D>
+__device__ __forceinline__ void fwd_idle_phased(int j, int n_kt, uint16_t* __restrict__ Kdst,
+                                                uint16_t* __restrict__ Vdst, __amdgpu_buffer_rsrc_t krs,
+                                                __amdgpu_buffer_rsrc_t vrs, uint32_t krow, uint32_t vrow, uint32_t ktb,
+                                                uint32_t vtb, int lane, int wave) {
+  using TC = TileCopy<D>;
+  constexpr int PD = FwdCfg<D, true>::NBUF - 1;
+  if (j + PD < n_kt) {
+    TC::issue(krs, krow, (uint32_t)(j + PD) * ktb, Kdst, lane, wave);
+    TC::issue(vrs, vrow, (uint32_t)(j + PD) * vtb, Vdst, lane, wave);
+    wait_vmcnt<(PD - 2) * 2 * TC::NI>();
+  } else {
+    wait_loads();
+  }
+  lds_barrier();
+}
+
 // Key tiles [lo, hi) of query block qb (kBM queries): those some query of
 // the block admits (all of them without a band).
 __host__ __device__ __forceinline__ void block_tiles(int qb, int Nq, int Nk, int wl, int wr, bool band, int& lo,
@@ -730,24 +750,45 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
 
   if constexpr (PHASED) {
     if (jt0 < n_kt) {
-      f32x16 sa[kNQB];
-#pragma unroll
-      for (int nb = 0; nb < kNQB; ++nb) sa[nb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 a = lds_rowmajor<D>(Ks[0], ta, ks);
-#pragma unroll
-        for (int nb = 0; nb < kNQB; ++nb) sa[nb] = mfma32<DT>(a, qf[nb][ks], sa[nb]);
+      // This wave's own tiles [wlo, whi): those one of its queries admits.
+      // The workgroup's band can reach further (its other waves' queries);
+      // there the wave's weights would be exact zeros, so it only takes
+      // its part in the ring (copies, wait, barrier) and skips the work.
+      // The result is bit for bit the same (O never holds -0).
+      int wlo = jt0, whi = n_kt;
+      if constexpr (BAND) {
+        if (p.wl >= 0) wlo = max(wlo, max(0, qw0 - p.wl) / kBN);
+        if (p.wr >= 0) whi = min(whi, (qw0 + kQW - 1 + p.wr) / kBN + 1);
+        whi = max(whi, wlo);
       }
       auto wrap = [](int x) { return x >= NBUF ? x - NBUF : x; };
       int sl = 0;  // slot of tile j
-      for (int j = jt0; j < n_kt; ++j) {
+      int j = jt0;
+      auto idle = [&]() {
         const int sp = wrap(sl + NBUF - 1);  // slot of tile j-1
-        fwd_step_phased<D, DT, BAND, DROP, kNQB>(j, n_kt, sa, Vs[sl], Ks[wrap(sl + 1)], Ks[sp], Vs[sp], krs, vrs, krow,
-                                                 vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta,
-                                                 p.drop, (uint32_t)bh);
+        fwd_idle_phased<D>(j, n_kt, Ks[sp], Vs[sp], krs, vrs, krow, vrow, ktb, vtb, lane, wave);
         sl = wrap(sl + 1);
+      };
+      for (; j < wlo; ++j) idle();
+      if (j < whi) {
+        f32x16 sa[kNQB];
+#pragma unroll
+        for (int nb = 0; nb < kNQB; ++nb) sa[nb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 a = lds_rowmajor<D>(Ks[sl], ta, ks);
+#pragma unroll
+          for (int nb = 0; nb < kNQB; ++nb) sa[nb] = mfma32<DT>(a, qf[nb][ks], sa[nb]);
+        }
+        for (; j < whi; ++j) {
+          const int sp = wrap(sl + NBUF - 1);  // slot of tile j-1
+          fwd_step_phased<D, DT, BAND, DROP, kNQB>(j, n_kt, sa, Vs[sl], Ks[wrap(sl + 1)], Ks[sp], Vs[sp], krs, vrs,
+                                                   krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane,
+                                                   wave, ta, p.drop, (uint32_t)bh);
+          sl = wrap(sl + 1);
+        }
       }
+      for (; j < n_kt; ++j) idle();
     }
   } else if (jt0 < n_kt) {
     // Tile jt0 + t lives in slot t mod 4.
