@@ -322,10 +322,6 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
     // order the ring).  The tile of step u lives in slot u mod NB.
     wait_ring<PD - 2, NLOADS>(U - 2);  // the tiles of steps 0 and 1 landed
     lds_barrier();
-    if constexpr (A) {
-      auto s_tile = [&](const uint16_t* __restrict__ Qt) { sd = rows_times_regs<D, DT>(Qt, kv, ta); };
-      if (U > 0) s_tile(sm.q[0]);
-    }
 
     // One step.  (Unrolling by the ring depth would turn the slot bases
     // into immediates, but makes this compiler spill role A's registers.)
@@ -468,11 +464,47 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
         ++hcur;
       }
     };
-    for (int u = 0; u < U; ++u) step(u);
-    if constexpr (!A) {
-      auto last = [&](const uint16_t* __restrict__ Qt) { tile_t_times<D, DT>(acc, Qt, pk, ta); };
-      if (U > 0) last(sm.q[(U - 1) & (NB - 1)]);
+    // A step with no work for this pair: its part in the ring's copies,
+    // wait and barrier.
+    auto idle = [&](int u) {
+      const int SL = u & (NB - 1);
+      wait_ring<PD - 2, NLOADS>(U - 1 - (u + 1));
+      lds_barrier();
+      if (u + PD < U) issue((SL + PD) & (NB - 1));
+      if (++it == qhi) {
+        it = qlo;
+        ++hcur;
+      }
+    };
+    // With equal heads the steps are one run of query tiles, and this
+    // pair's own steps [ulo, uhi) are those whose queries admit one of its
+    // keys; outside them (tiles the workgroup's band reaches for its other
+    // pairs) its P and dS would be exact zeros, so it idles there (the
+    // result is bit for bit the same).
+    int ulo = 0, uhi = U;
+    if (BAND && p.G == 1) {
+      int plo = qlo, phi = qhi;
+      if (p.wr >= 0) plo = max(plo, max(0, kw0 - p.wr) / kT);
+      if (p.wl >= 0) phi = min(phi, (kw0 + KW - 1 + p.wl) / kT + 1);
+      ulo = min(U, max(0, plo - it0));
+      uhi = max(ulo, min(U, phi - it0));
     }
+    int u = 0;
+    for (; u < ulo; ++u) idle(u);
+    if (u < uhi) {
+      if constexpr (A) {  // S of the first own step's tile
+        auto s_tile = [&](const uint16_t* __restrict__ Qt) { sd = rows_times_regs<D, DT>(Qt, kv, ta); };
+        s_tile(sm.q[u & (NB - 1)]);
+      }
+      for (; u < uhi; ++u) step(u);
+      // the previous-tile product of the last own step: B's dK (its slot is
+      // refilled only after the next step's barrier)
+      if constexpr (!A) {
+        auto last = [&](const uint16_t* __restrict__ Qt) { tile_t_times<D, DT>(acc, Qt, pk, ta); };
+        last(sm.q[(uhi - 1) & (NB - 1)]);
+      }
+    }
+    for (; u < U; ++u) idle(u);
 
     if (key < p.Nk) {
       if (p.S > 1) {  // fp32 partial row of dK (B) or dV (A), scaled by the reduction
@@ -655,13 +687,37 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
   }
   lds_barrier();
 
-  // S(jt0)^T and dP(jt0)^T - D: rows are keys j0 + acc_row(half, r), column this lane's query
-  f32x16 s, dp;
-  if (jt0 < n_kt) {
-    s = rows_times_regs<D, DT>(Ks[0], qf, ta);
-    dp = rows_times_regs<D, DT>(Vs[0], of, ta, dinit);
+  // This wave's own key tiles [wlo, whi): those one of its queries admits.
+  // Outside them (tiles the workgroup's band reaches for its other waves)
+  // the wave's dS would be exact zeros: it only takes its part in the
+  // ring's copies, waits and barriers (the result is bit for bit the same).
+  int wlo = jt0, whi = n_kt;
+  if constexpr (BAND) {
+    if (p.wl >= 0) wlo = max(wlo, max(0, qw0 - p.wl) / kT);
+    if (p.wr >= 0) whi = min(whi, (qw0 + QW - 1 + p.wr) / kT + 1);
+    whi = max(whi, wlo);
   }
-  for (int j = jt0; j < n_kt; ++j) {
+  auto idle = [&](int jj) {
+    const int sl = (jj - jt0) & 3;
+    if (jj + 3 < n_kt) {
+      issue(jj + 3, (sl + 3) & 3);
+      wait_vmcnt<2 * NI>();
+    } else {
+      wait_loads();
+    }
+    lds_barrier();
+  };
+  int j = jt0;
+  for (; j < wlo; ++j) idle(j);
+
+  // S(j)^T and dP(j)^T - D of the first own tile: rows are keys
+  // j0 + acc_row(half, r), column this lane's query
+  f32x16 s, dp;
+  if (j < whi) {
+    s = rows_times_regs<D, DT>(Ks[(j - jt0) & 3], qf, ta);
+    dp = rows_times_regs<D, DT>(Vs[(j - jt0) & 3], of, ta, dinit);
+  }
+  for (; j < whi; ++j) {
     const int j0 = j * kT;
     const int sl = (j - jt0) & 3;
     if (j + 3 < n_kt) issue(j + 3, (sl + 3) & 3);
@@ -725,6 +781,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
   }
+  for (; j < n_kt; ++j) idle(j);
 
   if constexpr (KSPLIT > 1) {
     // one barrier per step: pad the shorter runs to the longest
