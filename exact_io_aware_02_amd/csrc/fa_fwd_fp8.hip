@@ -561,8 +561,19 @@ __global__ __launch_bounds__(kT8) __attribute__((amdgpu_waves_per_eu(Fp8Cfg<D, P
         scores8<D>(ka, qf, sa);
       }
       auto wrap = [](int x) { return x >= NBUF ? x - NBUF : x; };
-      int sl = 0;  // slot of tile j
-      for (int j = jt0; j < n_kt; ++j) {
+      int j = jt0;
+      // Whole turns of the ring with every slot a constant, so the LDS
+      // addresses are immediate offsets (8 fewer VALU instructions per
+      // tile; 3% measured at 16K d = 128), then the rest one by one.
+      for (; j + NBUF <= n_kt; j += NBUF) {
+#pragma unroll
+        for (int r = 0; r < NBUF; ++r)
+          fwd8_step_phased<D, BAND>(j + r, n_kt, sa, sm.v[r], sm.k[(r + 1) % NBUF], sm.k[(r + NBUF - 1) % NBUF],
+                                    sm.v[(r + NBUF - 1) % NBUF], krs, vrs, krow, vrow, qf, acc, m, l, p.Nk, p.wl, p.wr,
+                                    qw0, c, lane, wave, ta);
+      }
+      int sl = (j - jt0) % NBUF;  // slot of tile j
+      for (; j < n_kt; ++j) {
         const int sp = wrap(sl + NBUF - 1);  // slot of tile j-1
         fwd8_step_phased<D, BAND>(j, n_kt, sa, sm.v[sl], sm.k[wrap(sl + 1)], sm.k[sp], sm.v[sp], krs, vrs, krow, vrow,
                                   qf, acc, m, l, p.Nk, p.wl, p.wr, qw0, c, lane, wave, ta);
