@@ -780,13 +780,29 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
 #pragma unroll
           for (int nb = 0; nb < kNQB; ++nb) sa[nb] = mfma32<DT>(a, qf[nb][ks], sa[nb]);
         }
-        for (; j < whi; ++j) {
+        auto one = [&]() {
           const int sp = wrap(sl + NBUF - 1);  // slot of tile j-1
           fwd_step_phased<D, DT, BAND, DROP, kNQB>(j, n_kt, sa, Vs[sl], Ks[wrap(sl + 1)], Ks[sp], Vs[sp], krs, vrs,
                                                    krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane,
                                                    wave, ta, p.drop, (uint32_t)bh);
           sl = wrap(sl + 1);
+        };
+        // Whole turns of the ring with every slot a constant (LDS addresses
+        // as immediate offsets; 0.6-0.9% at 16K causal d = 128), from the
+        // first step whose tile sits in slot 0.  With dropout the unrolled
+        // turn spills registers at d = 128, so it steps one by one.
+        if constexpr (!DROP) {
+          for (; j < whi && sl != 0; ++j) one();
+          for (; j + NBUF <= whi; j += NBUF) {
+#pragma unroll
+            for (int r = 0; r < NBUF; ++r)
+              fwd_step_phased<D, DT, BAND, DROP, kNQB>(j + r, n_kt, sa, Vs[r], Ks[(r + 1) % NBUF],
+                                                       Ks[(r + NBUF - 1) % NBUF], Vs[(r + NBUF - 1) % NBUF], krs, vrs,
+                                                       krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane,
+                                                       wave, ta, p.drop, (uint32_t)bh);
+          }
         }
+        for (; j < whi; ++j) one();
       }
       for (; j < n_kt; ++j) idle();
     }
