@@ -846,6 +846,25 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
                                            lane, wave, ta, p.drop, (uint32_t)bh);
       }
     }
+    // d = 64: whole turns of the 4-slot ring with constant slots (LDS
+    // addresses as immediates; 157 registers, three waves per SIMD still):
+    // B2 H8 N2048 29.3 -> 27.2 us, B2 H8 N512 -5%, others within +-1% or
+    // faster.
+    if constexpr (!kSep && !DROP) {
+      for (; j < n_kt && ((j - jt0) & 3) != 0; ++j) {
+        const int sl = (j - jt0) & 3;
+        fwd_step<D, DT, BAND, DROP, false>(j, n_kt, sa, sb, pf, va, Ks[sl], Ks[(sl + 1) & 3], Vs[sl], Ks[(sl + 3) & 3],
+                                           Vs[(sl + 3) & 3], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr,
+                                           qw0, c, lane, wave, ta, p.drop, (uint32_t)bh);
+      }
+      for (; j + 4 <= n_kt; j += 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          fwd_step<D, DT, BAND, DROP, false>(j + r, n_kt, sa, sb, pf, va, Ks[r], Ks[(r + 1) & 3], Vs[r], Ks[(r + 3) & 3],
+                                             Vs[(r + 3) & 3], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr,
+                                             qw0, c, lane, wave, ta, p.drop, (uint32_t)bh);
+      }
+    }
     for (; j < n_kt; ++j) {
       const int sl = (j - jt0) & 3;
       fwd_step<D, DT, BAND, DROP, false>(j, n_kt, sa, sb, pf, va, Ks[sl], Ks[(sl + 1) & 3], Vs[sl],
