@@ -1017,20 +1017,21 @@ float* bwd_lse2_region(void* workspace, int B, int H, int Nq) {
 // per CU), S the smallest divisor of G that gets there (else G), so each
 // run is whole query heads.  With equal heads (G = 1) a key block's query
 // tiles are cut into S = 2 runs when the grid has fewer dK/dV workgroups
-// than the chip has CUs and Nk >= kEqSplitMinKeys: the heaviest causal
-// block (all query tiles) is then the critical path, and dK/dV is issued
-// before dQ, so the runs take CUs that would idle.  Measured: B1 H2 N16384
-// d128 0.61 -> 0.55 ms, B1 H1 N16384 0.53 -> 0.36 ms, B1 H2 N8192 0.43 ->
-// 0.32 ms.  Grids that already give every CU a workgroup are not split:
-// at B2 H8 N2048 d64 (256 workgroups) four runs cost 30% (67 MB of partial
-// sums against a short critical path).
+// than the chip holds at once (one per CU at d = 128, two at d = 64) and
+// Nk >= kEqSplitMinKeys: the heaviest causal block (all query tiles) is
+// then the critical path, and dK/dV is issued before dQ, so the runs take
+// CUs that would idle.  Measured: B1 H2 N16384 d128 0.61 -> 0.55 ms, B1 H1
+// N16384 0.53 -> 0.36 ms, B1 H2 N8192 0.43 -> 0.32 ms, B1 H2 N16384 d64
+// 0.51 -> 0.42 ms, B1 H16 N2048 d64 -5%, B2 H8 N2048 d64 +-1%.  Four runs
+// at B2 H8 N2048 d64 cost 30% (67 MB of partial sums against a short
+// critical path).
 constexpr int kEqSplitMinKeys = 2048;
 int bwd_kv_splits(int B, int H, int H_kv, int Nk, int d) {
   if (H_kv <= 0 || H % H_kv != 0) return 1;
   const int G = H / H_kv;
   const int bnk = 32 * (d == 64 ? kDkvPairs<64> : kDkvPairs<128>);
   const int64_t base = (int64_t)((Nk + bnk - 1) / bnk) * B * H_kv;
-  if (G == 1) return base < kChipCUs && Nk >= kEqSplitMinKeys ? 2 : 1;
+  if (G == 1) return base < (int64_t)kChipCUs * (d == 64 ? 2 : 1) && Nk >= kEqSplitMinKeys ? 2 : 1;
   for (int S = 1; S < G; ++S)
     if (G % S == 0 && base * S >= 1024) return S;
   return G;

@@ -303,11 +303,16 @@ def test_ex_workspace_bytes():
     # ...two runs per key block when it does not (86 x 2 = 172 < 256 CUs)
     assert fa.fa_bwd_ex_workspace_bytes(1, 2, 2, 16384, 16384, 128, fa.FA_BF16) == \
         fa.fa_bwd_workspace_bytes(1, 2, 16384, 16384, 128, fa.FA_BF16) + 2 * 2 * 1 * 2 * 16384 * 128 * 4
-    # ...but not below 2048 keys, nor at 256 workgroups (B2 H8 N2048 d64: 16 x 16)
+    # ...at d = 64 below the 512 workgroups the chip holds (B2 H8 N2048: 16 x 16)...
+    assert fa.fa_bwd_ex_workspace_bytes(2, 8, 8, 2048, 2048, 64, fa.FA_FP16) == \
+        fa.fa_bwd_workspace_bytes(2, 8, 2048, 2048, 64, fa.FA_FP16) + 2 * 2 * 2 * 8 * 2048 * 64 * 4
+    # ...but not below 2048 keys, nor from a full chip on (d = 128: 256; d = 64: 512)
     assert fa.fa_bwd_ex_workspace_bytes(1, 2, 2, 1024, 1024, 128, fa.FA_BF16) == \
         fa.fa_bwd_workspace_bytes(1, 2, 1024, 1024, 128, fa.FA_BF16)
-    assert fa.fa_bwd_ex_workspace_bytes(2, 8, 8, 2048, 2048, 64, fa.FA_FP16) == \
-        fa.fa_bwd_workspace_bytes(2, 8, 2048, 2048, 64, fa.FA_FP16)
+    assert fa.fa_bwd_ex_workspace_bytes(1, 3, 3, 16384, 16384, 128, fa.FA_BF16) == \
+        fa.fa_bwd_workspace_bytes(1, 3, 16384, 16384, 128, fa.FA_BF16)
+    assert fa.fa_bwd_ex_workspace_bytes(1, 4, 4, 16384, 16384, 64, fa.FA_BF16) == \
+        fa.fa_bwd_workspace_bytes(1, 4, 16384, 16384, 64, fa.FA_BF16)
     # 16 query heads on 2 K/V heads at 16K, d = 128 (192 keys per dK/dV
     # workgroup): 86 key blocks x 2 = 172 workgroups, split 8 ways to reach 1024
     big = fa.fa_bwd_ex_workspace_bytes(1, 16, 2, 16384, 16384, 128, fa.FA_BF16)
