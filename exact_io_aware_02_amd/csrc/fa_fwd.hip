@@ -834,6 +834,31 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
     }
     int j = jt0 + 1;
     if constexpr (kSep) {
+      if constexpr (!DROP) {
+        // single steps (S(j+1) copied back) until tile j sits in slot 0,
+        // then whole turns of the ring with constant slots (LDS addresses
+        // as immediates), two swapped pairs per turn: -1 to -3% on grids of
+        // 512 blocks
+        for (; j < n_kt && ((j - jt0) & 3) != 0; ++j) {
+          const int sl = (j - jt0) & 3;
+          fwd_step<D, DT, BAND, DROP, false>(j, n_kt, sa, sb, pf, va, Ks[sl], Ks[(sl + 1) & 3], Vs[sl], Ks[sl],
+                                             Vs[(sl + 3) & 3], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl,
+                                             p.wr, qw0, c, lane, wave, ta, p.drop, (uint32_t)bh);
+#pragma unroll
+          for (int nb = 0; nb < kNQB; ++nb) sa[nb] = sb[nb];
+        }
+        for (; j + 3 < n_kt; j += 4) {
+#pragma unroll
+          for (int r = 0; r < 4; r += 2) {
+            fwd_step<D, DT, BAND, DROP, false>(j + r, n_kt, sa, sb, pf, va, Ks[r], Ks[r + 1], Vs[r], Ks[r],
+                                               Vs[(r + 3) & 3], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl,
+                                               p.wr, qw0, c, lane, wave, ta, p.drop, (uint32_t)bh);
+            fwd_step<D, DT, BAND, DROP, false>(j + r + 1, n_kt, sb, sa, pf, va, Ks[r + 1], Ks[(r + 2) & 3], Vs[r + 1],
+                                               Ks[r + 1], Vs[r], krs, vrs, krow, vrow, ktb, vtb, qf, acc, st, p.Nk,
+                                               p.wl, p.wr, qw0, c, lane, wave, ta, p.drop, (uint32_t)bh);
+          }
+        }
+      }
       // two steps per iteration with the roles of sa and sb swapped, so
       // S(j+1) is not copied back every step
       for (; j + 1 < n_kt; j += 2) {
