@@ -1150,13 +1150,17 @@ hipError_t launch_dc(const FwdParams& p, bool banded, hipStream_t stream) {
 // The partial results cost a merge kernel (~10 us for ~20 MB of them), so
 // the plan is kept only when its longest chunk is at least
 // kChunkMinSaving tiles shorter than the critical path without it (the
-// intra-workgroup split's run where that applies).  Planned for the
-// MI355X's 256 CUs (a fixed number, so the workspace size depends on the
-// sizes alone).
+// intra-workgroup split's run where that applies), or kChunkMinSaving2
+// when the grid already gives every CU a workgroup and a second one to
+// some: there the unsplit blocks already share the CUs about evenly, and
+// chunks paid only on long rows (B1 H4 N16384 d128: -5%; B1 H16 N4096 d128:
+// +3% with 32).  Planned for the MI355X's 256 CUs (a fixed number, so the
+// workspace size depends on the sizes alone).
 constexpr int kChipCUs = 256;
 constexpr int kSplitMaxBlocks = 2 * kChipCUs;
 constexpr int kMinChunkTiles = 8;
 constexpr int kChunkMinSaving = 32;
+constexpr int kChunkMinSaving2 = 96;
 
 }  // namespace
 
@@ -1195,7 +1199,7 @@ FwdSplitPlan fwd_split_plan(int B, int H, int Nq, int Nk, int d, int wl, int wr)
   const int unsplit = n_qt * BH <= kChipCUs && most >= kKSplitMinTiles
                           ? (most + (d == 64 ? kKSplit<64> : kKSplit<128>) - 1) / (d == 64 ? kKSplit<64> : kKSplit<128>)
                           : most;
-  if (chunk + kChunkMinSaving > unsplit) return pl;
+  if (chunk + (n_qt * BH <= kChipCUs ? kChunkMinSaving : kChunkMinSaving2) > unsplit) return pl;
   int n_chunks = 0, n_split = 0, P = 0;
   for (int x : tiles) {
     const int sb = block_chunks(x, chunk);

@@ -352,10 +352,10 @@ def _plan_model(B, H, Nq, Nk, d, causal, wl=-1, wr=-1):
     S = floor(F * 256 / (B H)) the resident workgroups per head (F = 4 at
     d = 64, else 3), the chunk length starts at max(8, ceil(W / S)) and
     grows by max(1, chunk // 32) while the chunks exceed S and it is below
-    the longest block; the plan is dropped unless chunk + 32 <= the
-    unsplit critical path (the longest block's tiles divided by 3,
-    rounded up, when the grid has at most 256 blocks and that block 32+
-    tiles); a block of n tiles has
+    the longest block; the plan is dropped unless chunk + 32 (chunk + 96
+    with more than 256 blocks) <= the unsplit critical path (the longest
+    block's tiles divided by 3, rounded up, when the grid has at most 256
+    blocks and that block 32+ tiles); a block of n tiles has
     ceil(n / chunk) chunks (1 if n = 0); the workspace holds
     (d + 2) * 128 floats per chunk of a block with two or more."""
     wl = -1 if wl < 0 or wl >= Nq else wl
@@ -381,7 +381,7 @@ def _plan_model(B, H, Nq, Nk, d, causal, wl=-1, wr=-1):
     most = max(tiles)
     ks = 3
     unsplit = -(-most // ks) if n_qt * B * H <= 256 and most >= 32 else most
-    if chunk + 32 > unsplit:
+    if chunk + (32 if n_qt * B * H <= 256 else 96) > unsplit:
         return 0
     P = sum(c for c in (max(1, -(-n // chunk)) for n in tiles) if c > 1)
     return 0 if P == 0 else -(-(B * H * P * 128 * (d + 2) * 4) // 256) * 256
@@ -396,6 +396,9 @@ def _plan_model(B, H, Nq, Nk, d, causal, wl=-1, wr=-1):
     (1, 16, 16384, 16384, 128, 1, -1, -1),  # 2048 blocks: fills the chip
     (1, 4, 3000, 2000, 128, 0, 300, 40),    # a window (rows past 2040 admit no key)
     (3, 1, 5000, 7000, 64, 1, -1, -1),
+    (1, 4, 16384, 16384, 128, 1, -1, -1),   # 512 blocks, long rows: chunks kept
+    (1, 16, 4096, 4096, 128, 1, -1, -1),    # 512 blocks, short rows: dropped
+    (1, 8, 8192, 8192, 128, 1, -1, -1),
 ])
 def test_fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, causal, wl, wr):
     assert fa.fa_fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, causal, (wl, wr)) == \
@@ -411,6 +414,9 @@ def test_fwd_splitk_workspace_examples():
     assert fa.fa_fwd_splitk_workspace_bytes(1, 2, 16384, 16384, 128, 1) > 0
     assert fa.fa_fwd_splitk_workspace_bytes(1, 16, 16384, 16384, 128, 1) == 0
     assert fa.fa_fwd_splitk_workspace_bytes(1, 1, 1, 1, 96, 0) == 0
+    # 512 blocks (two per CU for some): chunks only for long rows
+    assert fa.fa_fwd_splitk_workspace_bytes(1, 4, 16384, 16384, 128, 1) > 0
+    assert fa.fa_fwd_splitk_workspace_bytes(1, 16, 4096, 4096, 128, 1) == 0
 
 
 S = 1 << 30  # fake addresses far enough apart for tensors of up to 1 GiB
