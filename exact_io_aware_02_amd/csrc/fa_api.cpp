@@ -93,6 +93,43 @@ int check_tensor(const char* name, const void* ptr, const int64_t st[3], int B, 
   return FA_OK;
 }
 
+// An output's distinct (b, h, row, column) elements must sit at distinct
+// addresses, or the workgroups that write them race.  Taking the dimensions
+// of size > 1 in increasing stride order (the contiguous d first), each
+// stride must clear the span of the dimensions inside it.  Every dense or
+// row-padded layout (BHSD, BSHD) passes; a zero stride or two dimensions
+// sharing a stride do not.  Runs after check_tensor, so the spans fit int64.
+int check_output_layout(const char* name, const int64_t st[3], int B, int H, int N, int d) {
+  if (N == 0) return FA_OK;
+  int64_t dims[3][2] = {{st[0], B}, {st[1], H}, {st[2], N}};
+  for (int i = 1; i < 3; ++i)  // insertion sort by stride
+    for (int j = i; j > 0 && dims[j][0] < dims[j - 1][0]; --j)
+      for (int f = 0; f < 2; ++f) {
+        const int64_t t = dims[j][f];
+        dims[j][f] = dims[j - 1][f];
+        dims[j - 1][f] = t;
+      }
+  int64_t span = d;
+  for (int i = 0; i < 3; ++i) {
+    if (dims[i][1] <= 1) continue;
+    if (dims[i][0] < span)
+      return fail(FA_ERR_INVALID_ARG, "%s: strides {%lld, %lld, %lld} put distinct elements at one address", name,
+                  (long long)st[0], (long long)st[1], (long long)st[2]);
+    span += (dims[i][1] - 1) * dims[i][0];
+  }
+  return FA_OK;
+}
+
+// Rows in all (b, h) slices together; far below this every byte count the
+// library forms (tensor extents, LSE, workspaces) fits in 64 bits.
+constexpr int64_t kMaxTotalRows = (int64_t)1 << 48;
+
+bool rows_fit(int B, int H, int Nq, int Nk) {
+  const int64_t bh = (int64_t)B * H;  // both < 2^31: no overflow
+  if (bh > 0x7fffffffLL) return false;
+  return bh * (Nq > Nk ? Nq : Nk) <= kMaxTotalRows;
+}
+
 bool overlaps(const void* a, const Extent& ea, const void* b, const Extent& eb) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
   const uintptr_t a1 = a0 + (uintptr_t)ea.hi_bytes, b1 = b0 + (uintptr_t)eb.hi_bytes;
@@ -109,6 +146,7 @@ int check_common(int B, int H, int Nq, int Nk, int d, float scale, int causal, i
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
   if (Nq > 0 && B > 0 && H > 0 && Nk < 1) return fail(FA_ERR_INVALID_ARG, "Nk must be >= 1 when there are queries");
   if ((int64_t)B * H > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "B*H overflows");
+  if (!rows_fit(B, H, Nq, Nk)) return fail(FA_ERR_INVALID_ARG, "B*H*max(Nq, Nk) exceeds 2^48 rows");
   return FA_OK;
 }
 
@@ -204,6 +242,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   if ((st = check_tensor("k", k, k_strides, B, H_kv, Nk, d, &ek))) return st;
   if ((st = check_tensor("v", v, v_strides, B, H_kv, Nk, d, &ev))) return st;
   if ((st = check_tensor("o", o, o_strides, B, H, Nq, d, &eo))) return st;
+  if ((st = check_output_layout("o", o_strides, B, H, Nq, d))) return st;
   if (!lse) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   Extent el{0, (int64_t)B * H * Nq * 4};
@@ -276,6 +315,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 size_t fa_fwd_splitk_workspace_bytes(int B, int H, int Nq, int Nk, int d, int causal, int window_left,
                                      int window_right) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || (d != 64 && d != 128) || (causal != 0 && causal != 1)) return 0;
+  if (!rows_fit(B, H, Nq, Nk)) return 0;
   const Band band = make_band(causal, window_left, window_right, Nq, Nk);
   return fa::fwd_splitk_workspace_bytes(B, H, Nq, Nk, d, band.wl, band.wr);
 }
@@ -325,6 +365,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   if ((st = check_tensor("k", k, k_strides, B, H_kv, Nk, d, &ek, 1))) return st;
   if ((st = check_tensor("v", v, v_strides, B, H_kv, Nk, d, &ev, 1))) return st;
   if ((st = check_tensor("o", o, o_strides, B, H, Nq, d, &eo))) return st;
+  if ((st = check_output_layout("o", o_strides, B, H, Nq, d))) return st;
   if (!lse) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   Extent el{0, (int64_t)B * H * Nq * 4};
@@ -363,11 +404,13 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_bwd_ex_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d, int dtype) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || (d != 64 && d != 128) || (dtype != FA_FP16 && dtype != FA_BF16)) return 0;
   if (H > 0 && (H_kv < 1 || H % H_kv != 0)) return 0;
+  if (!rows_fit(B, H, Nq, Nk)) return 0;
   return fa::bwd_split_workspace_bytes(B, H, H > 0 ? H_kv : 1, Nq, Nk, d);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || (d != 64 && d != 128) || (dtype != FA_FP16 && dtype != FA_BF16)) return 0;
+  if (!rows_fit(B, H, Nq, Nk)) return 0;
   return fa::bwd_workspace_bytes(B, H, Nq);
 }
 
@@ -406,6 +449,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   if ((st = check_tensor("dq", dq, dq_strides, B, H, Nq, d, &edq))) return st;
   if ((st = check_tensor("dk", dk, dk_strides, B, H_kv, Nk, d, &edk))) return st;
   if ((st = check_tensor("dv", dv, dv_strides, B, H_kv, Nk, d, &edv))) return st;
+  if ((st = check_output_layout("dq", dq_strides, B, H, Nq, d))) return st;
+  if ((st = check_output_layout("dk", dk_strides, B, H_kv, Nk, d))) return st;
+  if ((st = check_output_layout("dv", dv_strides, B, H_kv, Nk, d))) return st;
   if (Nq > 0 && !lse) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   const size_t need = fa_bwd_workspace_bytes(B, H, Nq, Nk, d, dtype);

@@ -51,6 +51,12 @@
  *    8 elements (16 for fa_fwd_fp8's byte tensors); element offsets within
  *    one (b, h) slice must fit in 31 bits (offsets across batches and heads
  *    are 64-bit).  O must not alias Q, K or V; dQ/dK/dV must not alias any input.
+ *    An output's strides must give its distinct elements distinct addresses:
+ *    with its dimensions of size > 1 in increasing stride order, each stride
+ *    at least the span of the dimensions inside it (dense and row-padded
+ *    BHSD/BSHD pass; a zero stride is for inputs only).
+ *  - B * H * max(Nq, Nk) must not exceed 2^48 rows (the workspace-size
+ *    queries return 0 beyond it).
  *  - Return value: FA_OK (0) or an fa_status code.  Arguments are checked
  *    before any HIP call; on error nothing is enqueued.  A thread-local
  *    human-readable detail is available from fa_last_error_message().

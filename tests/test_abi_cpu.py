@@ -126,6 +126,76 @@ def test_fwd_strided_rejects_bad_strides():
     assert fwd_strided(huge) == fa.FA_ERR_INVALID_ARG  # per-head extent > 2^31 elements
 
 
+BH2 = dict(B=2, H=2, Nq=16, Nk=16)
+DENSE = (2 * 16 * 64, 16 * 64, 64)   # BHSD, B=H=2, N=16, d=64
+BSHD = (16 * 2 * 64, 64, 2 * 64)
+
+
+@pytest.mark.parametrize("o_st", [
+    (0, 16 * 64, 64),          # every batch on one slice
+    (2 * 16 * 64, 0, 64),      # every head on one slice
+    (16 * 64, 16 * 64, 64),    # batch and head share a stride
+    (2 * 16 * 64, 512, 64),    # head slices interleave with rows
+    (64, 192, 128),            # [N][H][B] order, but the head stride lands inside the rows
+])
+def test_fwd_rejects_self_overlapping_output(o_st):
+    """Two (b, h, row) elements of o at one address would be written by two
+    workgroups; only inputs may broadcast with such strides."""
+    assert fwd_strided([DENSE] * 3 + [o_st], **BH2) == fa.FA_ERR_INVALID_ARG
+    assert "one address" in fa.fa_last_error_message()
+
+
+@pytest.mark.parametrize("q_st", [(0, 16 * 64, 64), (0, 0, 64), (16 * 64, 16 * 64, 64)])
+def test_fwd_inputs_may_broadcast(q_st):
+    """A zero or shared stride is fine on an input: the call gets past
+    validation (the device check fails here, or on a GPU machine it runs)."""
+    if _gpu_visible():
+        pytest.skip("a valid call would run on the device")
+    assert fwd_strided([q_st, DENSE, DENSE, DENSE], **BH2) == fa.FA_ERR_DEVICE
+
+
+@pytest.mark.parametrize("o_st", [DENSE, BSHD, (4 * 16 * 64, 2 * 16 * 64, 128)])  # dense, BSHD, padded
+def test_fwd_accepts_non_overlapping_outputs(o_st):
+    if _gpu_visible():
+        pytest.skip("a valid call would run on the device")
+    assert fwd_strided([DENSE] * 3 + [o_st], **BH2) == fa.FA_ERR_DEVICE
+
+
+def bwd_strided(out_st, ws_bytes=1 << 16):
+    lib = fa.load_library()
+    I3 = ctypes.c_int64 * 3
+    st = [I3(*DENSE)] * 5 + [I3(*x) for x in out_st]
+    return lib.fa_bwd_strided(P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), P(6 * A), P(7 * A), P(8 * A), P(9 * A),
+                              2, 2, 16, 16, 64, 0.125, 1, 0, *st, P(10 * A), ws_bytes, None)
+
+
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_bwd_rejects_self_overlapping_gradient(which):
+    out = [DENSE] * 3
+    out[which] = (2 * 16 * 64, 0, 64)
+    assert bwd_strided(out) == fa.FA_ERR_INVALID_ARG
+    assert ("dq", "dk", "dv")[which] + ": strides" in fa.fa_last_error_message()
+
+
+def test_bwd_accepts_bshd_gradients():
+    if _gpu_visible():
+        pytest.skip("a valid call would run on the device")
+    assert bwd_strided([BSHD] * 3) == fa.FA_ERR_DEVICE
+
+
+def test_sizes_beyond_the_row_bound_are_rejected():
+    """B*H*max(Nq, Nk) above 2^48 rows: every byte count stays far from
+    64-bit overflow (the LSE and workspaces are B*H*N-sized)."""
+    B, H, N = 1 << 20, 1 << 10, 1 << 20           # 2^50 rows
+    assert fwd(q=0, k=0, v=0, o=0, lse=0, B=B, H=H, Nq=N, Nk=N) == fa.FA_ERR_INVALID_ARG
+    assert "2^48" in fa.fa_last_error_message()
+    assert fa.fa_bwd_workspace_bytes(B, H, N, N, 64, 0) == 0
+    assert fa.fa_bwd_ex_workspace_bytes(B, H, H, N, N, 64, 0) == 0
+    assert fa.fa_fwd_splitk_workspace_bytes(B, H, N, N, 64, 1) == 0
+    # at the bound itself the queries still answer
+    assert fa.fa_bwd_workspace_bytes(1 << 17, 1 << 10, 1 << 21, 1, 64, 0) == 2 * (1 << 48) * 4
+
+
 # --- backward validation ------------------------------------------------------
 
 def bwd(ws=10 * A, ws_bytes=1 << 16, dq=7 * A, dk=8 * A, dv=9 * A, d=64, Nq=16, Nk=16, dtype=0):
