@@ -365,6 +365,12 @@ def test_python_fp8_binding_checks_dtypes():
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
 
 
+def split_extra(S, B, Hkv, Nk, d):
+    """Bytes the split dK/dV stage adds to the workspace: S fp32 partial
+    sums of dK and of dV."""
+    return 2 * S * B * Hkv * Nk * d * 4
+
+
 def test_ex_workspace_bytes():
     base = fa.fa_bwd_workspace_bytes(1, 16, 16384, 16384, 128, fa.FA_BF16)
     # equal heads: nothing extra when the dK/dV grid gives every CU a
@@ -372,10 +378,10 @@ def test_ex_workspace_bytes():
     assert fa.fa_bwd_ex_workspace_bytes(1, 16, 16, 16384, 16384, 128, fa.FA_BF16) == base
     # ...two runs per key block when it does not (86 x 2 = 172 < 256 CUs)
     assert fa.fa_bwd_ex_workspace_bytes(1, 2, 2, 16384, 16384, 128, fa.FA_BF16) == \
-        fa.fa_bwd_workspace_bytes(1, 2, 16384, 16384, 128, fa.FA_BF16) + 2 * 2 * 1 * 2 * 16384 * 128 * 4
+        fa.fa_bwd_workspace_bytes(1, 2, 16384, 16384, 128, fa.FA_BF16) + split_extra(2, 1, 2, 16384, 128)
     # ...at d = 64 below the 512 workgroups the chip holds (B2 H8 N2048: 16 x 16)...
     assert fa.fa_bwd_ex_workspace_bytes(2, 8, 8, 2048, 2048, 64, fa.FA_FP16) == \
-        fa.fa_bwd_workspace_bytes(2, 8, 2048, 2048, 64, fa.FA_FP16) + 2 * 2 * 2 * 8 * 2048 * 64 * 4
+        fa.fa_bwd_workspace_bytes(2, 8, 2048, 2048, 64, fa.FA_FP16) + split_extra(2, 2, 8, 2048, 64)
     # ...but not below 2048 keys, nor from a full chip on (d = 128: 256; d = 64: 512)
     assert fa.fa_bwd_ex_workspace_bytes(1, 2, 2, 1024, 1024, 128, fa.FA_BF16) == \
         fa.fa_bwd_workspace_bytes(1, 2, 1024, 1024, 128, fa.FA_BF16)
@@ -386,11 +392,11 @@ def test_ex_workspace_bytes():
     # 16 query heads on 2 K/V heads at 16K, d = 128 (192 keys per dK/dV
     # workgroup): 86 key blocks x 2 = 172 workgroups, split 8 ways to reach 1024
     big = fa.fa_bwd_ex_workspace_bytes(1, 16, 2, 16384, 16384, 128, fa.FA_BF16)
-    assert big == base + 2 * 8 * 1 * 2 * 16384 * 128 * 4
+    assert big == base + split_extra(8, 1, 2, 16384, 128)
     # d = 64 (128 keys per workgroup): 128 x 2 = 256 workgroups, split 4 ways
     base64 = fa.fa_bwd_workspace_bytes(1, 16, 16384, 16384, 64, fa.FA_BF16)
     assert fa.fa_bwd_ex_workspace_bytes(1, 16, 2, 16384, 16384, 64, fa.FA_BF16) == \
-        base64 + 2 * 4 * 1 * 2 * 16384 * 64 * 4
+        base64 + split_extra(4, 1, 2, 16384, 64)
     # a problem that already fills the chip is not split
     assert fa.fa_bwd_ex_workspace_bytes(8, 64, 8, 16384, 16384, 128, fa.FA_BF16) == \
         fa.fa_bwd_workspace_bytes(8, 64, 16384, 16384, 128, fa.FA_BF16)

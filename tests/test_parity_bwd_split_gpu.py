@@ -80,15 +80,34 @@ def test_split_backward(case):
     s = 1.0 / math.sqrt(d)
     w = window if window is not None else (-1, -1)
     o, lse = fa.attention_fwd(q, k, v, causal=causal, scale=s, layout=layout, window=window, dropout=dr)
+    grads = lambda: [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]  # noqa: E731
     outs = []
-    for nbytes in (big, big, small):
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
-        g = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    # a zeroed workspace, one of all-ones bytes (NaN partial sums, counters
+    # at 2^32 - 1: the library must zero its counters and read only this
+    # call's sums), and the statistics-only size (no split)
+    for nbytes, fill in ((big, 0), (big, 0xFF), (small, 0)):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        g = grads()
         fa.fa_bwd_ex(q, k, v, o, lse, do, *g, s, causal, ws, w, fa.FA_BWD_ALL, layout, None, dr)
         outs.append(g)
+    # the stages as three calls on an all-ones workspace (dK/dV without the
+    # statistics stage zeroes the counters itself), then the whole backward
+    # again on that workspace with another dO: equal to a fresh call with it
+    ws = torch.full((big,), 0xFF, dtype=torch.uint8, device=DEV)
+    g = grads()
+    for stage in (fa.FA_BWD_PREP, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
+        fa.fa_bwd_ex(q, k, v, o, lse, do, *g, s, causal, ws, w, stage, layout, None, dr)
+    do2 = torch.flip(do, dims=(0,)).contiguous() * 0.5
+    g2, g2_fresh = grads(), grads()
+    fa.fa_bwd_ex(q, k, v, o, lse, do2, *g2, s, causal, ws, w, fa.FA_BWD_ALL, layout, None, dr)
+    fa.fa_bwd_ex(q, k, v, o, lse, do2, *g2_fresh, s, causal, torch.zeros(big, dtype=torch.uint8, device=DEV), w,
+                 fa.FA_BWD_ALL, layout, None, dr)
     torch.cuda.synchronize()
-    for a, b in zip(outs[0], outs[1]):
-        assert torch.equal(a, b), "run to run"
+    for a, b, c in zip(outs[0], outs[1], g):
+        assert torch.equal(a, b), "run to run (all-ones workspace)"
+        assert torch.equal(a, c), "stages as separate calls"
+    for a, b in zip(g2, g2_fresh):
+        assert torch.equal(a, b), "a second call on the same workspace"
     args = [to_bhsd64(inp[x], layout) for x in ("q", "k", "v", "do")]
     refs = attention_bwd64(*args, s, causal, window=w, dropout=dr)
     for tag, g in (("split", outs[0]), ("unsplit dK/dV", outs[2])):
