@@ -196,3 +196,36 @@ def test_fp8_fwd_phased_schedule(case):
     for r in range(1, R):
         assert torch.equal(o[r * B:(r + 1) * B].view(torch.int16), o[:B].view(torch.int16)), r
         assert torch.equal(lse[r * B:(r + 1) * B], lse[:B]), r
+
+
+@pytest.mark.parametrize("shape", ["interleaved", "phased"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_rising_scores(d, shape):
+    """Keys scaled by 1 + 3 j / N along the sequence (then rounded to
+    e4m3fn, the bytes both sides get) and a scale of 2 / sqrt(d): under the
+    causal mask a row's running maximum rises on almost every 64-key tile,
+    so the lazy rescale's slow path runs in both schedules (the phased one
+    from 768 / 1536 workgroups, reached by copies along the batch); against
+    the oracle under the rounding model, copies bitwise equal."""
+    B, H, N = 1, 2, 320
+    blocks = math.ceil(N / 128) * B * H
+    R = 1 if shape == "interleaved" else math.ceil({64: 1536, 128: 768}[d] / blocks)
+    say("case fp8 rising scores d=%d %s (%d copies)" % (d, shape, R))
+    inp = make_qkv(B, H, N, N, d, "fp8", "bhsd", seed=97)
+    ramp = 1.0 + 3.0 * torch.arange(N, dtype=torch.float32) / N
+    k = (inp["k"].float() * ramp[None, None, :, None]).to(torch.float8_e4m3fn)
+    q, v = inp["q"], inp["v"]
+    rep = [x.view(torch.uint8).repeat(R, 1, 1, 1).view(torch.float8_e4m3fn).to(DEV) for x in (q, k, v)]
+    scale = 2.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd_fp8(*rep, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    q8, k8, v8 = (fp8_bytes(x) for x in (q, k, v))
+    o_ref, lse_ref = attention_fp8_fwd64(q8, k8, v8, scale, True)
+    rows = np.tile(np.arange(N), (B, H, 1))
+    bound, sigma = fp8_rounding_model(q8, k8, v8, scale, True, rows)
+    check("rising d%d %s" % (d, shape), to_bhsd64(o[:B]), lse[:B].numpy().astype(np.float64), o_ref, lse_ref,
+          bound, sigma)
+    for r in range(1, R):
+        assert torch.equal(o[r * B:(r + 1) * B].view(torch.int16), o[:B].view(torch.int16)), r
+        assert torch.equal(lse[r * B:(r + 1) * B], lse[:B]), r
