@@ -38,7 +38,8 @@ class Workload:
         return "Workload(%s)" % self.name
 
 
-# The five problems from the benchmark spec, named by what they are.
+# The five named workloads (the small-to-long-context shapes of the parity
+# tests and the benchmark), each named by what it is.
 WORKLOADS = {
     w.name: w
     for w in [

@@ -1,6 +1,8 @@
 import os
 import sys
+import zlib
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -28,3 +30,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _rng_per_test(request):
+    """A test module's ``RNG`` (the oracle pins draw their inputs from one)
+    is reseeded from the test's own id before each test, so the inputs do
+    not depend on which tests ran before it in the same process (as they
+    would when tests are spread over several worker processes)."""
+    mod = request.module
+    if isinstance(getattr(mod, "RNG", None), np.random.Generator):
+        mod.RNG = np.random.default_rng(zlib.crc32(request.node.nodeid.split("::", 1)[-1].encode()))

@@ -148,7 +148,7 @@ def test_fwd_rejects_self_overlapping_output(o_st):
 @pytest.mark.parametrize("q_st", [(0, 16 * 64, 64), (0, 0, 64), (16 * 64, 16 * 64, 64)])
 def test_fwd_inputs_may_broadcast(q_st):
     """A zero or shared stride is fine on an input: the call gets past
-    validation (the device check fails here, or on a GPU machine it runs)."""
+    validation (the device check fails where no device exists)."""
     if _gpu_visible():
         pytest.skip("a valid call would run on the device")
     assert fwd_strided([q_st, DENSE, DENSE, DENSE], **BH2) == fa.FA_ERR_DEVICE

@@ -13,7 +13,7 @@ import torch
 
 from oracle import attention_bwd64, attention_fwd64, dropout_keep, dropout_threshold, philox4x32_10
 
-RNG = np.random.default_rng(2468)
+RNG = np.random.default_rng(2468)  # reseeded per test (tests/conftest.py)
 M32 = 0xFFFFFFFF
 
 

@@ -16,7 +16,7 @@ import torch
 
 from oracle import attention_bwd64, attention_fwd64, attention_rows_fwd64
 
-RNG = np.random.default_rng(4321)
+RNG = np.random.default_rng(4321)  # reseeded per test (tests/conftest.py)
 
 
 def rand(*shape):

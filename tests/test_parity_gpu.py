@@ -1,6 +1,6 @@
 """GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
 
-Tolerances (stated in the task's target and used unchanged here):
+Tolerances (the parity bounds for these shapes, used unchanged here):
   O      max |gpu - oracle| <= 2e-3 (fp16), 1.6e-2 (bf16)
   LSE    max |gpu - oracle| <= 1e-3
   dQ/dK/dV  ||gpu - oracle||_F / ||oracle||_F <= 2e-2 per tensor
