@@ -1,11 +1,12 @@
 """The oracle's pins catch plausible mistakes in it (CPU).
 
-Each mutant below is a copy of one oracle function with one plausible
-mistake planted (the oracle itself is untouched: the copy is swapped in for
-the duration of one test).  Every pin of ``tests/test_oracle_pins.py`` is
-then run against the mutated oracle; at least one must fail.  A control
-run with the unmodified oracle must pass them all, which checks this
-harness itself.
+Each mutant below is a copy of one or two oracle functions with one
+plausible mistake planted (the oracle itself is untouched: the copies are
+swapped in for the duration of one test).  Every pin of the pin module the
+mistake concerns (``tests/test_oracle_pins.py``, ``..._gqa_window.py``,
+``..._dropout.py``) is then run against the mutated oracle; at least one
+must fail.  A control run of each module with the unmodified oracle must
+pass them all, which checks this harness itself.
 """
 import importlib
 import zlib
@@ -16,9 +17,13 @@ import pytest
 import oracle.attention as oa
 
 
-def _pins():
-    """(name, callable) for every pin, parametrizations written out."""
-    pins = importlib.import_module("tests.test_oracle_pins")
+PIN_MODULES = ("tests.test_oracle_pins", "tests.test_oracle_pins_gqa_window", "tests.test_oracle_pins_dropout")
+
+
+def _pins(module):
+    """(name, callable, kwargs) for every pin of ``module``, its
+    parametrizations written out."""
+    pins = importlib.import_module(module)
     out = []
     for name in sorted(dir(pins)):
         fn = getattr(pins, name)
@@ -39,9 +44,9 @@ def _pins():
     return pins, out
 
 
-def _run_pins():
-    """Names of the pins that fail (assertion or any error)."""
-    pins, cases = _pins()
+def _run_pins(module):
+    """Names of the pins of ``module`` that fail (assertion or any error)."""
+    pins, cases = _pins(module)
     failed = []
     for label, fn, kwargs in cases:
         pins.RNG = np.random.default_rng(zlib.crc32(label.encode()))
@@ -102,6 +107,7 @@ def _bwd_mutant(kind):
     def bwd(q, k, v, do, scale, causal, window=(-1, -1), dropout=None):
         q, k, v, do = oa._as64(q), oa._as64(k), oa._as64(v), oa._as64(do)
         B, H, Nq, d, G = oa._check(q, k, v)
+        Hkv = H // G
         scale = float(scale)
         dq = np.empty_like(q)
         dk = np.zeros_like(k)
@@ -109,45 +115,140 @@ def _bwd_mutant(kind):
         rows = np.arange(Nq)
         for b in range(B):
             for h in range(H):
-                qq, kk, vv, g = q[b, h], k[b, h // G], v[b, h // G], do[b, h]
+                hk = h % Hkv if kind == "head_map" else h // G
+                qq, kk, vv, g = q[b, h], k[b, hk], v[b, hk], do[b, h]
                 p, _ = oa._softmax_rows(oa._scores(qq, kk, scale, causal, rows, window))
                 wgt = oa._dropped(p, b, h, H, rows, dropout)
-                dv[b, h // G] += (wgt @ g) if kind == "dv_p_not_pt" else (wgt.T @ g)
+                dvv = (wgt @ g) if kind == "dv_p_not_pt" else ((p if kind == "dv_no_mask" else wgt).T @ g)
                 dp = g @ vv.T
                 axis = 0 if kind == "ds_wrong_axis" else 1
                 ds = p * (oa._dropped(dp, b, h, H, rows, dropout) - np.sum(wgt * dp, axis=axis, keepdims=True))
                 dq[b, h] = (ds @ kk) if kind == "dq_no_scale" else scale * (ds @ kk)
                 dkk = scale * (ds.T @ qq)
-                dk[b, h // G] += dkk * (1 + 1e-6) if kind == "dk_perturbed" else dkk
+                if kind == "dk_perturbed":
+                    dkk = dkk * (1 + 1e-6)
+                if kind == "group_overwritten":
+                    dk[b, hk], dv[b, hk] = dkk, dvv
+                else:
+                    dk[b, hk] += dkk
+                    dv[b, hk] += dvv
         return dq, dk, dv
     return bwd
 
 
+def _fwd_head_map_mod(q, k, v, scale, causal, window=(-1, -1), dropout=None):
+    q, k, v = oa._as64(q), oa._as64(k), oa._as64(v)
+    B, H, Nq, d, G = oa._check(q, k, v)
+    Hkv = H // G
+    o = np.empty((B, H, Nq, d))
+    lse = np.empty((B, H, Nq))
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(H):
+            hk = h % Hkv  # planted: query head h reads K/V head h mod H_kv, not h / G
+            p, lse[b, h] = oa._softmax_rows(oa._scores(q[b, h], k[b, hk], float(scale), causal, rows, window))
+            o[b, h] = oa._dropped(p, b, h, H, rows, dropout) @ v[b, hk]
+    return o, lse
+
+
+def _allowed_window_edge(which):
+    def allowed(rows, nk, causal, window):
+        left, right = int(window[0]), int(window[1])
+        keys = np.arange(nk)[None, :]
+        i = np.asarray(rows)[:, None]
+        ok = np.ones((len(rows), nk), dtype=bool)
+        if causal:
+            ok &= keys <= i
+        if left >= 0:
+            ok &= (keys > i - left) if which == "left" else (keys >= i - left)  # planted for "left"
+        if right >= 0:
+            ok &= (keys < i + right) if which == "right" else (keys <= i + right)  # planted for "right"
+        return ok
+    return allowed
+
+
+def _keep_mutant(kind):
+    def keep(b, h, H, rows, nk, p, seed, offset):
+        thr, _ = oa.dropout_threshold(p)
+        i = np.asarray(rows, dtype=np.uint64)[:, None]
+        j = np.arange(nk, dtype=np.uint64)[None, :]
+        ctr = np.stack(np.broadcast_arrays((j >> np.uint64(5)) * np.uint64(2) + ((j >> np.uint64(2)) & np.uint64(1)),
+                                           i, np.uint64(b * H + h), np.uint64(offset)), axis=-1)
+        seed = int(seed)
+        key = (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+        if kind == "seed_halves_swapped":
+            key = key[::-1]
+        w = oa.philox4x32_10(ctr, key)
+        word = np.take_along_axis(w, ((j >> np.uint64(3)) & np.uint64(3)).astype(np.int64)[..., None]
+                                  .repeat(len(rows), axis=0), axis=-1)[..., 0]
+        byte = (word >> ((j & np.uint64(3)) * np.uint64(8)).astype(np.uint32)) & np.uint32(0xFF)
+        return (byte > thr) if kind == "strict_compare" else (byte >= thr)
+    return keep
+
+
+def _threshold_exact_scale(p):
+    thr, _ = _REAL_THRESHOLD(p)
+    return thr, 1.0 / (1.0 - float(np.float32(p)))  # planted: 1/(1-p) instead of 256/(256-thr)
+
+
+def _philox_nine_rounds(ctr, key):
+    c = np.asarray(ctr, dtype=np.uint64)
+    k = np.asarray(key, dtype=np.uint64)
+    x0, x1, x2, x3 = c[..., 0], c[..., 1], c[..., 2], c[..., 3]
+    k0, k1 = k[..., 0], k[..., 1]
+    m32 = np.uint64(0xFFFFFFFF)
+    for r in range(9):  # planted: one round short
+        if r > 0:
+            k0 = (k0 + np.uint64(0x9E3779B9)) & m32
+            k1 = (k1 + np.uint64(0xBB67AE85)) & m32
+        p0 = np.uint64(0xD2511F53) * x0
+        p1 = np.uint64(0xCD9E8D57) * x2
+        x0, x1, x2, x3 = (p1 >> np.uint64(32)) ^ x1 ^ k0, p1 & m32, (p0 >> np.uint64(32)) ^ x3 ^ k1, p0 & m32
+    return np.stack([x0, x1, x2, x3], axis=-1).astype(np.uint32)
+
+
+_REAL_THRESHOLD = oa.dropout_threshold
+CORE, GQA_WINDOW, DROPOUT = PIN_MODULES
+
+# mutant: (pin module, [(oracle function, mutated copy), ...])
 MUTANTS = {
-    "causal mask reversed": ("_allowed", _allowed_mask_reversed),
-    "LSE without the row maximum": ("_softmax_rows", _softmax_rows_lse_without_max),
-    "softmax over the wrong axis": ("_softmax_rows", _softmax_over_queries),
-    "scale applied twice": ("_scores", _scores_scale_twice),
-    "dQ missing the scale": ("attention_bwd64", _bwd_mutant("dq_no_scale")),
-    "dV with P instead of P^T": ("attention_bwd64", _bwd_mutant("dv_p_not_pt")),
-    "dS row sum over the wrong axis": ("attention_bwd64", _bwd_mutant("ds_wrong_axis")),
-    "dK off by 1e-6 relative": ("attention_bwd64", _bwd_mutant("dk_perturbed")),
+    "causal mask reversed": (CORE, [("_allowed", _allowed_mask_reversed)]),
+    "LSE without the row maximum": (CORE, [("_softmax_rows", _softmax_rows_lse_without_max)]),
+    "softmax over the wrong axis": (CORE, [("_softmax_rows", _softmax_over_queries)]),
+    "scale applied twice": (CORE, [("_scores", _scores_scale_twice)]),
+    "dQ missing the scale": (CORE, [("attention_bwd64", _bwd_mutant("dq_no_scale"))]),
+    "dV with P instead of P^T": (CORE, [("attention_bwd64", _bwd_mutant("dv_p_not_pt"))]),
+    "dS row sum over the wrong axis": (CORE, [("attention_bwd64", _bwd_mutant("ds_wrong_axis"))]),
+    "dK off by 1e-6 relative": (CORE, [("attention_bwd64", _bwd_mutant("dk_perturbed"))]),
+    "window left edge off by one": (GQA_WINDOW, [("_allowed", _allowed_window_edge("left"))]),
+    "window right edge off by one": (GQA_WINDOW, [("_allowed", _allowed_window_edge("right"))]),
+    "K/V head map h mod H_kv": (GQA_WINDOW, [("attention_fwd64", _fwd_head_map_mod),
+                                             ("attention_bwd64", _bwd_mutant("head_map"))]),
+    "group gradients overwritten, not summed": (GQA_WINDOW, [("attention_bwd64", _bwd_mutant("group_overwritten"))]),
+    "dropout keeps byte > thr": (DROPOUT, [("dropout_keep", _keep_mutant("strict_compare"))]),
+    "dropout seed halves swapped": (DROPOUT, [("dropout_keep", _keep_mutant("seed_halves_swapped"))]),
+    "dropout scale 1/(1-p)": (DROPOUT, [("dropout_threshold", _threshold_exact_scale)]),
+    "Philox one round short": (DROPOUT, [("philox4x32_10", _philox_nine_rounds)]),
+    "dV without the dropout mask": (DROPOUT, [("attention_bwd64", _bwd_mutant("dv_no_mask"))]),
 }
 
 
-def test_pins_pass_on_the_oracle():
-    failed, n = _run_pins()
-    assert n >= 30  # every parametrization of every pin was found
+@pytest.mark.parametrize("module", PIN_MODULES)
+def test_pins_pass_on_the_oracle(module):
+    failed, n = _run_pins(module)
+    assert n >= 10  # the module's pins and their parametrizations were found
     assert failed == [], failed
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(mutant, monkeypatch):
-    attr, fn = MUTANTS[mutant]
-    pins, _ = _pins()
-    monkeypatch.setattr(oa, attr, fn)
-    if hasattr(pins, attr):  # a pin module that imported the function by name
-        monkeypatch.setattr(pins, attr, fn)
-    failed, n = _run_pins()
+    module, swaps = MUTANTS[mutant]
+    pins, _ = _pins(module)
+    for attr, fn in swaps:
+        assert hasattr(oa, attr), attr
+        monkeypatch.setattr(oa, attr, fn)
+        if hasattr(pins, attr):  # the pin module imported the function by name
+            monkeypatch.setattr(pins, attr, fn)
+    failed, n = _run_pins(module)
     print("%s: %d of %d pins fail" % (mutant, len(failed), n))
     assert failed, "no pin catches: " + mutant
