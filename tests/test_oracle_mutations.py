@@ -4,7 +4,7 @@ Each mutant below is a copy of one or two oracle functions with one
 plausible mistake planted (the oracle itself is untouched: the copies are
 swapped in for the duration of one test).  Every pin of the pin module the
 mistake concerns (``tests/test_oracle_pins.py``, ``..._gqa_window.py``,
-``..._dropout.py``) is then run against the mutated oracle; at least one
+``..._dropout.py``, ``..._fp8.py``) is then run against the mutated oracle; at least one
 must fail.  A control run of each module with the unmodified oracle must
 pass them all, which checks this harness itself.
 """
@@ -15,9 +15,11 @@ import numpy as np
 import pytest
 
 import oracle.attention as oa
+import oracle.fp8 as of
 
 
-PIN_MODULES = ("tests.test_oracle_pins", "tests.test_oracle_pins_gqa_window", "tests.test_oracle_pins_dropout")
+PIN_MODULES = ("tests.test_oracle_pins", "tests.test_oracle_pins_gqa_window", "tests.test_oracle_pins_dropout",
+               "tests.test_oracle_pins_fp8")
 
 
 def _pins(module):
@@ -207,10 +209,33 @@ def _philox_nine_rounds(ctr, key):
     return np.stack([x0, x1, x2, x3], axis=-1).astype(np.uint32)
 
 
-_REAL_THRESHOLD = oa.dropout_threshold
-CORE, GQA_WINDOW, DROPOUT = PIN_MODULES
+def _e4m3_mutant(kind):
+    def decode(b):
+        b = np.asarray(b)
+        bi = b.astype(np.int64)
+        sign = 1.0 if kind == "no_sign" else np.where(bi & 0x80, -1.0, 1.0)
+        e = (bi >> 3) & 0xF
+        m = (bi & 7).astype(np.float64)
+        normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - (8.0 if kind == "bias8" else 7.0))
+        sub = ((1.0 + m / 8.0) if kind == "no_subnormals" else (m / 8.0)) * 2.0 ** -6
+        mag = np.where(e == 0, sub, normal)
+        if kind != "no_nan":
+            mag = np.where((bi & 0x7F) == 0x7F, np.nan, mag)
+        return sign * mag
+    return decode
 
-# mutant: (pin module, [(oracle function, mutated copy), ...])
+
+def _decoded_descales_swapped(q8, k8, v8, descale):
+    qd, kd, vd = (float(x) for x in descale)
+    return of.e4m3fn_to_float64(q8) * qd, of.e4m3fn_to_float64(k8) * vd, of.e4m3fn_to_float64(v8) * kd
+
+
+_REAL_THRESHOLD = oa.dropout_threshold
+CORE, GQA_WINDOW, DROPOUT, FP8 = PIN_MODULES
+
+# mutant: (pin module, [(oracle function, mutated copy), ...]); the
+# functions are those of oracle.attention unless the name is one of
+# oracle.fp8's
 MUTANTS = {
     "causal mask reversed": (CORE, [("_allowed", _allowed_mask_reversed)]),
     "LSE without the row maximum": (CORE, [("_softmax_rows", _softmax_rows_lse_without_max)]),
@@ -230,7 +255,13 @@ MUTANTS = {
     "dropout scale 1/(1-p)": (DROPOUT, [("dropout_threshold", _threshold_exact_scale)]),
     "Philox one round short": (DROPOUT, [("philox4x32_10", _philox_nine_rounds)]),
     "dV without the dropout mask": (DROPOUT, [("attention_bwd64", _bwd_mutant("dv_no_mask"))]),
+    "e4m3 exponent bias 8": (FP8, [("e4m3fn_to_float64", _e4m3_mutant("bias8"))]),
+    "e4m3 subnormals decoded as normals": (FP8, [("e4m3fn_to_float64", _e4m3_mutant("no_subnormals"))]),
+    "e4m3 0x7f not NaN": (FP8, [("e4m3fn_to_float64", _e4m3_mutant("no_nan"))]),
+    "e4m3 sign bit ignored": (FP8, [("e4m3fn_to_float64", _e4m3_mutant("no_sign"))]),
+    "fp8 K and V descales swapped": (FP8, [("_decoded", _decoded_descales_swapped)]),
 }
+FP8_FUNCTIONS = ("e4m3fn_to_float64", "_decoded")
 
 
 @pytest.mark.parametrize("module", PIN_MODULES)
@@ -245,8 +276,9 @@ def test_pins_catch_planted_mistake(mutant, monkeypatch):
     module, swaps = MUTANTS[mutant]
     pins, _ = _pins(module)
     for attr, fn in swaps:
-        assert hasattr(oa, attr), attr
-        monkeypatch.setattr(oa, attr, fn)
+        target = of if attr in FP8_FUNCTIONS else oa
+        assert hasattr(target, attr), attr
+        monkeypatch.setattr(target, attr, fn)
         if hasattr(pins, attr):  # the pin module imported the function by name
             monkeypatch.setattr(pins, attr, fn)
     failed, n = _run_pins(module)
