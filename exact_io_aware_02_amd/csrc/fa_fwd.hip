@@ -97,12 +97,12 @@ template <int D>
 constexpr int64_t kPhasedMinBlocks = D == 64 ? 1536 : 1024;
 
 static_assert(kBN == 32, "K/V tiles are the 32-row tiles of fa_device.h");
-template <int D>
+template <int D, int NW = kWaves>  // NW: the waves of a key group, which share its tile copies
 struct TileCopy {
-  static constexpr int NI = TileLayout<D>::template copy_insts<kWaves>();  // instructions per wave per tile
+  static constexpr int NI = TileLayout<D>::template copy_insts<NW>();  // instructions per wave per tile
   static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t tile_byte_off,
                                                uint16_t* lds, int lane, int wave) {
-    TileLayout<D>::template issue<kWaves>(rs, row_bytes, tile_byte_off, lds, lane, wave);
+    TileLayout<D>::template issue<NW>(rs, row_bytes, tile_byte_off, lds, lane, wave);
   }
 };
 
@@ -409,7 +409,7 @@ __device__ __forceinline__ void fwd_step(int j, int n_kt, f32x16 (&s)[kNQB], f32
 // MFMAs ahead), which overwrite S(j).  The waves sharing a SIMD fill each
 // other's phases.  The ring holds NBUF tiles; step j requests tile
 // j + NBUF - 1 into the slot of tile j-1, read in full by the last step.
-template <int D, int DT, bool BAND, bool DROP, int kNQB>
+template <int D, int DT, bool BAND, bool DROP, int kNQB, int NW = kWaves, int NB = FwdCfg<D, true>::NBUF>
 __device__ __forceinline__ void fwd_step_phased(int j, int n_kt, f32x16 (&s)[kNQB], const uint16_t* __restrict__ Vj,
                                             const uint16_t* __restrict__ Kn, uint16_t* __restrict__ Kdst,
                                             uint16_t* __restrict__ Vdst, __amdgpu_buffer_rsrc_t krs,
@@ -417,12 +417,12 @@ __device__ __forceinline__ void fwd_step_phased(int j, int n_kt, f32x16 (&s)[kNQ
                                             uint32_t vtb, const u32x4 (&qf)[kNQB][D / 16], f32x16 (&acc)[D / 32][kNQB],
                                             RowState<kNQB>& st, int Nk, int wl, int wr, int qw0, float c, int lane,
                                             int wave, const TileLayout<D>& ta, const DropoutParams& dp, uint32_t bh) {
-  using TC = TileCopy<D>;
+  using TC = TileCopy<D, NW>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   const int j0 = j * kBN;
   const int col = lane & 31, half = lane >> 5;
-  constexpr int PD = FwdCfg<D, true>::NBUF - 1;  // tile j+PD goes to the slot of tile j-1
+  constexpr int PD = NB - 1;  // tile j+PD goes to the slot of tile j-1
   if (j + PD < n_kt) {
     TC::issue(krs, krow, (uint32_t)(j + PD) * ktb, Kdst, lane, wave);
     TC::issue(vrs, vrow, (uint32_t)(j + PD) * vtb, Vdst, lane, wave);
@@ -495,13 +495,13 @@ __device__ __forceinline__ void fwd_step_phased(int j, int n_kt, f32x16 (&s)[kNQ
 // A step of the phased ring for a wave with no work on tile j: its share
 // of the copy of tile j + NBUF - 1 (into the slot of tile j - 1), the wait
 // for tile j + 1 and the barrier, as in fwd_step_phased.
-template <int D>
+template <int D, int NW = kWaves, int NB = FwdCfg<D, true>::NBUF>
 __device__ __forceinline__ void fwd_idle_phased(int j, int n_kt, uint16_t* __restrict__ Kdst,
                                                 uint16_t* __restrict__ Vdst, __amdgpu_buffer_rsrc_t krs,
                                                 __amdgpu_buffer_rsrc_t vrs, uint32_t krow, uint32_t vrow, uint32_t ktb,
                                                 uint32_t vtb, int lane, int wave) {
-  using TC = TileCopy<D>;
-  constexpr int PD = FwdCfg<D, true>::NBUF - 1;
+  using TC = TileCopy<D, NW>;
+  constexpr int PD = NB - 1;
   if (j + PD < n_kt) {
     TC::issue(krs, krow, (uint32_t)(j + PD) * ktb, Kdst, lane, wave);
     TC::issue(vrs, vrow, (uint32_t)(j + PD) * vtb, Vdst, lane, wave);
@@ -604,14 +604,22 @@ constexpr bool kKSplitPhased = D == 128;
 // tiles cut into ceil(n / p.chunk) near-equal runs.  A block of one chunk writes O and
 // LSE; the chunks of a split block write their partial state (O^T, m, l)
 // to p.part, which fwd_merge_kernel combines.
-template <int D, int DT, bool BAND, bool DROP, bool PHASED, int KSPLIT, bool CHUNK>
-__global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_eu(
-    FwdCfg<D, PHASED>::WAVES_PER_SIMD, FwdCfg<D, PHASED>::WAVES_PER_SIMD))) void fwd_kernel(FwdParams p) {
+// GW: waves per query block (and per key group), 32 queries each.  Four
+// everywhere but the small-block split below, which runs six groups of two
+// waves on 64-query blocks with three-slot rings (its LDS: six rings).
+template <int D, bool PHASED, int GW>
+constexpr int kFwdWavesPerSimd = GW < kWaves ? 3 : FwdCfg<D, PHASED>::WAVES_PER_SIMD;
+
+template <int D, int DT, bool BAND, bool DROP, bool PHASED, int KSPLIT, bool CHUNK, int GW = kWaves>
+__global__ __launch_bounds__(64 * GW * KSPLIT) __attribute__((amdgpu_waves_per_eu(
+    kFwdWavesPerSimd<D, PHASED, GW>, kFwdWavesPerSimd<D, PHASED, GW>))) void fwd_kernel(FwdParams p) {
   static_assert(!CHUNK || KSPLIT == 1, "key chunks run whole workgroups");
+  static_assert(GW == kWaves || (PHASED && !CHUNK), "two-wave groups run the phased step");
   constexpr int kNQB = 1;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NBUF = FwdCfg<D, PHASED>::NBUF;  // K/V ring (see fwd_step, fwd_step_phased)
+  constexpr int BMG = GW * kQW;  // queries per block
+  constexpr int NBUF = GW < kWaves ? 3 : FwdCfg<D, PHASED>::NBUF;  // K/V ring (see fwd_step, fwd_step_phased)
   constexpr int TILE = kTileElems<D>;
 
   // One LDS object for the whole ring: the compiler gives every separate
@@ -627,8 +635,8 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
   const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave_all / kWaves;          // key group (0 without a split)
-  const int wave = wave_all - grp * kWaves;   // wave within the group: its 32 queries
+  const int grp = wave_all / GW;          // key group (0 without a split)
+  const int wave = wave_all - grp * GW;   // wave within the group: its 32 queries
   auto& Ks = sm.k[grp];
   auto& Vs = sm.v[grp];
 
@@ -636,7 +644,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
   // head t % BH.  Consecutive blocks land on different XCDs round-robin,
   // so a head's tiles share one XCD's L2 when B*H is a multiple of 8.
   const int BH = p.B * p.H;
-  const int n_qt = (p.Nq + kBM - 1) / kBM;
+  const int n_qt = (p.Nq + BMG - 1) / BMG;
   const int t = blockIdx.x;
   const int bh = t - (t / BH) * BH;
   int qt = n_qt - 1 - t / BH;
@@ -651,7 +659,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
     if (cp.sb > 1) slot = cp.base + cp.idx;
   }
   const int b = bh / p.H, h = bh - b * p.H;
-  const int q0 = qt * kBM;
+  const int q0 = qt * BMG;
   const int qw0 = q0 + wave * kQW;
 
   const int hk = h / p.G;  // K/V head shared by p.G consecutive query heads
@@ -663,7 +671,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
   // split, this group's run of them
   int kend = p.Nk, jt0 = 0;
   if (BAND) {
-    const int qlast = min(q0 + kBM, p.Nq) - 1;
+    const int qlast = min(q0 + BMG, p.Nq) - 1;
     if (p.wr >= 0) kend = min(p.Nk, qlast + p.wr + 1);
     if (p.wl >= 0) jt0 = max(0, q0 - p.wl) / kBN;
   }
@@ -685,7 +693,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vp, p.Nk, p.sv.s, D);
   const uint32_t krow = (uint32_t)(p.sk.s * 2), vrow = (uint32_t)(p.sv.s * 2);
   const uint32_t ktb = kBN * krow, vtb = kBN * vrow;
-  using TC = TileCopy<D>;
+  using TC = TileCopy<D, GW>;
 
   // Q^T as the B operand, resident in registers: lane holds
   // Q[qw0 + 32*nb + col][16*ks + 8*half .. +7].  Its loads go first so the
@@ -766,7 +774,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
       int j = jt0;
       auto idle = [&]() {
         const int sp = wrap(sl + NBUF - 1);  // slot of tile j-1
-        fwd_idle_phased<D>(j, n_kt, Ks[sp], Vs[sp], krs, vrs, krow, vrow, ktb, vtb, lane, wave);
+        fwd_idle_phased<D, GW, NBUF>(j, n_kt, Ks[sp], Vs[sp], krs, vrs, krow, vrow, ktb, vtb, lane, wave);
         sl = wrap(sl + 1);
       };
       for (; j < wlo; ++j) idle();
@@ -782,7 +790,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
         }
         auto one = [&]() {
           const int sp = wrap(sl + NBUF - 1);  // slot of tile j-1
-          fwd_step_phased<D, DT, BAND, DROP, kNQB>(j, n_kt, sa, Vs[sl], Ks[wrap(sl + 1)], Ks[sp], Vs[sp], krs, vrs,
+          fwd_step_phased<D, DT, BAND, DROP, kNQB, GW, NBUF>(j, n_kt, sa, Vs[sl], Ks[wrap(sl + 1)], Ks[sp], Vs[sp], krs, vrs,
                                                    krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane,
                                                    wave, ta, p.drop, (uint32_t)bh);
           sl = wrap(sl + 1);
@@ -796,7 +804,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
           for (; j + NBUF <= whi; j += NBUF) {
 #pragma unroll
             for (int r = 0; r < NBUF; ++r)
-              fwd_step_phased<D, DT, BAND, DROP, kNQB>(j + r, n_kt, sa, Vs[r], Ks[(r + 1) % NBUF],
+              fwd_step_phased<D, DT, BAND, DROP, kNQB, GW, NBUF>(j + r, n_kt, sa, Vs[r], Ks[(r + 1) % NBUF],
                                                        Ks[(r + NBUF - 1) % NBUF], Vs[(r + NBUF - 1) % NBUF], krs, vrs,
                                                        krow, vrow, ktb, vtb, qf, acc, st, p.Nk, p.wl, p.wr, qw0, c, lane,
                                                        wave, ta, p.drop, (uint32_t)bh);
@@ -916,8 +924,8 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
     for (int i = barriers(max(0, n_kt - jt0)); i < barriers(per); ++i) lds_barrier();
     // every group is done with its ring: reuse it for the hand-over
     constexpr int NV = DB * 16 + 2;  // floats per lane: O^T, m, l
-    static_assert((size_t)(KSPLIT - 1) * kWaves * NV * 64 * 4 <= sizeof(Smem), "hand-over fits the rings");
-    float* xo = reinterpret_cast<float*>(&sm) + (size_t)((grp - 1) * kWaves + wave) * NV * 64 + lane;
+    static_assert((size_t)(KSPLIT - 1) * GW * NV * 64 * 4 <= sizeof(Smem), "hand-over fits the rings");
+    float* xo = reinterpret_cast<float*>(&sm) + (size_t)((grp - 1) * GW + wave) * NV * 64 + lane;
     lds_barrier();
     if (grp > 0) {
 #pragma unroll
@@ -931,7 +939,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT) __attribute__((amdgpu_waves_per_
     if (grp > 0) return;
 #pragma unroll
     for (int g = 1; g < KSPLIT; ++g) {
-      const float* xi = reinterpret_cast<const float*>(&sm) + (size_t)((g - 1) * kWaves + wave) * NV * 64 + lane;
+      const float* xi = reinterpret_cast<const float*>(&sm) + (size_t)((g - 1) * GW + wave) * NV * 64 + lane;
       const float mg = xi[(DB * 16) * 64], lg = xi[(DB * 16 + 1) * 64];
       const float mn = fmaxf(st.m[0], mg);
       const float a0 = exp2_fast(st.m[0] - mn), ag = exp2_fast(mg - mn);
@@ -1066,10 +1074,10 @@ __global__ __launch_bounds__(kThreads) void fwd_merge_kernel(FwdParams p) {
   if (ch == 0) p.lse[(int64_t)bh * p.Nq + qi] = L > 0.f ? (M + log2_fast(L)) * kLn2 : -__builtin_inff();
 }
 
-template <int D, int DT, bool BAND, bool DROP, bool PHASED, int KSPLIT>
+template <int D, int DT, bool BAND, bool DROP, bool PHASED, int KSPLIT, int GW>
 hipError_t launch_t(const FwdParams& p, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND, DROP, PHASED, KSPLIT, false>), dim3((unsigned)blocks),
-                     dim3(kThreads * KSPLIT), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, DT, BAND, DROP, PHASED, KSPLIT, false, GW>), dim3((unsigned)blocks),
+                     dim3(64 * GW * KSPLIT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1094,13 +1102,13 @@ hipError_t launch_chunked(const FwdParams& p, const FwdSplitPlan& plan, bool ban
                 : launch_chunked_t<D, DT, false, false>(p, plan, stream);
 }
 
-template <int D, int DT, bool PHASED, int KSPLIT>
+template <int D, int DT, bool PHASED, int KSPLIT, int GW = kWaves>
 hipError_t launch_ds(const FwdParams& p, bool banded, int64_t blocks, hipStream_t stream) {
   if (p.drop.thr > 0)
-    return banded ? launch_t<D, DT, true, true, PHASED, KSPLIT>(p, blocks, stream)
-                  : launch_t<D, DT, false, true, PHASED, KSPLIT>(p, blocks, stream);
-  return banded ? launch_t<D, DT, true, false, PHASED, KSPLIT>(p, blocks, stream)
-                : launch_t<D, DT, false, false, PHASED, KSPLIT>(p, blocks, stream);
+    return banded ? launch_t<D, DT, true, true, PHASED, KSPLIT, GW>(p, blocks, stream)
+                  : launch_t<D, DT, false, true, PHASED, KSPLIT, GW>(p, blocks, stream);
+  return banded ? launch_t<D, DT, true, false, PHASED, KSPLIT, GW>(p, blocks, stream)
+                : launch_t<D, DT, false, false, PHASED, KSPLIT, GW>(p, blocks, stream);
 }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
@@ -1120,6 +1128,13 @@ int device_cus() {
 // The intra-workgroup key split pays when the heaviest query block has at
 // least this many key tiles; below, the merge costs more than it saves.
 constexpr int kKSplitMinTiles = 32;
+// At d = 64, from this many key tiles on, the split runs on 64-query blocks
+// with six groups of two waves (three-slot rings): each heavy block's keys
+// in sixths on twice the blocks.  Measured on grids of 256 128-query
+// blocks: B1 H2 N16384 131 -> 93 us, B1 H4 N8192 72 -> 56 us; with 64
+// tiles (B2 H8 N2048) no change, with 32-36 (B2 H16 N1024, a 1000-key
+// window at N4096) 15-17% slower, where the blocks' own latency dominates.
+constexpr int kSmallBlockSplitMinTiles = 128;
 
 template <int D, int DT>
 hipError_t launch_dc(const FwdParams& p, bool banded, hipStream_t stream) {
@@ -1129,11 +1144,18 @@ hipError_t launch_dc(const FwdParams& p, bool banded, hipStream_t stream) {
   if (blocks >= kPhasedMinBlocks<D>) return launch_ds<D, DT, true, 1>(p, banded, blocks, stream);
   // at most one workgroup per CU: split each block's keys over more waves
   if (blocks <= device_cus()) {
+    constexpr int enough = D == 64 ? kSmallBlockSplitMinTiles : kKSplitMinTiles;
     int most = 0;  // key tiles of the heaviest block (n_qt <= the CU count here)
-    for (int qb = 0; qb < n_qt && most < kKSplitMinTiles; ++qb) {
+    for (int qb = 0; qb < n_qt && most < enough; ++qb) {
       int lo, hi;
       block_tiles(qb, p.Nq, p.Nk, p.wl, p.wr, banded, lo, hi);
       most = max(most, hi - lo);
+    }
+    if constexpr (D == 64) {  // (six rings of 16 KiB slots would not fit the LDS at d = 128)
+      if (most >= kSmallBlockSplitMinTiles) {
+        const int64_t blocks64 = (int64_t)((p.Nq + 63) / 64) * p.B * p.H;
+        return launch_ds<D, DT, true, 6, 2>(p, banded, blocks64, stream);
+      }
     }
     if (most >= kKSplitMinTiles) return launch_ds<D, DT, kKSplitPhased<D>, kKSplit<D>>(p, banded, blocks, stream);
   }

@@ -14,7 +14,9 @@
   fa_fwd_ex for grids of at most one workgroup per CU whose heaviest block
   has 32 or more key tiles: three groups of four waves per workgroup (on
   the phased schedule at d = 128, the interleaved one at d = 64), each on
-  its own run of the keys, merged through LDS.
+  its own run of the keys, merged through LDS; at d = 64 from 128 key
+  tiles on, six groups of two waves on blocks of 64 queries (phased, with
+  three-slot rings).
 
 Each case is a small problem repeated along the batch until the grid
 reaches the shape's size.  The first copy is checked against the fp64 oracle
@@ -117,6 +119,11 @@ INTRA_CASES = [
     ("d64_gqa_window", 1, 4, 2, 1200, 1200, 64, "bf16", "bhsd", True, (900, -1), None),
     ("d128_window_empty_rows", 1, 2, 2, 1500, 1100, 128, "bf16", "bhsd", False, (1000, 200), None),
     ("d64_dropout", 1, 2, 2, 1100, 1100, 64, "fp16", "bhsd", True, None, (0.25, (9 << 32) + 1, 4)),
+    # d = 64, 128+ key tiles: six two-wave groups on 64-query blocks
+    ("d64_long_causal", 1, 2, 2, 4500, 4500, 64, "bf16", "bhsd", True, None, None),
+    ("d64_long_keys_rect", 1, 2, 2, 300, 5000, 64, "bf16", "bhsd", False, None, None),
+    ("d64_long_gqa_window_bshd", 1, 4, 2, 4200, 4200, 64, "fp16", "bshd", True, (4100, -1), None),
+    ("d64_long_dropout", 1, 1, 1, 4300, 4300, 64, "fp16", "bhsd", True, None, (0.15, (11 << 32) + 3, 6)),
 ]
 
 
@@ -198,7 +205,7 @@ def test_chunked_forward(case):
 
 
 RISE_CASES = [("d64_fp16", 64, "fp16"), ("d128_bf16", 128, "bf16")]
-RISE_SHAPES = ["small", "interleaved", "phased", "intra", "chunked"]
+RISE_SHAPES = ["small", "interleaved", "phased", "intra", "intra_long", "chunked"]
 
 
 @pytest.mark.parametrize("shape", RISE_SHAPES)
@@ -214,7 +221,7 @@ def test_rising_scores_every_schedule(case, shape):
     for; the bound adds O's own rounding to the output type, a unit roundoff
     (2^-8 bf16, 2^-11 fp16) times |O|."""
     name, d, dt = case
-    N = {"small": 300, "interleaved": 300, "phased": 300, "intra": 1100, "chunked": 4096}[shape]
+    N = {"small": 300, "interleaved": 300, "phased": 300, "intra": 1100, "intra_long": 4300, "chunked": 4096}[shape]
     B, H = 1, ({64: 1, 128: 2}[d] if shape == "chunked" else 2)
     blocks = math.ceil(N / 128) * B * H
     R = copies(shape, blocks, d) if shape in ("small", "interleaved", "phased") else 1
@@ -228,6 +235,7 @@ def test_rising_scores_every_schedule(case, shape):
         assert fa.fa_fwd_splitk_workspace_bytes(B, H, N, N, d, True, (-1, -1)) > 0
     qg, kg, vg = (x.repeat(R, 1, 1, 1).to(DEV) for x in (q, k, v))
     o, lse = fa.attention_fwd(qg, kg, vg, causal=True, scale=scale, splitk=shape in ("small", "chunked"))
+    # (intra_long: at d = 64 the six two-wave groups on 64-query blocks)
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
     o_ref, lse_ref = attention_fwd64(*(to_bhsd64(x) for x in (q, k, v)), scale, True)
