@@ -16,6 +16,7 @@ from .attention import (
     attention_fwd64,
     attention_rows_fwd64,
     attention_bwd64,
+    attention_rows_dq64,
     philox4x32_10,
     dropout_threshold,
     dropout_keep,
@@ -26,6 +27,7 @@ __all__ = [
     "attention_fwd64",
     "attention_rows_fwd64",
     "attention_bwd64",
+    "attention_rows_dq64",
     "philox4x32_10",
     "dropout_threshold",
     "dropout_keep",

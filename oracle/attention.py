@@ -69,6 +69,7 @@ __all__ = [
     "attention_fwd64",
     "attention_rows_fwd64",
     "attention_bwd64",
+    "attention_rows_dq64",
     "philox4x32_10",
     "dropout_threshold",
     "dropout_keep",
@@ -267,3 +268,33 @@ def attention_bwd64(q, k, v, do, scale, causal, window=(-1, -1), dropout=None):
             dq[b, h] = scale * (ds @ kk)
             dk[b, h // G] += scale * (ds.T @ qq)
     return dq, dk, dv
+
+
+def attention_rows_dq64(q, k, v, do, scale, causal, rows, window=(-1, -1), dropout=None):
+    """dQ of ``attention_bwd64`` restricted to selected query rows.
+
+    A query row's gradient depends only on its own softmax row (the same
+    chain rule, row by row: dS_i = P_i * (dP_i - rowsum(W_i * dP_i)),
+    dQ_i = scale * dS_i K), so it is computed here for the rows
+    ``rows`` [B, H, R] alone, each against all keys.  Returns
+    dq [B, H, R, d] in float64.
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    rows = np.asarray(rows, dtype=np.int64)
+    B, H, Nq, d, G = _check(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError("dO must have the shape of Q")
+    if rows.ndim != 3 or rows.shape[:2] != (B, H):
+        raise ValueError("rows must be [B, H, R]")
+    scale = float(scale)
+    dq = np.empty((B, H, rows.shape[2], d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            r = rows[b, h]
+            kk, vv, g = k[b, h // G], v[b, h // G], do[b, h][r]
+            p, _ = _softmax_rows(_scores(q[b, h][r], kk, scale, causal, r, window))
+            wgt = _dropped(p, b, h, H, r, dropout)
+            dp = g @ vv.T
+            ds = p * (_dropped(dp, b, h, H, r, dropout) - np.sum(wgt * dp, axis=1, keepdims=True))
+            dq[b, h] = scale * (ds @ kk)
+    return dq

@@ -138,6 +138,10 @@ def _bwd_mutant(kind):
     return bwd
 
 
+def _rows_dq_no_scale(q, k, v, do, scale, causal, rows, window=(-1, -1), dropout=None):
+    return _REAL_ROWS_DQ(q, k, v, do, scale, causal, rows, window, dropout) / float(scale)  # planted
+
+
 def _fwd_head_map_mod(q, k, v, scale, causal, window=(-1, -1), dropout=None):
     q, k, v = oa._as64(q), oa._as64(k), oa._as64(v)
     B, H, Nq, d, G = oa._check(q, k, v)
@@ -231,6 +235,7 @@ def _decoded_descales_swapped(q8, k8, v8, descale):
 
 
 _REAL_THRESHOLD = oa.dropout_threshold
+_REAL_ROWS_DQ = oa.attention_rows_dq64
 CORE, GQA_WINDOW, DROPOUT, FP8 = PIN_MODULES
 
 # mutant: (pin module, [(oracle function, mutated copy), ...]); the
@@ -245,6 +250,7 @@ MUTANTS = {
     "dV with P instead of P^T": (CORE, [("attention_bwd64", _bwd_mutant("dv_p_not_pt"))]),
     "dS row sum over the wrong axis": (CORE, [("attention_bwd64", _bwd_mutant("ds_wrong_axis"))]),
     "dK off by 1e-6 relative": (CORE, [("attention_bwd64", _bwd_mutant("dk_perturbed"))]),
+    "rows dQ missing the scale": (CORE, [("attention_rows_dq64", _rows_dq_no_scale)]),
     "window left edge off by one": (GQA_WINDOW, [("_allowed", _allowed_window_edge("left"))]),
     "window right edge off by one": (GQA_WINDOW, [("_allowed", _allowed_window_edge("right"))]),
     "K/V head map h mod H_kv": (GQA_WINDOW, [("attention_fwd64", _fwd_head_map_mod),

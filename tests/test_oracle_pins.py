@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_bwd64, attention_fwd64, attention_rows_fwd64
+from oracle import attention_bwd64, attention_fwd64, attention_rows_dq64, attention_rows_fwd64
 
 RNG = np.random.default_rng(1234)  # reseeded per test (tests/conftest.py)
 
@@ -291,3 +291,16 @@ def test_bwd_uses_rowsum_identity_consistently():
     dq, dk, _ = attention_bwd64(q, k, v, do, s, True)
     np.testing.assert_allclose(dq[0, 0], s * ds @ k[0, 0], atol=1e-12)
     np.testing.assert_allclose(dk[0, 0], s * ds.T @ q[0, 0], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_dq_matches_full(causal):
+    """dQ restricted to chosen query rows equals those rows of the full
+    backward's dQ (itself pinned to finite differences and torch autograd)."""
+    q, k, v, do = rand(2, 2, 30, 8), rand(2, 2, 30, 8), rand(2, 2, 30, 8), rand(2, 2, 30, 8)
+    rows = np.array([[[0, 5, 29], [3, 3, 17]], [[28, 1, 14], [0, 29, 2]]])
+    dq, _, _ = attention_bwd64(q, k, v, do, 0.4, causal)
+    got = attention_rows_dq64(q, k, v, do, 0.4, causal, rows)
+    for b in range(2):
+        for h in range(2):
+            np.testing.assert_allclose(got[b, h], dq[b, h][rows[b, h]], rtol=1e-12, atol=1e-13)

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_bwd64, attention_fwd64, dropout_keep, dropout_threshold, philox4x32_10
+from oracle import (attention_bwd64, attention_fwd64, attention_rows_dq64, dropout_keep, dropout_threshold,
+                    philox4x32_10)
 
 RNG = np.random.default_rng(2468)  # reseeded per test (tests/conftest.py)
 M32 = 0xFFFFFFFF
@@ -174,3 +175,17 @@ def test_dropout_bwd_finite_differences():
             num[idx] = (lp - lm) / (2 * h)
         err = np.abs(num - g).max() / max(np.abs(num).max(), 1e-3)
         assert err < 1e-6, err
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_dq_matches_full_with_dropout(causal):
+    """Row-restricted dQ under dropout (the rows' own keep bits, by global
+    row index) equals those rows of the full backward."""
+    q, k, v, do = rand(2, 3, 40, 8), rand(2, 3, 40, 8), rand(2, 3, 40, 8), rand(2, 3, 40, 8)
+    drop = (0.3, (7 << 32) + 5, 3)
+    rows = np.tile(np.array([0, 9, 33, 39]), (2, 3, 1))
+    dq, _, _ = attention_bwd64(q, k, v, do, 0.35, causal, dropout=drop)
+    got = attention_rows_dq64(q, k, v, do, 0.35, causal, rows, dropout=drop)
+    for b in range(2):
+        for h in range(3):
+            np.testing.assert_allclose(got[b, h], dq[b, h][rows[b, h]], rtol=1e-12, atol=1e-13)

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_bwd64, attention_fwd64, attention_rows_fwd64
+from oracle import attention_bwd64, attention_fwd64, attention_rows_dq64, attention_rows_fwd64
 
 RNG = np.random.default_rng(4321)  # reseeded per test (tests/conftest.py)
 
@@ -219,3 +219,16 @@ def test_window_gqa_bwd_finite_differences(window, causal):
             num[idx] = (lp - lm) / (2 * h)
         err = np.abs(num - g).max() / max(np.abs(num).max(), 1e-3)
         assert err < 1e-6, err
+
+
+@pytest.mark.parametrize("window,causal", [((3, -1), True), ((2, 4), False), ((0, 0), False)])
+def test_rows_dq_matches_full_gqa_window(window, causal):
+    """Row-restricted dQ with fewer K/V heads and a window equals those rows
+    of the full backward (including rows whose window is cut by the ends)."""
+    q, do = rand(1, 4, 25, 8), rand(1, 4, 25, 8)
+    k, v = rand(1, 2, 25, 8), rand(1, 2, 25, 8)
+    rows = np.array([[[0, 24, 12], [1, 2, 3], [24, 23, 0], [7, 7, 19]]])
+    dq, _, _ = attention_bwd64(q, k, v, do, 0.5, causal, window=window)
+    got = attention_rows_dq64(q, k, v, do, 0.5, causal, rows, window=window)
+    for h in range(4):
+        np.testing.assert_allclose(got[0, h], dq[0, h][rows[0, h]], rtol=1e-12, atol=1e-13)
