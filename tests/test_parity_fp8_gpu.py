@@ -229,3 +229,43 @@ def test_fp8_rising_scores(d, shape):
     for r in range(1, R):
         assert torch.equal(o[r * B:(r + 1) * B].view(torch.int16), o[:B].view(torch.int16)), r
         assert torch.equal(lse[r * B:(r + 1) * B], lse[:B]), r
+
+
+def draw_fp8(i):
+    rng = np.random.default_rng(7000 + i)
+    d = int(rng.choice([64, 128]))
+    B, H = int(rng.choice([1, 2])), int(rng.choice([1, 2, 3, 4, 6]))
+    Hkv = int(rng.choice([g for g in range(1, H + 1) if H % g == 0]))
+    Nq, Nk = (int(x) for x in rng.integers(1, 600, size=2))
+    window = None
+    if rng.random() < 0.4:
+        window = tuple(int(rng.choice([-1, int(rng.integers(0, max(Nk, 2)))])) for _ in range(2))
+    descale = tuple(float(rng.choice([-1.0, 1.0, 1.0, 1.0]) * 2.0 ** rng.uniform(-2, 2)) for _ in range(3))
+    scale = float(rng.uniform(0.5, 1.5)) / math.sqrt(d)
+    return dict(B=B, H=H, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, layout=str(rng.choice(["bhsd", "bhsd", "bshd"])),
+                causal=bool(rng.random() < 0.5), window=window, descale=descale, scale=scale,
+                seed=int(rng.integers(0, 2 ** 31)))
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_fp8_random_case(i):
+    """Seeded random combinations of the fp8 forward's options at once
+    (heads and K/V heads, ragged Nq and Nk, d, layout, causal, random window
+    edges, descale factors of either sign between 1/4 and 4, the scale),
+    each printed before it runs; against the oracle under the rounding
+    model, LSE within 1e-3."""
+    c = draw_fp8(i)
+    say("case fp8 random %d: %s" % (i, c))
+    B, H, Hkv, Nq, Nk, d, layout = c["B"], c["H"], c["Hkv"], c["Nq"], c["Nk"], c["d"], c["layout"]
+    inp = make_qkv(B, H, Nq, Nk, d, "fp8", layout, seed=c["seed"], Hkv=Hkv)
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    o, lse = fa.attention_fwd_fp8(q, k, v, causal=c["causal"], scale=c["scale"], layout=layout,
+                                  window=c["window"], descale=c["descale"])
+    torch.cuda.synchronize()
+    w = c["window"] if c["window"] is not None else (-1, -1)
+    q8, k8, v8 = (fp8_bytes(inp[x], layout) for x in ("q", "k", "v"))
+    o_ref, lse_ref = attention_fp8_fwd64(q8, k8, v8, c["scale"], c["causal"], window=w, descale=c["descale"])
+    rows = np.tile(np.arange(Nq), (B, H, 1))
+    bound, sigma = fp8_rounding_model(q8, k8, v8, c["scale"], c["causal"], rows, window=w, descale=c["descale"])
+    check("random %d" % i, to_bhsd64(o.cpu(), layout), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref,
+          bound, sigma)
