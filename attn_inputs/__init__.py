@@ -81,6 +81,30 @@ def make_qkv(B, H, Nq, Nk, d, dtype, layout="bhsd", seed=0, in_scale=1.0, with_d
     return out
 
 
+def make_qkv_pooled(B, H, N, d, dtype, layout="bhsd", seed=0, pool_rows=1 << 16, with_do=False):
+    """Inputs for grids too large to draw element by element in seconds.
+
+    For each of q, k, v (then dO) in that order: a pool of ``pool_rows``
+    rows drawn as in ``make_qkv`` (float32 standard normal, rounded to the
+    dtype), then a seeded offset o per (b, h); row i of head (b, h) is pool
+    row (o + i) mod pool_rows.  Heads hold distinct cyclic windows of the
+    pool, so a head read in place of another gives other values.  Returns
+    contiguous CPU tensors like ``make_qkv`` (K/V with H heads).
+    """
+    rng = np.random.default_rng(seed)
+    td = torch_dtype(dtype)
+    out = {}
+    for name in ("q", "k", "v") + (("do",) if with_do else ()):
+        pool = torch.from_numpy(rng.standard_normal((pool_rows, d), dtype=np.float32)).to(td)
+        off = torch.from_numpy(rng.integers(0, pool_rows, size=(B, H)))
+        idx = (off[:, :, None] + torch.arange(N)[None, None, :]) % pool_rows
+        x = pool[idx]  # [B, H, N, d]
+        if layout == "bshd":
+            x = x.transpose(1, 2)
+        out[name] = x.contiguous()
+    return out
+
+
 def workload_inputs(w, seed=None):
     """Inputs of a named workload (dO drawn only when it has a backward)."""
     return make_qkv(w.B, w.H, w.N, w.N, w.d, w.dtype, w.layout, w.seed if seed is None else seed,
@@ -120,4 +144,4 @@ def sample_rows(B, H, N, R, seed):
     return out
 
 
-__all__ += ["workload_inputs", "fp8_bytes"]
+__all__ += ["workload_inputs", "fp8_bytes", "make_qkv_pooled"]

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+from grad_identities import identity_errors
 from oracle import attention_bwd64, attention_fwd64, attention_rows_dq64, attention_rows_fwd64
 
 RNG = np.random.default_rng(1234)  # reseeded per test (tests/conftest.py)
@@ -275,6 +276,37 @@ def test_bwd_identities(causal):
     np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
     if causal:
         np.testing.assert_allclose(dq[:, :, 0], 0.0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_outer_identities(causal):
+    """sum_i dQ_i q_i^T = sum_j k_j dK_j^T (both scale sum_ij dS_ij k_j q_i^T)
+    and sum_i O_i dO_i^T = sum_j v_j dV_j^T (both sum_ij P_ij v_j dO_i^T):
+    they tie dK to dQ and dV to O with d x d equations per head (a scale
+    applied to one gradient only, P for P^T in dV, or a dS sign slip in one
+    of dQ and dK breaks them)."""
+    q, k, v, do = rand(2, 2, 23, 8), rand(2, 2, 19, 8), rand(2, 2, 19, 8), rand(2, 2, 23, 8)
+    o, _ = attention_fwd64(q, k, v, 0.4, causal)
+    dq, dk, dv = attention_bwd64(q, k, v, do, 0.4, causal)
+    err = identity_errors(q, k, v, do, o, dq, dk, dv)
+    assert max(err.values()) < 1e-12, err
+
+
+def test_outer_identities_under_output_rounding():
+    """The GPU tests check these identities on 16-bit outputs at 2e-2.
+    Rounding the oracle's inputs and outputs to bf16 moves them by about
+    2.4e-3 (a causal head of 512 rows at d = 128, inputs x0.5 as in the
+    16K workload), so the bound leaves room for the kernels' own rounding
+    of P and dS."""
+    def bf(x):
+        return torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+
+    q, k, v, do = (bf(0.5 * rand(1, 2, 512, 128)) for _ in range(4))
+    s = 1.0 / math.sqrt(128)
+    o, _ = attention_fwd64(q, k, v, s, True)
+    dq, dk, dv = attention_bwd64(q, k, v, do, s, True)
+    err = identity_errors(q, k, v, do, bf(o), bf(dq), bf(dk), bf(dv))
+    assert max(err.values()) < 5e-3, err
 
 
 def test_bwd_uses_rowsum_identity_consistently():

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+from grad_identities import identity_errors
 from oracle import (attention_bwd64, attention_fwd64, attention_rows_dq64, dropout_keep, dropout_threshold,
                     philox4x32_10)
 
@@ -189,3 +190,18 @@ def test_rows_dq_matches_full_with_dropout(causal):
     for b in range(2):
         for h in range(3):
             np.testing.assert_allclose(got[b, h], dq[b, h][rows[b, h]], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (5, -1))])
+def test_dropout_bwd_outer_identities(causal, window):
+    """With dropout O and dV use the kept weights W = P keep s_keep and dS the
+    kept dP, and the gradient identities still hold: sum_i dQ_i q_i^T =
+    sum_j k_j dK_j^T, sum_i O_i dO_i^T = sum_j v_j dV_j^T, sum_j dK_j = 0
+    (a keep mask applied to O but not to dV, or to dQ's dS but not to dK's,
+    breaks one of them)."""
+    q, k, v, do = rand(2, 4, 30, 8), rand(2, 2, 30, 8), rand(2, 2, 30, 8), rand(2, 4, 30, 8)
+    drop = (0.3, (5 << 32) + 11, 7)
+    o, _ = attention_fwd64(q, k, v, 0.5, causal, window=window, dropout=drop)
+    dq, dk, dv = attention_bwd64(q, k, v, do, 0.5, causal, window=window, dropout=drop)
+    err = identity_errors(q, k, v, do, o, dq, dk, dv)
+    assert max(err.values()) < 1e-12, err

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+from grad_identities import identity_errors
 from oracle import attention_bwd64, attention_fwd64, attention_rows_dq64, attention_rows_fwd64
 
 RNG = np.random.default_rng(4321)  # reseeded per test (tests/conftest.py)
@@ -232,3 +233,18 @@ def test_rows_dq_matches_full_gqa_window(window, causal):
     got = attention_rows_dq64(q, k, v, do, 0.5, causal, rows, window=window)
     for h in range(4):
         np.testing.assert_allclose(got[0, h], dq[0, h][rows[0, h]], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("window,causal", [((1, 1), False), ((2, -1), True), ((0, 0), False), ((-1, 2), False)])
+def test_gqa_window_bwd_outer_identities(window, causal):
+    """The gradient identities per K/V head, its sums running over the query
+    heads that use it (h // G), with windowed rows that admit no key (25
+    queries on 17 keys: under (1, 1) and (0, 0) the last rows see none and
+    contribute nothing)."""
+    q, k, v, do = rand(2, 6, 25, 8), rand(2, 2, 17, 8), rand(2, 2, 17, 8), rand(2, 6, 25, 8)
+    o, lse = attention_fwd64(q, k, v, 0.45, causal, window=window)
+    dq, dk, dv = attention_bwd64(q, k, v, do, 0.45, causal, window=window)
+    if window in ((1, 1), (0, 0)):
+        assert np.isneginf(lse[:, :, -1]).all()
+    err = identity_errors(q, k, v, do, o, dq, dk, dv)
+    assert max(err.values()) < 1e-12, err

@@ -10,8 +10,10 @@ and N-1 always): O and LSE, and dQ of those rows (``attention_rows_dq64``;
 a query row's gradient needs only its own softmax row).  dK and dV, whose
 rows need every query, are checked through identities that hold at any
 size: sum_j dK_j = 0 per K/V head (the rows of dS sum to zero, with
-dropout too), and without dropout sum_j dV_j = the sum of dO over the
-query heads and rows that use the K/V head (the rows of P sum to one).
+dropout too), without dropout sum_j dV_j = the sum of dO over the
+query heads and rows that use the K/V head (the rows of P sum to one),
+and in every case sum_j k_j dK_j^T = sum_i dQ_i q_i^T and sum_j v_j dV_j^T
+= sum_i O_i dO_i^T over those query heads (``grad_identities``).
 """
 import math
 import sys
@@ -22,6 +24,7 @@ import torch
 
 import exact_io_aware_02_amd as fa
 from attn_inputs import WORKLOADS, sample_rows, to_bhsd64, workload_inputs
+from grad_identities import identity_errors
 from oracle import attention_rows_dq64, attention_rows_fwd64, dropout_threshold
 
 pytestmark = pytest.mark.gpu
@@ -30,6 +33,7 @@ DEV = "cuda:0"
 TOL_O = 1.6e-2   # bf16
 TOL_LSE = 1e-3
 TOL_GRAD = 2e-2  # relative Frobenius, here over the sampled rows' dQ
+TOL_IDENT = 1e-2  # the d x d gradient identities: ~4x what bf16 rounding of exact outputs gives
 ROWS = 128
 
 CASES = [
@@ -101,3 +105,6 @@ def test_bench_rows_at_16k(inputs16k, case):
         rel_v = np.abs(gv.sum(axis=2) - sum_do).max() / np.abs(sum_do).max()
         say("  sum_j dV_j vs sum dO: rel %.2e" % rel_v)
         assert rel_v < TOL_GRAD
+    err = identity_errors(qc, kc, vc, doc, og, dqg, gk, gv)
+    say("  K^T dK vs dQ^T Q %.2e, V^T dV vs O^T dO %.2e" % (err["dk"], err["dv"]))
+    assert err["dk"] <= TOL_IDENT and err["dv"] <= TOL_IDENT
