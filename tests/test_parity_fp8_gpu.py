@@ -150,6 +150,38 @@ def test_fp8_fwd_16k_causal_sampled_rows():
     check("16k", go, gl, o_ref, lse_ref, bound, sigma)
 
 
+LONG_CASES = [
+    # name, H, Hkv, N, d, layout, causal, window, descale
+    ("n131072_d128_causal", 1, 1, 131072, 128, "bhsd", True, None, (1.0, 1.0, 1.0)),
+    ("n65536_d64_mqa_window_bshd_descales", 4, 1, 65536, 64, "bshd", False, (3000, 100), (0.5, 2.0, 1.5)),
+]
+
+
+@pytest.mark.parametrize("case", LONG_CASES, ids=[c[0] for c in LONG_CASES])
+def test_fp8_fwd_long_rows(case):
+    """Long rows (up to 2048 key tiles of 64 in the heaviest block), checked
+    on 128 seeded rows per head under the rounding model (its fp32
+    accumulation term grows with Nk)."""
+    name, H, Hkv, N, d, layout, causal, window, descale = case
+    say("case fp8 long rows %s" % name)
+    inp = make_qkv(1, H, N, N, d, "fp8", layout, seed=91, in_scale=0.5, Hkv=Hkv)
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.attention_fwd_fp8(q, k, v, causal=causal, scale=scale, layout=layout, window=window,
+                                  descale=descale)
+    torch.cuda.synchronize()
+    w = window if window is not None else (-1, -1)
+    rows = sample_rows(1, H, N, 128, seed=92)
+    q8, k8, v8 = (fp8_bytes(inp[x], layout) for x in ("q", "k", "v"))
+    o_ref, lse_ref = attention_fp8_rows_fwd64(q8, k8, v8, scale, causal, rows, window=w, descale=descale)
+    bound, sigma = fp8_rounding_model(q8, k8, v8, scale, causal, rows, window=w, descale=descale)
+    got_o = to_bhsd64(o.cpu(), layout)
+    got_l = lse.cpu().numpy().astype(np.float64)
+    go = np.stack([np.stack([got_o[0, h][rows[0, h]] for h in range(H)])])
+    gl = np.stack([np.stack([got_l[0, h][rows[0, h]] for h in range(H)])])
+    check(name, go, gl, o_ref, lse_ref, bound, sigma)
+
+
 def test_fp8_fwd_gqa_equals_repeated_heads():
     """Sharing a K/V head gives bit-for-bit the result of repeating it."""
     say("case fp8_gqa_vs_repeat")
