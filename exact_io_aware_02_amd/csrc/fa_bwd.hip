@@ -11,9 +11,10 @@
 // Three kernels, deterministic (no atomics):
 //   prep_kernel  -D_i = -dO_i . O_i and lse_i * log2(e) per query row, into
 //                the workspace (HBM bound, tiny).
-//   dkdv_kernel  a workgroup of NPAIR pairs of waves owns 32 * NPAIR keys
-//                (six pairs at d = 128, four at d = 64); the two waves of a
-//                pair share 32 keys and split the work by role (A: K in
+//   dkdv_kernel  a workgroup of NPAIR pairs of waves owns 32 * KB * NPAIR
+//                keys (at d = 128 four pairs of 64 keys, or six of 32 with
+//                dropout; at d = 64 four of 32); the two waves of a pair
+//                share its keys and split the work by role (A: K in
 //                registers, S, P, dV; B: V in registers, dP, dS, dK, with P
 //                handed over through LDS), skewed so that one role's MFMAs
 //                run under the other's VALU work.
@@ -138,6 +139,61 @@ __device__ __forceinline__ void tile_t_times(f32x16 (&acc)[D / 32], const uint16
     for (int db = 0; db < D / 32; ++db) acc[db] = mfma32<DT>(lds_transposed_a<D>(tile, ta, kk, db), bp[kk], acc[db]);
 }
 
+// The same two products for KB 32-key blocks at once: each LDS operand read
+// feeds one MFMA per block (s[kb] starts at init).
+template <int D, int DT, int KB>
+__device__ __forceinline__ void rows_times_regs_kb(f32x16 (&s)[KB], const uint16_t* tile,
+                                                   const u32x4 (&bf)[KB][D / 16], const TileLayout<D>& ta,
+                                                   const f32x16& init) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const u32x4 a = lds_rowmajor<D>(tile, ta, ks);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32<DT>(a, bf[kb][ks], ks == 0 ? init : s[kb]);
+  }
+}
+template <int D, int DT, int KB>
+__device__ __forceinline__ void tile_t_times_kb(f32x16 (&acc)[KB][D / 32], const uint16_t* tile,
+                                                const u32x4 (&bp)[KB][2], const TileLayout<D>& ta) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const u32x4 a = lds_transposed_a<D>(tile, ta, kk, db);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc[kb][db] = mfma32<DT>(a, bp[kb][kk], acc[kb][db]);
+    }
+}
+
+// Issue order of a run of MFMAs fed by LDS operand reads: NO1 operands of
+// R1 read instructions each, then NO2 operands of R2 each, every operand
+// feeding KB consecutive MFMAs.  After each MFMA the reads of the operand
+// LEAD operands ahead have gone out (the first LEAD operands' reads go
+// first), so a read runs about LEAD * KB MFMAs ahead of its use while only
+// LEAD operands are in flight.
+// PRE more reads (an accumulator's initial values) go out first.
+template <int NO1, int R1, int NO2, int R2>
+constexpr int reads_through(int o) {  // read instructions of operands 0 .. o
+  return o < NO1 ? R1 * (o + 1) : R1 * NO1 + R2 * (o - NO1 + 1);
+}
+template <int KB, int NO1, int R1, int NO2, int R2, int LEAD, int I, int ISSUED>
+__device__ __forceinline__ void sched_ops_step() {
+  constexpr int NM = KB * (NO1 + NO2);
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int o = I / KB + LEAD < NO1 + NO2 - 1 ? I / KB + LEAD : NO1 + NO2 - 1;
+    constexpr int T = reads_through<NO1, R1, NO2, R2>(o);
+    if constexpr (T > ISSUED) __builtin_amdgcn_sched_group_barrier(0x100, T - ISSUED, 0);
+    sched_ops_step<KB, NO1, R1, NO2, R2, LEAD, I + 1, (T > ISSUED ? T : ISSUED)>();
+  }
+}
+template <int KB, int NO1, int R1, int NO2, int R2, int LEAD, int PRE = 0>
+__device__ __forceinline__ void sched_ops() {
+  constexpr int first = reads_through<NO1, R1, NO2, R2>(LEAD - 1);
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE + first, 0);
+  sched_ops_step<KB, NO1, R1, NO2, R2, LEAD, 0, first>();
+}
+
 // Wait until the ring tile just after the one being consumed has landed:
 // `later` tiles were requested after it (at most MAXT, each L loads per
 // wave), and vmcnt counts in request order, so leaving min(later, MAXT) * L
@@ -161,23 +217,38 @@ __device__ __forceinline__ void wait_ring(int later) {
   }
 }
 
-// dK/dV workgroups hold NPAIR pairs of waves.  At d = 128 a wave needs
-// ~160 registers: six pairs (twelve waves, three per SIMD) in one
-// workgroup per CU measured 6% faster than four pairs (two per SIMD).  At
-// d = 64 a wave needs at most 128: two workgroups of four pairs share a CU
-// (four waves per SIMD, 20% faster than two).  A dQ wave at d = 64 needs at
-// most 168 registers (three per SIMD: 10% faster than two).
-template <int D>
-constexpr int kDkvPairs = D == 64 ? 4 : 6;
-template <int D>
-constexpr int kDkvWavesPerSimd = D == 64 ? 4 : 3;
+// dK/dV workgroups hold NPAIR pairs of waves, each wave KB blocks of 32
+// keys.  With KB = 1 at d = 128 a wave needs ~160 registers: six pairs
+// (twelve waves, three per SIMD) in one workgroup per CU measured 6% faster
+// than four pairs (two per SIMD).  With KB = 2 a pair owns 64 keys: every
+// LDS operand read feeds two MFMAs (one per key block), a barrier covers
+// twice the MFMA work per wave, and a wave needs ~255 registers, so four
+// pairs share a CU (two waves per SIMD; waves w and w + 4 share one, so
+// each SIMD holds one wave of each role).  At d = 128 that measured 6-7%
+// faster than six single-block pairs on 16K causal rows and 15% faster on
+// non-causal ones; with dropout (the keep-byte transpose is per 32 keys)
+// the single-block kernel runs.  At d = 64 a wave needs at most 128: two
+// workgroups of four single-block pairs share a CU (four waves per SIMD,
+// 20% faster than two).  A dQ wave at d = 64 needs at most 168 registers
+// (three per SIMD: 10% faster than two).
+template <int D, int KB = 1>
+constexpr int kDkvPairs = KB == 2 ? 4 : D == 64 ? 4 : 6;
+template <int D, int KB = 1>
+constexpr int kDkvWavesPerSimd = KB == 2 ? 2 : D == 64 ? 4 : 3;
+// key blocks per wave of the dK/dV kernel a call runs
+template <int D, bool DROP>
+constexpr int kDkvKB = (D == 128 && !DROP) ? 2 : 1;
+// keys per dK/dV workgroup
+template <int D, bool DROP>
+constexpr int kDkvKeys = 32 * kDkvKB<D, DROP> * kDkvPairs<D, kDkvKB<D, DROP>>;
 template <int D>
 constexpr int kDqWavesPerSimd = D == 64 ? 3 : 2;
 
 // ------------------------------------------------------------ dK, dV
-// NPAIR pairs of waves (four at d = 64, six at d = 128).  The two waves of
-// a pair own the same 32 keys and split the four contractions of a query
-// tile by role:
+// NPAIR pairs of waves (four at d = 64; at d = 128 four pairs of KB = 2
+// key blocks, six of one with dropout).  The two waves of a pair own the
+// same 32 * KB keys and split the four contractions of a query tile by
+// role:
 //   role A (waves 0 .. NPAIR-1): K rows in registers; S = Q K^T,
 //                       P = 2^(S c - lse2), dV^T += dO^T P; P goes to its
 //                       partner through LDS.
@@ -191,10 +262,11 @@ constexpr int kDqWavesPerSimd = D == 64 ? 3 : 2;
 //   phase 2: A  dV += .. P(t); S(t+1)               B  dS(t) = P(t) (dP(t) - D)
 // Query tiles (Q, dO and the two row statistics) stream HBM -> LDS through
 // a 4-slot ring; tile t+3 is requested in phase 2 of step t.
-template <int D, int DT, bool BAND, bool DROP>
-__global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per_eu(kDkvWavesPerSimd<D>, kDkvWavesPerSimd<D>))) void dkdv_kernel(BwdParams p) {
-  constexpr int KW = 32;            // keys per pair
-  constexpr int NPAIR = kDkvPairs<D>;  // pairs per workgroup
+template <int D, int DT, bool BAND, bool DROP, int KB>
+__global__ __launch_bounds__((128 * kDkvPairs<D, KB>)) __attribute__((amdgpu_waves_per_eu(kDkvWavesPerSimd<D, KB>, kDkvWavesPerSimd<D, KB>))) void dkdv_kernel(BwdParams p) {
+  static_assert(KB == 1 || !DROP, "dropout runs one key block per wave");
+  constexpr int KW = 32 * KB;       // keys per pair
+  constexpr int NPAIR = kDkvPairs<D, KB>;  // pairs per workgroup
   constexpr int NCOPY = 4;             // waves of a role that copy its tiles
   constexpr int BNK = NPAIR * KW;   // keys per workgroup
   constexpr int KS = D / 16;
@@ -213,7 +285,7 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
     uint16_t o[NB][kTileElems<D>];  // dO
     float l[NB][kT];         // lse * log2(e)
     float d[NB][kT];         // -D
-    f32x4 x[2][NPAIR][4][64];  // fp32 P hand-over, double buffered: [step & 1][pair][register group][lane]
+    f32x4 x[2][NPAIR][KB][4][64];  // fp32 P hand-over, double buffered: [step & 1][pair][key block][register group][lane]
     // dropout keep bytes of a pair's 32 keys x 32 queries, [step & 1][pair][key][query]
     uint8_t mk[DROP ? 2 : 1][NPAIR][KW * kT];
   };
@@ -235,7 +307,7 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
   const int b = bhk / Hkv, hk = bhk - b * Hkv;
   const int k0 = kt * BNK;
   const int kw0 = k0 + pair * KW;
-  const int key = kw0 + col;
+  const int key = kw0 + col;  // the lane's key of key block 0 (block kb: key + 32 kb)
 
   const int sst = stat_stride(p.Nq);
   const int64_t tstride = role_a ? p.sq.s : p.sdo.s;
@@ -285,16 +357,18 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
     constexpr bool A = decltype(role_tag)::value;
     // K rows (A) or V rows (B) of the pair's keys as B operands: lane holds
     // row `key`, columns 16*ks + 8*half .. +7 (zeros past Nk).
-    u32x4 kv[KS];
+    u32x4 kv[KB][KS];
     {
       const uint16_t* rp = A ? p.k + b * p.sk.b + hk * p.sk.h : p.v + b * p.sv.b + hk * p.sv.h;
       const int64_t rs = A ? p.sk.s : p.sv.s;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 x = u32x4{0, 0, 0, 0};
-        if (key < p.Nk) x = *(const u32x4*)(rp + key * rs + 16 * ks + 8 * half);
-        kv[ks] = x;
-      }
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 x = u32x4{0, 0, 0, 0};
+          if (key + 32 * kb < p.Nk) x = *(const u32x4*)(rp + (key + 32 * kb) * rs + 16 * ks + 8 * half);
+          kv[kb][ks] = x;
+        }
     }
     for (int i = 0; i < PD; ++i)
       if (i < U) issue(i);
@@ -306,11 +380,16 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
       for (int i = pair * 64 + lane; i < TileLayout<D>::BYTES / 16; i += 64 * NPAIR) z[i] = u32x4{0, 0, 0, 0};
     }
 
-    f32x16 acc[DB];  // dV^T (A) or dK^T (B)
+    f32x16 acc[KB][DB];  // dV^T (A) or dK^T (B) of each key block
+    f32x16 sd[KB];       // A: S of the next tile; B: dP - D of the current one
+    u32x4 pk[KB][2];     // A: P; B: dS of the previous tile
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-    f32x16 sd = f32x16{};  // A: S of the next tile; B: dP - D of the current one
-    u32x4 pk[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};  // A: P; B: dS of the previous tile
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[kb][db] = f32x16{};
+      sd[kb] = f32x16{};
+      pk[kb][0] = pk[kb][1] = u32x4{0, 0, 0, 0};
+    }
     const float c = p.c;
 
     TileLayout<D> ta;
@@ -340,7 +419,10 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
             const float4 lv = *(const float4*)(&Lt[8 * g4 + 4 * half]);
             const float lz[4] = {lv.x, lv.y, lv.z, lv.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sd[4 * g4 + e] = exp2_fast(__builtin_fmaf(sd[4 * g4 + e], c, -lz[e]));
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                sd[kb][4 * g4 + e] = exp2_fast(__builtin_fmaf(sd[kb][4 * g4 + e], c, -lz[e]));
           }
           // tiles that cross an edge of the pair's band
           if (BAND && ((p.wr >= 0 && i0 < kw0 + KW - 1 - p.wr) || (p.wl >= 0 && i0 + kT - 1 > kw0 + p.wl))) {
@@ -349,17 +431,32 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
             asm volatile("");
             // query of register r is i0 + 4*half + ro(r), ro(r) = 8*(r/4) + r%4;
             // key > query + wr  <=>  kd - wr > ro;  key < query - wl  <=>  kd + wl < ro
-            const int kd = key - i0 - 4 * half;
+            // key - query offset of the lane's registers; with two key
+            // blocks the lane id is re-read here instead of kept live
+            // through the loop (registers)
+            int kd0 = key - 4 * half;
+            if constexpr (KB > 1) {
+              uint32_t lo, ln;
+              asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %1, -1, %0" : "=&v"(lo), "=v"(ln));
+              kd0 = kw0 + (int)(ln & 31u) - 4 * (int)((ln >> 5) & 1u);
+            }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int ro = ((r >> 2) << 3) + (r & 3);
-              if ((p.wr >= 0 && kd - p.wr > ro) || (p.wl >= 0 && kd + p.wl < ro)) sd[r] = 0.f;
+            for (int kb = 0; kb < KB; ++kb) {
+              const int kd = kd0 + 32 * kb - i0;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int ro = ((r >> 2) << 3) + (r & 3);
+                if ((p.wr >= 0 && kd - p.wr > ro) || (p.wl >= 0 && kd + p.wl < ro)) sd[kb][r] = 0.f;
+              }
             }
           }
           // P in fp32 to the partner (exact dS, no unpacking there)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4)
-            X[64 * g4 + lane] = f32x4{sd[4 * g4], sd[4 * g4 + 1], sd[4 * g4 + 2], sd[4 * g4 + 3]};
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+              X[64 * (4 * kb + g4) + lane] =
+                  f32x4{sd[kb][4 * g4], sd[kb][4 * g4 + 1], sd[kb][4 * g4 + 2], sd[kb][4 * g4 + 3]};
           if constexpr (DROP) {
             // The forward's draw for query i0 + col and the 16 keys of the
             // pair with key bit 2 = half (one call per lane), turned to a
@@ -377,13 +474,16 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
               const uint32_t kw = *(const uint32_t*)&Mk[col * kT + 8 * g4 + 4 * half];
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (((kw >> (8 * e)) & 0xffu) < p.drop.thr) sd[4 * g4 + e] = 0.f;
+                if (((kw >> (8 * e)) & 0xffu) < p.drop.thr) sd[0][4 * g4 + e] = 0.f;
             }
           }
-          pk[0] = pack_acc8<DT>(sd, 0);  // P (kept P with dropout) for dV
-          pk[1] = pack_acc8<DT>(sd, 1);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            pk[kb][0] = pack_acc8<DT>(sd[kb], 0);  // P (kept P with dropout) for dV
+            pk[kb][1] = pack_acc8<DT>(sd[kb], 1);
+          }
         };
-        phase(sm.l[SL], &sm.x[XB][pair][0][0], &sm.mk[DROP ? XB : 0][pair][0]);
+        phase(sm.l[SL], &sm.x[XB][pair][0][0][0], &sm.mk[DROP ? XB : 0][pair][0]);
       } else {
         auto phase = [&](const uint16_t* __restrict__ Ot, const float* __restrict__ Dt,
                          const uint16_t* __restrict__ Qprev) {
@@ -403,12 +503,20 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
               dinit[4 * g4 + 3] = dv.w;
             }
           }
-          sd = rows_times_regs<D, DT>(Ot, kv, ta, dinit);
-          // dK^T += Q^T dS of the previous tile, after dP: dS of this tile
-          // (the next phase) waits only for dP, so its MFMAs go first
-          tile_t_times<D, DT>(acc, Qprev, pk, ta);
-          // issue order: operand reads kReadLead MFMAs ahead of their use
-          sched_reads_ahead<2 * DB + KS, (4 * DB + 4 + KS)>();
+          if constexpr (KB == 1) {
+            rows_times_regs_kb<D, DT, KB>(sd, Ot, kv, ta, dinit);
+            // dK^T += Q^T dS of the previous tile, after dP: dS of this tile
+            // (the next phase) waits only for dP, so its MFMAs go first
+            tile_t_times_kb<D, DT, KB>(acc, Qprev, pk, ta);
+            // issue order: operand reads kReadLead MFMAs ahead of their use
+            sched_reads_ahead<2 * DB + KS, (4 * DB + 4 + KS)>();
+          } else {
+            // with two key blocks dK goes first: dS of the previous tile
+            // then dies before dP is born (registers)
+            tile_t_times_kb<D, DT, KB>(acc, Qprev, pk, ta);
+            rows_times_regs_kb<D, DT, KB>(sd, Ot, kv, ta, dinit);
+            sched_ops<KB, 2 * DB, 2, KS, 1, 2, 4>();
+          }
           if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
         };
         // on the first step dS = 0 and the previous slot holds zeros
@@ -427,37 +535,43 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
       if constexpr (A) {
         auto phase = [&](const uint16_t* __restrict__ Ot, const uint16_t* __restrict__ Qn) {
           if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
-          tile_t_times<D, DT>(acc, Ot, pk, ta);  // dV^T += dO^T P
+          tile_t_times_kb<D, DT, KB>(acc, Ot, pk, ta);  // dV^T += dO^T P
           // S of the next tile (after the last tile this reads a stale slot
           // and the result is never used)
-          sd = rows_times_regs<D, DT>(Qn, kv, ta);
-          sched_reads_ahead<2 * DB + KS, 4 * DB + KS>();
+          rows_times_regs_kb<D, DT, KB>(sd, Qn, kv, ta, f32x16{});
+          if constexpr (KB == 1)
+            sched_reads_ahead<2 * DB + KS, 4 * DB + KS>();
+          else
+            sched_ops<KB, 2 * DB, 2, KS, 1, 2>();
           if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
         };
         phase(sm.o[SL], sm.q[(SL + 1) & (NB - 1)]);
       } else {
         auto phase = [&](const f32x4* __restrict__ X, const uint8_t* __restrict__ Mk, const float* __restrict__ Dt) {
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 pv = X[64 * g4 + lane];
-            if constexpr (DROP) {  // dS = P (keep * scale * dP - D)
-              const uint32_t kw = *(const uint32_t*)&Mk[col * kT + 8 * g4 + 4 * half];
-              const float4 nd = *(const float4*)(&Dt[8 * g4 + 4 * half]);
-              const float ndv[4] = {nd.x, nd.y, nd.z, nd.w};
+          for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float m = ((kw >> (8 * e)) & 0xffu) >= p.drop.thr ? p.drop.scale : 0.f;
-                sd[4 * g4 + e] = pv[e] * __builtin_fmaf(m, sd[4 * g4 + e], ndv[e]);
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const f32x4 pv = X[64 * (4 * kb + g4) + lane];
+              if constexpr (DROP) {  // dS = P (keep * scale * dP - D)
+                const uint32_t kw = *(const uint32_t*)&Mk[col * kT + 8 * g4 + 4 * half];
+                const float4 nd = *(const float4*)(&Dt[8 * g4 + 4 * half]);
+                const float ndv[4] = {nd.x, nd.y, nd.z, nd.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float m = ((kw >> (8 * e)) & 0xffu) >= p.drop.thr ? p.drop.scale : 0.f;
+                  sd[kb][4 * g4 + e] = pv[e] * __builtin_fmaf(m, sd[kb][4 * g4 + e], ndv[e]);
+                }
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sd[kb][4 * g4 + e] *= pv[e];
               }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) sd[4 * g4 + e] *= pv[e];
             }
+            pk[kb][0] = pack_acc8<DT>(sd[kb], 0);
+            pk[kb][1] = pack_acc8<DT>(sd[kb], 1);
           }
-          pk[0] = pack_acc8<DT>(sd, 0);
-          pk[1] = pack_acc8<DT>(sd, 1);
         };
-        phase(&sm.x[XB][pair][0][0], &sm.mk[DROP ? XB : 0][pair][0], sm.d[SL]);
+        phase(&sm.x[XB][pair][0][0][0], &sm.mk[DROP ? XB : 0][pair][0], sm.d[SL]);
       }
       if (++it == qhi) {
         it = qlo;
@@ -493,32 +607,37 @@ __global__ __launch_bounds__(128 * kDkvPairs<D>) __attribute__((amdgpu_waves_per
     for (; u < ulo; ++u) idle(u);
     if (u < uhi) {
       if constexpr (A) {  // S of the first own step's tile
-        auto s_tile = [&](const uint16_t* __restrict__ Qt) { sd = rows_times_regs<D, DT>(Qt, kv, ta); };
+        auto s_tile = [&](const uint16_t* __restrict__ Qt) { rows_times_regs_kb<D, DT, KB>(sd, Qt, kv, ta, f32x16{}); };
         s_tile(sm.q[u & (NB - 1)]);
       }
       for (; u < uhi; ++u) step(u);
       // the previous-tile product of the last own step: B's dK (its slot is
       // refilled only after the next step's barrier)
       if constexpr (!A) {
-        auto last = [&](const uint16_t* __restrict__ Qt) { tile_t_times<D, DT>(acc, Qt, pk, ta); };
+        auto last = [&](const uint16_t* __restrict__ Qt) { tile_t_times_kb<D, DT, KB>(acc, Qt, pk, ta); };
         last(sm.q[(uhi - 1) & (NB - 1)]);
       }
     }
     for (; u < U; ++u) idle(u);
 
-    if (key < p.Nk) {
-      if (p.S > 1) {  // fp32 partial row of dK (B) or dV (A), scaled by the reduction
-        float* rowp = p.part + ((((size_t)(A ? 1 : 0) * p.S + sp) * BH + bhk) * (size_t)p.Nk + key) * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int kb = 0; kb < KB; ++kb) {
+      const int kk = key + 32 * kb;
+      if (kk < p.Nk) {
+        if (p.S > 1) {  // fp32 partial row of dK (B) or dV (A), scaled by the reduction
+          float* rowp = p.part + ((((size_t)(A ? 1 : 0) * p.S + sp) * BH + bhk) * (size_t)p.Nk + kk) * D;
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4)
-            *(f32x4*)(rowp + db * 32 + 8 * g4 + 4 * half) =
-                f32x4{acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]};
-      } else if constexpr (A) {
-        store_rows<DT, DB>(p.dv + b * p.sdv.b + hk * p.sdv.h + key * p.sdv.s, acc, DROP ? p.drop.scale : 1.0f, half);
-      } else {
-        store_rows<DT, DB>(p.dk + b * p.sdk.b + hk * p.sdk.h + key * p.sdk.s, acc, p.scale, half);
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+              *(f32x4*)(rowp + db * 32 + 8 * g4 + 4 * half) = f32x4{acc[kb][db][4 * g4], acc[kb][db][4 * g4 + 1],
+                                                                    acc[kb][db][4 * g4 + 2], acc[kb][db][4 * g4 + 3]};
+        } else if constexpr (A) {
+          store_rows<DT, DB>(p.dv + b * p.sdv.b + hk * p.sdv.h + kk * p.sdv.s, acc[kb], DROP ? p.drop.scale : 1.0f,
+                             half);
+        } else {
+          store_rows<DT, DB>(p.dk + b * p.sdk.b + hk * p.sdk.h + kk * p.sdk.s, acc[kb], p.scale, half);
+        }
       }
     }
   };
@@ -915,7 +1034,8 @@ hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t st
   constexpr int RPB = kThreads / (D / 8);
   const int64_t prep_bpb = (stat_stride(p.Nq) + RPB - 1) / RPB;
   const int64_t g0 = prep_bpb * BH;
-  constexpr int BNK = 32 * kDkvPairs<D>;  // keys per dK/dV workgroup
+  constexpr int KB = kDkvKB<D, DROP>;
+  constexpr int BNK = kDkvKeys<D, DROP>;  // keys per dK/dV workgroup
   const int64_t g1 = (int64_t)((p.Nk + BNK - 1) / BNK) * BHkv * p.S;
   const int64_t rrows = BHkv * (int64_t)p.Nk;  // rows of dK (and of dV)
   const int64_t gr = (2 * rrows * (D / 8) + kThreads - 1) / kThreads;
@@ -958,7 +1078,8 @@ hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t st
   // first, and dQ's fill the CUs that the light key blocks free.
   if (side && (e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
   if ((stages & 2) && g1 > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP>), dim3((unsigned)g1), dim3(128 * kDkvPairs<D>), 0, stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP, KB>), dim3((unsigned)g1), dim3(128 * kDkvPairs<D, KB>), 0,
+                       stream, p);
     e = hipGetLastError();
     if (e == hipSuccess && p.S > 1) {
       hipLaunchKernelGGL((dkdv_reduce_kernel<D, DT>), dim3((unsigned)gr), dim3(kThreads), 0, stream, p, (int)rrows);
@@ -1029,7 +1150,8 @@ constexpr int kEqSplitMinKeys = 2048;
 int bwd_kv_splits(int B, int H, int H_kv, int Nk, int d) {
   if (H_kv <= 0 || H % H_kv != 0) return 1;
   const int G = H / H_kv;
-  const int bnk = 32 * (d == 64 ? kDkvPairs<64> : kDkvPairs<128>);
+  // (the key blocks of the kernel without dropout; the same S serves both)
+  const int bnk = d == 64 ? kDkvKeys<64, false> : kDkvKeys<128, false>;
   const int64_t base = (int64_t)((Nk + bnk - 1) / bnk) * B * H_kv;
   if (G == 1) return base < (int64_t)kChipCUs * (d == 64 ? 2 : 1) && Nk >= kEqSplitMinKeys ? 2 : 1;
   for (int S = 1; S < G; ++S)

@@ -374,9 +374,9 @@ def split_extra(S, B, Hkv, Nk, d):
 def test_ex_workspace_bytes():
     base = fa.fa_bwd_workspace_bytes(1, 16, 16384, 16384, 128, fa.FA_BF16)
     # equal heads: nothing extra when the dK/dV grid gives every CU a
-    # workgroup (86 key blocks x 16 heads)...
+    # workgroup (64 key blocks of 256 keys x 16 heads)...
     assert fa.fa_bwd_ex_workspace_bytes(1, 16, 16, 16384, 16384, 128, fa.FA_BF16) == base
-    # ...two runs per key block when it does not (86 x 2 = 172 < 256 CUs)
+    # ...two runs per key block when it does not (64 x 2 = 128 < 256 CUs)
     assert fa.fa_bwd_ex_workspace_bytes(1, 2, 2, 16384, 16384, 128, fa.FA_BF16) == \
         fa.fa_bwd_workspace_bytes(1, 2, 16384, 16384, 128, fa.FA_BF16) + split_extra(2, 1, 2, 16384, 128)
     # ...at d = 64 below the 512 workgroups the chip holds (B2 H8 N2048: 16 x 16)...
@@ -385,12 +385,14 @@ def test_ex_workspace_bytes():
     # ...but not below 2048 keys, nor from a full chip on (d = 128: 256; d = 64: 512)
     assert fa.fa_bwd_ex_workspace_bytes(1, 2, 2, 1024, 1024, 128, fa.FA_BF16) == \
         fa.fa_bwd_workspace_bytes(1, 2, 1024, 1024, 128, fa.FA_BF16)
+    assert fa.fa_bwd_ex_workspace_bytes(1, 4, 4, 16384, 16384, 128, fa.FA_BF16) == \
+        fa.fa_bwd_workspace_bytes(1, 4, 16384, 16384, 128, fa.FA_BF16)
     assert fa.fa_bwd_ex_workspace_bytes(1, 3, 3, 16384, 16384, 128, fa.FA_BF16) == \
-        fa.fa_bwd_workspace_bytes(1, 3, 16384, 16384, 128, fa.FA_BF16)
+        fa.fa_bwd_workspace_bytes(1, 3, 16384, 16384, 128, fa.FA_BF16) + split_extra(2, 1, 3, 16384, 128)
     assert fa.fa_bwd_ex_workspace_bytes(1, 4, 4, 16384, 16384, 64, fa.FA_BF16) == \
         fa.fa_bwd_workspace_bytes(1, 4, 16384, 16384, 64, fa.FA_BF16)
-    # 16 query heads on 2 K/V heads at 16K, d = 128 (192 keys per dK/dV
-    # workgroup): 86 key blocks x 2 = 172 workgroups, split 8 ways to reach 1024
+    # 16 query heads on 2 K/V heads at 16K, d = 128 (256 keys per dK/dV
+    # workgroup): 64 key blocks x 2 = 128 workgroups, split 8 ways to reach 1024
     big = fa.fa_bwd_ex_workspace_bytes(1, 16, 2, 16384, 16384, 128, fa.FA_BF16)
     assert big == base + split_extra(8, 1, 2, 16384, 128)
     # d = 64 (128 keys per workgroup): 128 x 2 = 256 workgroups, split 4 ways
