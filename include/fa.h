@@ -283,7 +283,7 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
  * (deterministic; results can differ from the unsplit order in the last
  * bits of fp32 rounding).  S > 1 with fewer K/V heads (whole query heads
  * per run, until there are 1024 workgroups); with H_kv = H, S = 2 when the
- * dK/dV grid (one workgroup per 192 keys at d = 128, 128 at d = 64, per
+ * dK/dV grid (one workgroup per 256 keys at d = 128, 128 at d = 64, per
  * (b, head)) has fewer workgroups than the MI355X holds at once (256 at
  * d = 128, 512 at d = 64) and Nk >= 2048; otherwise S = 1 (no extra part). */
 size_t fa_bwd_ex_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d, int dtype);
