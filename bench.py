@@ -136,7 +136,8 @@ def power_context(torch, fa, q, k, v, o, lse, s, causal, stream, fwd_flop, peak)
     """The chip's power cap sets its clock under load: the forward back to
     back with amd-smi's clock and power readings, beside a large bf16 GEMM
     (torch.matmul, hipBLASLt) on random N(0,1) operands as the dense-MFMA
-    rate a tuned library reaches under the same cap."""
+    rate a tuned library reaches under the same cap, and the same GEMM on
+    e4m3 operands (torch._scaled_mm) for the fp8 forward's row."""
     out = {}
     ms, mhz, w = sustained(torch, lambda: fa.fa_fwd(q, k, v, o, lse, s, causal, stream), 4.0, stream)
     tf = fwd_flop / ms / 1e9
@@ -154,6 +155,20 @@ def power_context(torch, fa, q, k, v, o, lse, s, causal, stream, fwd_flop, peak)
     if mhz:
         out["fwd_frac_of_peak_at_sclk"] = tf / (peak * mhz / 2400.0)
     del a, b, c
+    # the same for e4m3 operands (torch._scaled_mm, bf16 out): the rate the
+    # fp8 forward's row is compared with
+    try:
+        a8 = torch.randn(n, n, generator=g).to(q.device).to(torch.float8_e4m3fn)
+        b8 = torch.randn(n, n, generator=g).to(q.device).to(torch.float8_e4m3fn).t()
+        one = torch.ones((), device=q.device)
+        ms_8, mhz_8, w_8 = sustained(
+            torch, lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16), 4.0, stream)
+        tf_8 = 2.0 * n ** 3 / ms_8 / 1e9
+        out["gemm_fp8"] = {"m_n_k": [n, n, n], "ms": ms_8, "tflops": tf_8, "frac_of_fp8_peak": tf_8 / PEAK_TFLOPS["fp8"],
+                           "sclk_mhz": mhz_8, "socket_power_w": w_8}
+        del a8, b8
+    except Exception as e:  # no fp8 GEMM in this torch build: the row keeps only its peak fraction
+        out["gemm_fp8"] = {"error": repr(e)[:200]}
     return out
 
 
@@ -817,6 +832,9 @@ def main():
         log("power context: fwd %.1f TFLOP/s at %s MHz / %s W; bf16 GEMM 8192^3 %.1f TFLOP/s at %s MHz / %s W" % (
             pc["fwd"]["tflops"], pc["fwd"]["sclk_mhz"], pc["fwd"]["socket_power_w"], pc["gemm_bf16"]["tflops"],
             pc["gemm_bf16"]["sclk_mhz"], pc["gemm_bf16"]["socket_power_w"]))
+        if pc["gemm_fp8"].get("tflops"):
+            log("power context: fp8 GEMM 8192^3 %.1f TFLOP/s at %s MHz / %s W" % (
+                pc["gemm_fp8"]["tflops"], pc["gemm_fp8"]["sclk_mhz"], pc["gemm_fp8"]["socket_power_w"]))
     if not args.no_small_configs:
         log("configurations:")
         out["configs"] = config_report(fa, torch, stream, lambda dt: PEAK_TFLOPS[dt], with_oracle=not args.no_oracle)
@@ -824,6 +842,12 @@ def main():
         out["configs"].update(nc)
     if not args.no_rows_f:
         out["rows_f"] = next_rows(fa, torch, q, k, v, do, s, stream, peak, min(K, 10))
+        g8 = (out.get("power_context") or {}).get("gemm_fp8") or {}
+        if g8.get("tflops"):
+            r8 = out["rows_f"]["fp8_fwd"]
+            r8["frac_of_fp8_gemm"] = r8["fwd_tflops"] / g8["tflops"]
+            log("fp8_fwd: %.1f%% of the fp8 GEMM's %.1f TFLOP/s under the same cap" % (
+                100 * r8["frac_of_fp8_gemm"], g8["tflops"]))
     # the 16K workload's entry of the per-configuration report
     c4 = {"workload": "B1 H16 N16384 d128 bf16 BHSD causal, inputs x0.5",
           "fwd_ms": fwd_ms, "fwd_tflops": fwd_flop / fwd_ms / 1e9, "fwd_frac_of_peak": fwd_flop / fwd_ms / 1e9 / peak,
