@@ -1034,8 +1034,11 @@ hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t st
   constexpr int RPB = kThreads / (D / 8);
   const int64_t prep_bpb = (stat_stride(p.Nq) + RPB - 1) / RPB;
   const int64_t g0 = prep_bpb * BH;
-  constexpr int KB = kDkvKB<D, DROP>;
-  constexpr int BNK = kDkvKeys<D, DROP>;  // keys per dK/dV workgroup
+  // Two key blocks per wave at d = 128 without dropout, unless the band
+  // has a left edge (a window): there the single-block kernel measured 1-7%
+  // faster (B1 H16 N16384: windows (64, 64) to (4096, 0)).
+  const bool two = kDkvKB<D, DROP> == 2 && p.wl < 0;
+  const int BNK = two ? kDkvKeys<D, DROP> : 32 * kDkvPairs<D, 1>;  // keys per dK/dV workgroup
   const int64_t g1 = (int64_t)((p.Nk + BNK - 1) / BNK) * BHkv * p.S;
   const int64_t rrows = BHkv * (int64_t)p.Nk;  // rows of dK (and of dV)
   const int64_t gr = (2 * rrows * (D / 8) + kThreads - 1) / kThreads;
@@ -1078,8 +1081,17 @@ hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t st
   // first, and dQ's fill the CUs that the light key blocks free.
   if (side && (e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
   if ((stages & 2) && g1 > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP, KB>), dim3((unsigned)g1), dim3(128 * kDkvPairs<D, KB>), 0,
-                       stream, p);
+    if constexpr (kDkvKB<D, DROP> == 2) {
+      if (two)
+        hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP, 2>), dim3((unsigned)g1), dim3(128 * kDkvPairs<D, 2>), 0,
+                           stream, p);
+      else
+        hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP, 1>), dim3((unsigned)g1), dim3(128 * kDkvPairs<D, 1>), 0,
+                           stream, p);
+    } else {
+      hipLaunchKernelGGL((dkdv_kernel<D, DT, BAND, DROP, 1>), dim3((unsigned)g1), dim3(128 * kDkvPairs<D, 1>), 0,
+                         stream, p);
+    }
     e = hipGetLastError();
     if (e == hipSuccess && p.S > 1) {
       hipLaunchKernelGGL((dkdv_reduce_kernel<D, DT>), dim3((unsigned)gr), dim3(kThreads), 0, stream, p, (int)rrows);
