@@ -13,10 +13,11 @@
 //                the workspace (HBM bound, tiny).
 //   dkdv_kernel  a workgroup of NPAIR pairs of waves owns 32 * KB * NPAIR
 //                keys (at d = 128 four pairs of 64 keys, or six of 32 with
-//                dropout; at d = 64 four of 32); the two waves of a pair
-//                share its keys and split the work by role (A: K in
-//                registers, S, P, dV; B: V in registers, dP, dS, dK, with P
-//                handed over through LDS), skewed so that one role's MFMAs
+//                dropout or a sliding window; at d = 64 four of 32); the
+//                two waves of a pair share its keys and split the work by
+//                role (A: K in registers, S, P, dV; B: V in registers, dP,
+//                dS, dK, with P handed over through LDS), skewed so that
+//                one role's MFMAs
 //                run under the other's VALU work.
 //                32-query tiles of Q, dO and the two row statistics stream
 //                HBM -> LDS through a 4-slot ring.  S = Q K^T and dP = dO V^T
@@ -170,8 +171,8 @@ __device__ __forceinline__ void tile_t_times_kb(f32x16 (&acc)[KB][D / 32], const
 // feeding KB consecutive MFMAs.  After each MFMA the reads of the operand
 // LEAD operands ahead have gone out (the first LEAD operands' reads go
 // first), so a read runs about LEAD * KB MFMAs ahead of its use while only
-// LEAD operands are in flight.
-// PRE more reads (an accumulator's initial values) go out first.
+// LEAD operands are in flight.  PRE more reads (an accumulator's initial
+// values) go out first.
 template <int NO1, int R1, int NO2, int R2>
 constexpr int reads_through(int o) {  // read instructions of operands 0 .. o
   return o < NO1 ? R1 * (o + 1) : R1 * NO1 + R2 * (o - NO1 + 1);
@@ -235,10 +236,11 @@ template <int D, int KB = 1>
 constexpr int kDkvPairs = KB == 2 ? 4 : D == 64 ? 4 : 6;
 template <int D, int KB = 1>
 constexpr int kDkvWavesPerSimd = KB == 2 ? 2 : D == 64 ? 4 : 3;
-// key blocks per wave of the dK/dV kernel a call runs
+// key blocks per wave of the dK/dV kernel without a left band edge (a
+// sliding window runs the single-block kernel, see launch_t)
 template <int D, bool DROP>
 constexpr int kDkvKB = (D == 128 && !DROP) ? 2 : 1;
-// keys per dK/dV workgroup
+// keys per dK/dV workgroup of that kernel
 template <int D, bool DROP>
 constexpr int kDkvKeys = 32 * kDkvKB<D, DROP> * kDkvPairs<D, kDkvKB<D, DROP>>;
 template <int D>
@@ -246,9 +248,9 @@ constexpr int kDqWavesPerSimd = D == 64 ? 3 : 2;
 
 // ------------------------------------------------------------ dK, dV
 // NPAIR pairs of waves (four at d = 64; at d = 128 four pairs of KB = 2
-// key blocks, six of one with dropout).  The two waves of a pair own the
-// same 32 * KB keys and split the four contractions of a query tile by
-// role:
+// key blocks, six of one with dropout or a window).  The two waves of a
+// pair own the same 32 * KB keys and split the four contractions of a
+// query tile by role:
 //   role A (waves 0 .. NPAIR-1): K rows in registers; S = Q K^T,
 //                       P = 2^(S c - lse2), dV^T += dO^T P; P goes to its
 //                       partner through LDS.
