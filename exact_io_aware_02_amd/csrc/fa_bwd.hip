@@ -17,8 +17,7 @@
 //                two waves of a pair share its keys and split the work by
 //                role (A: K in registers, S, P, dV; B: V in registers, dP,
 //                dS, dK, with P handed over through LDS), skewed so that
-//                one role's MFMAs
-//                run under the other's VALU work.
+//                one role's MFMAs run under the other's VALU work.
 //                32-query tiles of Q, dO and the two row statistics stream
 //                HBM -> LDS through a 4-slot ring.  S = Q K^T and dP = dO V^T
 //                come out with a key per lane, which is the B-operand
