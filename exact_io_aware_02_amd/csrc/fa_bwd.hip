@@ -242,6 +242,8 @@ constexpr int kDkvKB = (D == 128 && !DROP) ? 2 : 1;
 // keys per dK/dV workgroup of that kernel
 template <int D, bool DROP>
 constexpr int kDkvKeys = 32 * kDkvKB<D, DROP> * kDkvPairs<D, kDkvKB<D, DROP>>;
+// causal bands run the two-block kernel from this many of its key blocks
+constexpr int64_t kDkvTwoMinBlocks = 65;
 template <int D>
 constexpr int kDqWavesPerSimd = D == 64 ? 3 : 2;
 
@@ -1036,9 +1038,15 @@ hipError_t launch_t(const BwdParams& p, int stages, bool side_ok, hipStream_t st
   const int64_t prep_bpb = (stat_stride(p.Nq) + RPB - 1) / RPB;
   const int64_t g0 = prep_bpb * BH;
   // Two key blocks per wave at d = 128 without dropout, unless the band
-  // has a left edge (a window): there the single-block kernel measured 1-7%
-  // faster (B1 H16 N16384: windows (64, 64) to (4096, 0)).
-  const bool two = kDkvKB<D, DROP> == 2 && p.wl < 0;
+  // has a left edge (a window: there the single-block kernel measured 1-7%
+  // faster, B1 H16 N16384 with windows (64, 64) to (4096, 0)), or a causal
+  // band leaves the grid at most kDkvTwoMinBlocks - 1 two-block key blocks
+  // (the heaviest block's run is then the critical path, and the smaller
+  // blocks shorten it: B1 H1 N16384 0.388 -> 0.351 ms, B1 H2 N8192 0.223 ->
+  // 0.197, B1 H4 N4096 0.136 -> 0.119; at 128 blocks the two were within
+  // +-4% either way).
+  const int64_t blocks2 = (int64_t)((p.Nk + kDkvKeys<D, false> - 1) / kDkvKeys<D, false>) * BHkv;
+  const bool two = kDkvKB<D, DROP> == 2 && p.wl < 0 && (!BAND || blocks2 >= kDkvTwoMinBlocks);
   const int BNK = two ? kDkvKeys<D, DROP> : 32 * kDkvPairs<D, 1>;  // keys per dK/dV workgroup
   const int64_t g1 = (int64_t)((p.Nk + BNK - 1) / BNK) * BHkv * p.S;
   const int64_t rrows = BHkv * (int64_t)p.Nk;  // rows of dK (and of dV)

@@ -655,3 +655,29 @@ def test_small_backward_captured_while_another_thread_runs_eagerly():
         if not all(torch.equal(a, b) for a, b in zip(outs_a, ref)):
             bad.append(("replay", i))
     assert not bad, bad
+
+
+@pytest.mark.parametrize("B,H,N,dtype,layout", [
+    (1, 72, 256, "fp16", "bhsd"),    # 72 key blocks of 256: one per head
+    (1, 40, 300, "bf16", "bshd"),    # 80 blocks; the second one's pairs partly or wholly past Nk
+    (1, 9, 2048, "bf16", "bhsd"),    # 72 blocks, fewer than the CUs: each block's query tiles in two runs
+])
+def test_causal_two_key_blocks(B, H, N, dtype, layout):
+    """Causal d = 128 bands with at least 65 key blocks of 256 run the
+    dK/dV kernel with two 32-key blocks per wave (smaller grids and windows
+    run the single-block one): full tensors against the oracle."""
+    d = 128
+    say("case causal two-block B%d H%d N%d %s %s" % (B, H, N, dtype, layout))
+    assert B * H * ((N + 255) // 256) >= 65
+    inp = make_qkv(B, H, N, N, d, dtype, layout, seed=N + H, with_do=True)
+    s = scale_of(d)
+    o, lse = fwd_gpu(inp, True, s, layout)
+    q, k, v, do = (to_bhsd64(inp[x], layout) for x in ("q", "k", "v", "do"))
+    ro, rl = attention_fwd64(q, k, v, s, True)
+    check_o(o, ro, dtype, layout)
+    check_lse(lse, rl)
+    dq, dk, dv = bwd_gpu(inp, o, lse, True, s, layout)
+    rq, rk, rv = attention_bwd64(q, k, v, do, s, True)
+    check_grad(dq, rq, layout, "dQ")
+    check_grad(dk, rk, layout, "dK")
+    check_grad(dv, rv, layout, "dV")
